@@ -1,0 +1,128 @@
+/*
+ * libfkl: fused output projection + sparse top-K KL divergence, forward and
+ * backward with recomputation, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. The method fuses the student's output projection into
+ * the distillation loss: it walks the token positions one chunk at a time,
+ * forms that chunk's logits from the hidden states and the head weight,
+ * folds them into a running loss against the teacher's cached top-K
+ * (index, logit) pairs, and drops them; backward forms each chunk's logits
+ * again instead of storing them (blog post on the page "Efficient Offline
+ * Top-K Logits and Fused Chunked KL Loss Enable Scalable LLM Distillation",
+ * section "Two systems changes"). The pages print no formula; the library
+ * implements these readings of the prose:
+ *
+ *   s[r,v]  = (h[r,:] . W[v,:]) / T                        (all rows)
+ *   lse[r]  = log sum_v exp(s[r,v])                        -> row_lse
+ *   p[r,k]  = softmax_k(t_logit[r,k] / T)   over the K cached entries
+ *   KL[r]   = sum_k p[r,k] (log p[r,k] - s[r, t_idx[r,k]] + lse[r])
+ *             (forward KL teacher || student; 0 on masked rows) -> row_kl
+ *   loss    = T^2 / n * sum_{r valid} KL[r]      (n valid rows; 0 if n = 0)
+ *   G[r,v]  = g * (T/n) * mask[r] * (exp(s[r,v] - lse[r]) - p~[r,v])
+ *   grad_h  = G W        grad_W = G^T h
+ *
+ * where p~ is p scattered onto the vocabulary at t_idx (zero elsewhere) and
+ * g the upstream gradient of the loss.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE memory owned by the caller. The library
+ *     allocates and frees nothing and keeps no state between calls.
+ *   - Row-major, contiguous. h: bf16 [N, d]; W: bf16 [V, d]; t_idx: int32
+ *     [N, K]; t_logit: fp32 [N, K]; row_mask: uint8 [N] (nonzero = valid) or
+ *     NULL (all valid); fp32 outputs.
+ *   - h and W must be 16-byte aligned; every other array 4-byte aligned.
+ *   - d must be a multiple of 8; 1 <= K <= min(V, 1024); T > 0 and finite.
+ *   - Teacher indices must lie in [0, V) and be distinct within each row
+ *     (checked only by fkl_validate_teacher); t_logit finite.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream)
+ *     and is complete when the stream is. No call synchronises the host.
+ *   - Argument errors are reported before any device work is enqueued; such
+ *     calls never touch the device, so they are safe without a GPU.
+ *   - The same workspace must not be used by two calls in flight at once.
+ */
+#ifndef FKL_H
+#define FKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FKL_OK = 0,
+  FKL_EINVAL = 1,       /* bad shape, NULL or misaligned pointer */
+  FKL_EWORKSPACE = 2,   /* workspace NULL or smaller than fkl_workspace_size() */
+  FKL_EINDEX = 3,       /* reserved for teacher-data errors */
+  FKL_EDEVICE = 4,      /* a HIP call failed; see fkl_last_error() */
+  FKL_EUNSUPPORTED = 5  /* shape outside what this build supports */
+} fkl_status;
+
+typedef struct {
+  int64_t N;     /* token positions (rows); N >= 0 */
+  int64_t d;     /* hidden size; multiple of 8, 8 <= d <= 65536 */
+  int64_t V;     /* vocabulary size; V >= 1 */
+  int32_t K;     /* cached teacher entries per row */
+  float T;       /* temperature */
+  int32_t chunk; /* rows per pass; 0 = 4096. Results do not depend on it. */
+  int32_t vslab; /* vocabulary columns per backward pass; 0 = chosen so that
+                    a pass's gradient block holds about 32 Mi elements.
+                    Rounded up to a multiple of 256. Results do not depend
+                    on it beyond fp32 summation order of grad_h. */
+} fkl_shape;
+
+/*
+ * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
+ * Pure host code. The sizes grow with chunk, vslab and K only (never with
+ * N or with V beyond one slab): forward O(chunk * (K + 64)), backward
+ * O(chunk * (vslab + K)).
+ */
+fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/*
+ * Forward pass: loss (fp32 [1]), row_lse (fp32 [N], logsumexp over the
+ * vocabulary of s = z/T, for every row including masked ones) and, if
+ * row_kl is not NULL, the per-row KL (fp32 [N], 0 on masked rows).
+ * Deterministic: the same inputs give bitwise the same outputs.
+ */
+fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
+                       const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
+                       float* loss, float* row_lse, float* row_kl,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass with recomputation of the logits. row_lse is the forward's
+ * output for the same inputs. grad_loss is a device fp32 [1] holding g, or
+ * NULL for g = 1. grad_h (fp32 [N, d]) and grad_W (fp32 [V, d]) are
+ * overwritten. Masked rows get exactly zero grad_h rows.
+ */
+fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
+                        const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
+                        const float* row_lse, const float* grad_loss,
+                        float* grad_h, float* grad_W,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Checks the teacher cache on the device: every index in [0, V), no index
+ * repeated within a row, every logit finite. Writes the number of offending
+ * rows to bad_rows (device int32 [1]). The cache is the method's offline
+ * top-K store (section "Two systems changes" of the blog post).
+ */
+fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx,
+                                const float* t_logit, int32_t* bad_rows, void* stream);
+
+/* Static description of a status code. */
+const char* fkl_status_string(fkl_status status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* fkl_last_error(void);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int fkl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FKL_H */

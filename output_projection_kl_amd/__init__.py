@@ -1,0 +1,220 @@
+"""Fused output projection + sparse top-K KL loss for AMD MI355X.
+
+A thin ctypes binding over ``libfkl.so`` (C ABI declared in ``include/fkl.h``).
+Every step of the loss runs in the library's HIP kernels; this module only
+checks tensors, allocates outputs and workspace through torch, and passes
+device pointers and torch's current stream. There is no fallback: if the
+library is missing, every call raises.
+
+The method (blog post on the page "Efficient Offline Top-K Logits and Fused
+Chunked KL Loss Enable Scalable LLM Distillation", section "Two systems
+changes"): the student's output projection is fused into a KL loss against
+the teacher's cached top-K logits; the logits are formed one chunk at a time
+and never stored, and backward forms them again.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FklError",
+    "lib",
+    "library_path",
+    "Shape",
+    "workspace_size",
+    "forward",
+    "backward",
+    "validate_teacher",
+    "EXPORTED_SYMBOLS",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfkl.so"
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "fkl_workspace_size",
+    "fkl_forward",
+    "fkl_backward",
+    "fkl_validate_teacher",
+    "fkl_status_string",
+    "fkl_last_error",
+    "fkl_version",
+)
+
+
+class FklError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfkl status {status}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``fkl_shape``."""
+
+    _fields_ = [
+        ("N", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("K", ctypes.c_int32),
+        ("T", ctypes.c_float),
+        ("chunk", ctypes.c_int32),
+        ("vslab", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("FKL_LIBRARY", os.path.join(_PKG_DIR, _LIB_NAME))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfkl.so (built by ``python -m output_projection_kl_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FklError(-1, f"{path} is missing; build it with `python -m output_projection_kl_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    shp = ctypes.POINTER(Shape)
+    L.fkl_workspace_size.argtypes = [shp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
+    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_version"):
+        getattr(L, f).restype = ctypes.c_int
+    L.fkl_status_string.argtypes = [ctypes.c_int]
+    L.fkl_status_string.restype = ctypes.c_char_p
+    L.fkl_last_error.argtypes = []
+    L.fkl_last_error.restype = ctypes.c_char_p
+    L.fkl_version.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise FklError(status, f"{L.fkl_status_string(status).decode()}: {L.fkl_last_error().decode()}")
+
+
+def make_shape(N, d, V, K, T=1.0, chunk=0, vslab=0) -> Shape:
+    return Shape(int(N), int(d), int(V), int(K), float(T), int(chunk), int(vslab))
+
+
+def workspace_size(N, d, V, K, T=1.0, chunk=0, vslab=0):
+    """(forward_bytes, backward_bytes) of workspace for this shape."""
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    s = make_shape(N, d, V, K, T, chunk, vslab)
+    _check(lib().fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, shape):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _inputs(h, W, t_idx, t_logit, mask):
+    torch = _torch()
+    if h.dim() != 2 or W.dim() != 2 or t_idx.dim() != 2:
+        raise ValueError("h, W and t_idx must be 2-D")
+    N, d = h.shape
+    V = W.shape[0]
+    K = t_idx.shape[1]
+    _need(h, "h", torch.bfloat16, (N, d))
+    _need(W, "W", torch.bfloat16, (V, d))
+    _need(t_idx, "t_idx", torch.int32, (N, K))
+    _need(t_logit, "t_logit", torch.float32, (N, K))
+    if mask is not None:
+        _need(mask, "mask", torch.uint8, (N,))
+    return N, d, V, K
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vslab: int = 0,
+            workspace=None, return_row_kl: bool = False):
+    """Fused forward. Returns (loss [1], row_lse [N]) or (loss, row_lse, row_kl)."""
+    torch = _torch()
+    N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
+    s = make_shape(N, d, V, K, T, chunk, vslab)
+    fb, _ = workspace_size(N, d, V, K, T, chunk, vslab)
+    ws = _workspace(fb, h.device, workspace)
+    loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    row_lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    row_kl = torch.empty(N, dtype=torch.float32, device=h.device) if return_row_kl else None
+    _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
+                             _ptr(loss), _ptr(row_lse), _ptr(row_kl), _ptr(ws),
+                             ctypes.c_size_t(ws.numel()), _stream()))
+    return (loss, row_lse, row_kl) if return_row_kl else (loss, row_lse)
+
+
+def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss=None, chunk: int = 0,
+             vslab: int = 0, workspace=None, grad_h=None, grad_W=None):
+    """Fused backward with recomputation. Returns (grad_h fp32 [N, d], grad_W fp32 [V, d])."""
+    torch = _torch()
+    N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
+    _need(row_lse, "row_lse", torch.float32, (N,))
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss", torch.float32, (1,))
+    s = make_shape(N, d, V, K, T, chunk, vslab)
+    _, bb = workspace_size(N, d, V, K, T, chunk, vslab)
+    ws = _workspace(bb, h.device, workspace)
+    if grad_h is None:
+        grad_h = torch.empty((N, d), dtype=torch.float32, device=h.device)
+    else:
+        _need(grad_h, "grad_h", torch.float32, (N, d))
+    if grad_W is None:
+        grad_W = torch.empty((V, d), dtype=torch.float32, device=h.device)
+    else:
+        _need(grad_W, "grad_W", torch.float32, (V, d))
+    _check(lib().fkl_backward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
+                              _ptr(row_lse), _ptr(grad_loss), _ptr(grad_h), _ptr(grad_W), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream()))
+    return grad_h, grad_W
+
+
+def validate_teacher(t_idx, t_logit, V: int) -> int:
+    """Number of teacher rows with an index outside [0, V), a repeated index, or a non-finite logit."""
+    torch = _torch()
+    N, K = t_idx.shape
+    _need(t_idx, "t_idx", torch.int32, (N, K))
+    _need(t_logit, "t_logit", torch.float32, (N, K))
+    s = make_shape(N, 8, V, K, 1.0)
+    bad = torch.empty(1, dtype=torch.int32, device=t_idx.device)
+    _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad), _stream()))
+    return int(bad.item())

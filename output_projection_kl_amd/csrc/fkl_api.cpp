@@ -1,0 +1,189 @@
+// C ABI of libfkl: argument checks (pure host code, no HIP call), workspace
+// planning, and dispatch of the kernel sequences in fkl_kernels.hip.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fkl.h"
+#include "fkl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fkl_status fail(fkl_status st, const char* msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+namespace fkl {
+
+fkl_status make_plan(const fkl_shape* s, Plan* p) {
+  if (!s) return fail(FKL_EINVAL, "shape is NULL");
+  if (s->N < 0) return fail(FKL_EINVAL, "N must be >= 0");
+  if (s->N > (int64_t(1) << 31) - 1) return fail(FKL_EUNSUPPORTED, "N must be < 2^31");
+  if (s->d < 8 || s->d % 8 != 0) return fail(FKL_EINVAL, "d must be a positive multiple of 8");
+  if (s->d > 65536) return fail(FKL_EUNSUPPORTED, "d must be <= 65536");
+  if (s->V < 1) return fail(FKL_EINVAL, "V must be >= 1");
+  if (s->V > (int64_t(1) << 31) - 1024) return fail(FKL_EUNSUPPORTED, "V must be < 2^31 - 1024");
+  if (s->K < 1) return fail(FKL_EINVAL, "K must be >= 1");
+  if (s->K > 1024) return fail(FKL_EUNSUPPORTED, "K must be <= 1024");
+  if (s->K > s->V) return fail(FKL_EINVAL, "K must be <= V");
+  if (!(s->T > 0.0f) || !std::isfinite(s->T)) return fail(FKL_EINVAL, "T must be finite and > 0");
+  if (s->chunk < 0) return fail(FKL_EINVAL, "chunk must be >= 0");
+  if (s->vslab < 0) return fail(FKL_EINVAL, "vslab must be >= 0");
+
+  p->N = s->N;
+  p->d = s->d;
+  p->V = s->V;
+  p->K = s->K;
+  p->T = s->T;
+  int64_t chunk = s->chunk ? s->chunk : kDefaultChunk;
+  if (s->N > 0 && chunk > s->N) chunk = s->N;
+  p->chunk = chunk;
+  p->chunk_alloc = round_up(chunk, kTile);
+  int64_t vslab = s->vslab ? s->vslab : kDefaultSlabElems / p->chunk_alloc;
+  vslab = round_up(vslab < kTile ? kTile : vslab, kTile);
+  const int64_t v_all = round_up(s->V, kTile);
+  if (vslab > v_all) vslab = v_all;
+  p->vslab = vslab;
+  p->n_vt = ceil_div(s->V, kTile);
+  const int64_t rbs = p->chunk_alloc / kTile;
+  p->fwd_splits = static_cast<int32_t>(ceil_div(kTargetBlocks, rbs));
+
+  size_t off = 0;
+  p->off_scalars = off;
+  off += 256;
+  p->off_negent = off;
+  off = align256(off + static_cast<size_t>(p->chunk_alloc) * 4);
+  p->off_tidx = off;
+  off = align256(off + static_cast<size_t>(p->chunk_alloc) * p->K * 4);
+  p->off_tp = off;
+  off = align256(off + static_cast<size_t>(p->chunk_alloc) * p->K * 4);
+  const size_t shared_end = off;
+  // forward: split partials for up to (256 + rbs) workgroups' rows, then block sums
+  p->off_partial = off;
+  off = align256(off + static_cast<size_t>(kTargetBlocks + rbs) * kTile * 16);
+  p->off_blocksum = off;
+  off = align256(off + static_cast<size_t>(rbs) * 8);
+  p->fwd_bytes = off;
+  // backward: the bf16 gradient block of chunk_alloc x vslab
+  p->off_G = shared_end;
+  p->bwd_bytes = align256(shared_end + static_cast<size_t>(p->chunk_alloc) * p->vslab * 2);
+  return FKL_OK;
+}
+
+}  // namespace fkl
+
+extern "C" {
+
+fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t* bwd_bytes) {
+  fkl::Plan p;
+  const fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (fwd_bytes) *fwd_bytes = p.fwd_bytes;
+  if (bwd_bytes) *bwd_bytes = p.bwd_bytes;
+  return FKL_OK;
+}
+
+fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
+                       const float* t_logit, const uint8_t* row_mask, float* loss, float* row_lse,
+                       float* row_kl, void* workspace, size_t workspace_bytes, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (!loss) return fail(FKL_EINVAL, "loss is NULL");
+  if (!aligned(loss, 4)) return fail(FKL_EINVAL, "loss must be 4-byte aligned");
+  if (p.N > 0) {
+    if (!h || !W || !t_idx || !t_logit || !row_lse)
+      return fail(FKL_EINVAL, "h, W, t_idx, t_logit and row_lse must not be NULL");
+    if (!aligned(h, 16) || !aligned(W, 16)) return fail(FKL_EINVAL, "h and W must be 16-byte aligned");
+    if (!aligned(t_idx, 4) || !aligned(t_logit, 4) || !aligned(row_lse, 4) ||
+        (row_kl && !aligned(row_kl, 4)))
+      return fail(FKL_EINVAL, "t_idx, t_logit, row_lse and row_kl must be 4-byte aligned");
+  }
+  if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
+  fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
+                 loss, row_lse, row_kl, static_cast<char*>(workspace)};
+  const hipError_t e = fkl::launch_forward(p, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("forward launch failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return FKL_OK;
+}
+
+fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
+                        const float* t_logit, const uint8_t* row_mask, const float* row_lse,
+                        const float* grad_loss, float* grad_h, float* grad_W, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (!grad_W) return fail(FKL_EINVAL, "grad_W is NULL");
+  if (!aligned(grad_W, 4)) return fail(FKL_EINVAL, "grad_W must be 4-byte aligned");
+  if (grad_loss && !aligned(grad_loss, 4)) return fail(FKL_EINVAL, "grad_loss must be 4-byte aligned");
+  if (p.N > 0) {
+    if (!h || !W || !t_idx || !t_logit || !row_lse || !grad_h)
+      return fail(FKL_EINVAL, "h, W, t_idx, t_logit, row_lse and grad_h must not be NULL");
+    if (!aligned(h, 16) || !aligned(W, 16)) return fail(FKL_EINVAL, "h and W must be 16-byte aligned");
+    if (!aligned(t_idx, 4) || !aligned(t_logit, 4) || !aligned(row_lse, 4) || !aligned(grad_h, 4))
+      return fail(FKL_EINVAL, "t_idx, t_logit, row_lse and grad_h must be 4-byte aligned");
+  }
+  if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.bwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
+  fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
+                 row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
+  const hipError_t e = fkl::launch_backward(p, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("backward launch failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return FKL_OK;
+}
+
+fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx, const float* t_logit,
+                                int32_t* bad_rows, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (!bad_rows || !aligned(bad_rows, 4)) return fail(FKL_EINVAL, "bad_rows must be a 4-byte aligned pointer");
+  if (p.N > 0 && (!t_idx || !t_logit)) return fail(FKL_EINVAL, "t_idx and t_logit must not be NULL");
+  if (p.N > 0 && (!aligned(t_idx, 4) || !aligned(t_logit, 4)))
+    return fail(FKL_EINVAL, "t_idx and t_logit must be 4-byte aligned");
+  const hipError_t e =
+      fkl::launch_validate(p.N, p.V, p.K, t_idx, t_logit, bad_rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("validate launch failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return FKL_OK;
+}
+
+const char* fkl_status_string(fkl_status status) {
+  switch (status) {
+    case FKL_OK: return "ok";
+    case FKL_EINVAL: return "invalid argument";
+    case FKL_EWORKSPACE: return "workspace missing or too small";
+    case FKL_EINDEX: return "bad teacher index";
+    case FKL_EDEVICE: return "device error";
+    case FKL_EUNSUPPORTED: return "unsupported shape";
+  }
+  return "unknown status";
+}
+
+const char* fkl_last_error(void) { return g_last_error.c_str(); }
+
+int fkl_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Host-side plan and kernel launchers shared by the C-ABI layer and the
+// kernel translation unit. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fkl.h"
+
+namespace fkl {
+
+constexpr int kTile = 256;          // rows and vocabulary columns of one logits tile
+constexpr int kTargetBlocks = 256;  // workgroups a launch aims for (one per CU on MI355X)
+constexpr int kDefaultChunk = 4096;
+constexpr int64_t kDefaultSlabElems = int64_t(32) << 20;  // gradient block of ~32 Mi bf16
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// Everything derived from the shape; computed on the host only.
+struct Plan {
+  int64_t N, d, V;
+  int32_t K;
+  float T;
+  int64_t chunk;        // rows per pass (<= N rounded up to 256 when N is small)
+  int64_t chunk_alloc;  // chunk rounded up to 256
+  int64_t vslab;        // vocabulary columns per backward pass, multiple of 256
+  int64_t n_vt;         // ceil(V / 256): logits tiles along the vocabulary
+  int32_t fwd_splits;   // vocabulary splits of the forward sweep
+  // workspace offsets (bytes)
+  size_t off_scalars, off_negent, off_tidx, off_tp, off_partial, off_blocksum, fwd_bytes;
+  size_t off_G, bwd_bytes;
+};
+
+fkl_status make_plan(const fkl_shape* s, Plan* p);
+
+// Per-call device pointers of the forward pass.
+struct FwdArgs {
+  const uint16_t* h;
+  const uint16_t* W;
+  const int32_t* t_idx;
+  const float* t_logit;
+  const uint8_t* mask;
+  float* loss;
+  float* row_lse;
+  float* row_kl;
+  char* ws;
+};
+
+struct BwdArgs {
+  const uint16_t* h;
+  const uint16_t* W;
+  const int32_t* t_idx;
+  const float* t_logit;
+  const uint8_t* mask;
+  const float* row_lse;
+  const float* grad_loss;
+  float* grad_h;
+  float* grad_W;
+  char* ws;
+};
+
+hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx,
+                           const float* t_logit, int32_t* bad_rows, hipStream_t stream);
+
+}  // namespace fkl

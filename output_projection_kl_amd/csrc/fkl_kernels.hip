@@ -1,0 +1,629 @@
+// HIP kernels of libfkl for gfx950, and their launch sequences.
+//
+// Forward, per chunk of rows (blog post on the page "Efficient Offline Top-K
+// Logits and Fused Chunked KL Loss Enable Scalable LLM Distillation",
+// section "Two systems changes": logits are formed one chunk at a time,
+// folded into the running loss and dropped):
+//   k_teacher_prep  softmax of the cached teacher logits over K, its
+//                   negative entropy, and each row's (index, p) list sorted by
+//                   vocabulary index
+//   k_fwd_sweep     256-row block x a run of 256-column vocabulary tiles:
+//                   MFMA logits tile -> LDS -> per-row online max / sum of
+//                   exp2, and the logits at the teacher indices picked up by a
+//                   per-row cursor while the tile is resident
+//   k_fwd_combine   merge the vocabulary splits -> row_lse, row KL, block sums
+//   k_accumulate    fixed-order fp64 running loss
+// Backward, per chunk and vocabulary slab (same section: each chunk's logits
+// are recomputed rather than stored):
+//   k_bwd_g         logits tile again -> G = c (exp(s - lse) - p~) -> bf16
+//                   gradient block in the workspace
+//   k_gemm_acc      grad_h[chunk] (+)= G W_slab ; grad_W[slab] (+)= G^T h_chunk
+#include <climits>
+#include <cmath>
+
+#include "fkl_device.h"
+#include "fkl_internal.h"
+
+namespace fkl {
+
+struct Scalars {
+  double acc;       // running sum of valid-row KL (fp64, fixed order)
+  int64_t n_valid;  // number of valid rows
+};
+
+constexpr int kStageLd = 132;  // fp32 LDS stride of a staged 256 x 128 half tile
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__ mask, int64_t N,
+                                                     Scalars* sc) {
+  __shared__ int64_t part[256];
+  int64_t cnt = 0;
+  if (mask) {
+    for (int64_t r = threadIdx.x; r < N; r += 256) cnt += (mask[r] != 0);
+  } else if (threadIdx.x == 0) {
+    cnt = N;
+  }
+  part[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    sc->n_valid = part[0];
+    sc->acc = 0.0;
+  }
+}
+
+// One wave per row, four rows per workgroup. p = softmax(t_logit / T) over
+// the K cached entries; negent = sum_k p log p; the (index, p) pairs are
+// written in ascending index order (stable rank, so even repeated indices
+// fill every slot).
+__global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict__ t_idx,
+                                                      const float* __restrict__ t_logit, int64_t r0,
+                                                      int32_t rows, int32_t K, float invT,
+                                                      int32_t* __restrict__ tsort_idx,
+                                                      float* __restrict__ tsort_p,
+                                                      float* __restrict__ negent) {
+  __shared__ int32_t sidx[4][1024];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  const bool active = r < rows;
+  const int32_t* ti = t_idx + (r0 + r) * static_cast<int64_t>(K);
+  const float* tl = t_logit + (r0 + r) * static_cast<int64_t>(K);
+  float mx = -INFINITY;
+  if (active) {
+    for (int k = lane; k < K; k += 64) {
+      mx = fmaxf(mx, tl[k] * invT);
+      sidx[wave][k] = ti[k];
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  mx = wave_max(mx);
+  float se = 0.f;
+  for (int k = lane; k < K; k += 64) se += expf(tl[k] * invT - mx);
+  se = wave_sum(se);
+  const float lnorm = mx + logf(se);
+  float ne = 0.f;
+  int32_t* oi = tsort_idx + static_cast<int64_t>(r) * K;
+  float* op = tsort_p + static_cast<int64_t>(r) * K;
+  for (int k = lane; k < K; k += 64) {
+    const float lp = tl[k] * invT - lnorm;
+    const float p = expf(lp);
+    ne += p * lp;
+    const int32_t key = sidx[wave][k];
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int32_t o = sidx[wave][j];
+      rank += (o < key) | ((o == key) & (j < k));
+    }
+    oi[rank] = key;
+    op[rank] = p;
+  }
+  ne = wave_sum(ne);
+  if (lane == 0) negent[r] = ne;
+}
+
+__global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, Scalars* sc) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    double a = sc->acc;
+    for (int i = 0; i < nblocks; ++i) a += block_sum[i];
+    sc->acc = a;
+  }
+}
+
+__global__ void k_finalize(const Scalars* sc, float T, float* loss) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const int64_t n = sc->n_valid;
+    loss[0] = n > 0 ? static_cast<float>(static_cast<double>(T) * T * sc->acc / static_cast<double>(n))
+                    : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n; i += stride)
+    p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row sorted teacher cursor
+// ---------------------------------------------------------------------------
+
+struct Cursor {
+  const int32_t* idx;
+  const float* p;
+  int pos, K;
+  int cur;    // current index, INT_MAX when exhausted
+  float cp;   // its probability
+
+  __device__ __forceinline__ void init(const int32_t* i, const float* pp, int k, int target, bool on) {
+    idx = i;
+    p = pp;
+    K = k;
+    cur = INT_MAX;
+    cp = 0.f;
+    pos = k;
+    if (!on) return;
+    int lo = 0, hi = k;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (idx[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    pos = lo;
+    if (pos < K) {
+      cur = idx[pos];
+      cp = p[pos];
+    }
+  }
+  __device__ __forceinline__ void next() {
+    ++pos;
+    if (pos < K) {
+      cur = idx[pos];
+      cp = p[pos];
+    } else {
+      cur = INT_MAX;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Forward sweep
+// ---------------------------------------------------------------------------
+
+struct FwdSweepParams {
+  const uint16_t* h;
+  const uint16_t* W;
+  int64_t d, V;
+  int64_t r0;
+  int32_t rows, K;
+  float k2;  // log2(e) / T
+  const int32_t* tsort_idx;
+  const float* tsort_p;
+  int32_t n_vt, tiles_per_split;
+  f32x4* partial;  // [splits][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
+  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int rb = blockIdx.x;
+  const int split = blockIdx.y;
+  const int vt0 = split * P.tiles_per_split;
+  const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
+  const int row = rb * kTile + tid;  // chunk-local row whose statistics this thread keeps
+  const bool row_ok = row < P.rows;
+
+  Cursor cur;
+  cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
+           P.K, vt0 * kTile, row_ok && vt0 < vt1);
+
+  const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
+  const Operand B{P.W, P.d, P.V, P.d};
+  const int64_t kdepth = (P.d + kBK - 1) / kBK * kBK;  // loaders zero-fill past d
+  float* stage = reinterpret_cast<float*>(lds);
+  float m2 = -INFINITY, se = 0.f, gz = 0.f;
+
+  for (int vt = vt0; vt < vt1; ++vt) {
+    f32x16 acc[4][4];
+    zero_acc<256>(acc);
+    gemm_mainloop<256, false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
+                                     static_cast<int64_t>(vt) * kTile, 0, kdepth, acc, lds);
+    for (int half = 0; half < 2; ++half) {
+      if (wn == half) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + acc_col(nb, lane)] = acc[mb][nb][i];
+      }
+      __syncthreads();
+      const int64_t col0 = static_cast<int64_t>(vt) * kTile + half * 128;
+      const int nvalid = static_cast<int>(min<int64_t>(128, P.V - col0));
+      if (nvalid > 0) {
+        const float* sr = stage + tid * kStageLd;
+        float mx = -INFINITY;
+        if (nvalid == 128) {
+#pragma unroll 8
+          for (int c = 0; c < 128; c += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
+            mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+          }
+        } else {
+          for (int c = 0; c < nvalid; ++c) mx = fmaxf(mx, sr[c]);
+        }
+        const float mnew = fmaxf(m2, mx * P.k2);
+        float s = 0.f;
+        if (nvalid == 128) {
+#pragma unroll 8
+          for (int c = 0; c < 128; c += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
+            s += __builtin_amdgcn_exp2f(fmaf(x[0], P.k2, -mnew));
+            s += __builtin_amdgcn_exp2f(fmaf(x[1], P.k2, -mnew));
+            s += __builtin_amdgcn_exp2f(fmaf(x[2], P.k2, -mnew));
+            s += __builtin_amdgcn_exp2f(fmaf(x[3], P.k2, -mnew));
+          }
+        } else {
+          for (int c = 0; c < nvalid; ++c) s += __builtin_amdgcn_exp2f(fmaf(sr[c], P.k2, -mnew));
+        }
+        se = se * __builtin_amdgcn_exp2f(m2 - mnew) + s;
+        m2 = mnew;
+        const int c0 = static_cast<int>(col0);
+        while (cur.cur < c0 + 128) {
+          if (cur.cur >= c0) gz += cur.cp * sr[cur.cur - c0];
+          cur.next();
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int ld = gridDim.x * kTile;
+  P.partial[static_cast<int64_t>(split) * ld + row] = f32x4{m2, se, gz, 0.f};
+}
+
+// One thread per row of the chunk: merge the split statistics.
+__global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int splits,
+                                                     int rows, int64_t r0,
+                                                     const float* __restrict__ negent,
+                                                     const uint8_t* __restrict__ mask, float invT,
+                                                     float* __restrict__ row_lse,
+                                                     float* __restrict__ row_kl,
+                                                     double* __restrict__ block_sum) {
+  __shared__ double red[256];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int ld = gridDim.x * 256;
+  double kl_d = 0.0;
+  if (r < rows) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
+    float sum = 0.f, gz = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const f32x4 pr = partial[static_cast<int64_t>(s) * ld + r];
+      if (pr[1] > 0.f) sum += pr[1] * exp2f(pr[0] - M);
+      gz += pr[2];
+    }
+    const float lse = (M + log2f(sum)) * kLn2;
+    const float kl = negent[r] - gz * invT + lse;
+    const bool valid = !mask || mask[r0 + r] != 0;
+    row_lse[r0 + r] = lse;
+    if (row_kl) row_kl[r0 + r] = valid ? kl : 0.f;
+    kl_d = valid ? static_cast<double>(kl) : 0.0;
+  }
+  red[threadIdx.x] = kl_d;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_sum[blockIdx.x] = red[0];
+}
+
+// ---------------------------------------------------------------------------
+// Backward: recompute the logits tile and form the bf16 gradient block
+// ---------------------------------------------------------------------------
+
+struct BwdGParams {
+  const uint16_t* h;
+  const uint16_t* W;
+  int64_t d, V;
+  int64_t r0;
+  int32_t rows, K;
+  float k2, T;
+  const int32_t* tsort_idx;
+  const float* tsort_p;
+  const float* row_lse;
+  const uint8_t* mask;
+  const float* grad_loss;
+  const Scalars* sc;
+  int64_t slab0;
+  int32_t slab_w;
+  int64_t vslab;
+  uint16_t* G;  // [chunk_alloc][vslab]
+  int32_t n_vt, tiles_per_split;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
+  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
+  __shared__ float s_lse2[kTile];
+  __shared__ float s_c[kTile];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int rb = blockIdx.x;
+  const int vt0 = blockIdx.y * P.tiles_per_split;
+  const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
+  const int row = rb * kTile + tid;
+  const int64_t grow = P.r0 + row;
+
+  float c = 0.f, lse2 = 0.f;
+  if (row < P.rows) {
+    const int64_t n = P.sc->n_valid;
+    const float g = P.grad_loss ? P.grad_loss[0] : 1.0f;
+    const bool valid = !P.mask || P.mask[grow] != 0;
+    c = (valid && n > 0) ? static_cast<float>(static_cast<double>(g) * P.T / static_cast<double>(n)) : 0.f;
+    lse2 = P.row_lse[grow] * kLog2e;
+  }
+  s_lse2[tid] = lse2;
+  s_c[tid] = c;
+  Cursor cur;
+  cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
+           P.K, static_cast<int>(P.slab0) + vt0 * kTile, c != 0.f && vt0 < vt1);
+  __syncthreads();
+
+  const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
+  const Operand B{P.W, P.d, P.V, P.d};
+  const int64_t kdepth = (P.d + kBK - 1) / kBK * kBK;
+  float* stage = reinterpret_cast<float*>(lds);
+  const int64_t slab_end = P.slab0 + P.slab_w;
+
+  for (int vt = vt0; vt < vt1; ++vt) {
+    f32x16 acc[4][4];
+    zero_acc<256>(acc);
+    const int64_t vbase = P.slab0 + static_cast<int64_t>(vt) * kTile;
+    gemm_mainloop<256, false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, 0, kdepth,
+                                     acc, lds);
+    for (int half = 0; half < 2; ++half) {
+      const int64_t col0 = vbase + half * 128;
+      if (wn == half) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wm * 128 + acc_row(mb, i, lane);
+            const float l2 = s_lse2[r];
+            const float cc = s_c[r];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int col = acc_col(nb, lane);
+              float v = 0.f;
+              if (cc != 0.f && col0 + col < slab_end)
+                v = cc * __builtin_amdgcn_exp2f(fmaf(acc[mb][nb][i], P.k2, -l2));
+              stage[r * kStageLd + col] = v;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      {
+        const int c0 = static_cast<int>(col0);
+        float* sr = stage + tid * kStageLd;
+        while (cur.cur < c0 + 128) {
+          if (cur.cur >= c0) sr[cur.cur - c0] -= c * cur.cp;
+          cur.next();
+        }
+      }
+      __syncthreads();
+      uint16_t* gdst = P.G + static_cast<int64_t>(rb) * kTile * P.vslab + static_cast<int64_t>(vt) * kTile +
+                       half * 128;
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int q = tid + i * kThreads;
+        const int r = q >> 4;
+        const int cc8 = (q & 15) * 8;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + cc8);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + cc8 + 4);
+        bf16x8 o;
+        o[0] = static_cast<__bf16>(x0[0]);
+        o[1] = static_cast<__bf16>(x0[1]);
+        o[2] = static_cast<__bf16>(x0[2]);
+        o[3] = static_cast<__bf16>(x0[3]);
+        o[4] = static_cast<__bf16>(x1[0]);
+        o[5] = static_cast<__bf16>(x1[1]);
+        o[6] = static_cast<__bf16>(x1[2]);
+        o[7] = static_cast<__bf16>(x1[3]);
+        *reinterpret_cast<bf16x8*>(gdst + static_cast<int64_t>(r) * P.vslab + cc8) = o;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward contractions with an fp32 read-modify-write epilogue
+// ---------------------------------------------------------------------------
+
+struct GemmAccParams {
+  Operand A, B;
+  int64_t kend;
+  float* C;
+  int64_t ldc, m_lim, n_lim;
+  int32_t beta;  // 0: C = A B^T, 1: C += A B^T
+};
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
+  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTile;
+  f32x16 acc[4][4];
+  zero_acc<256>(acc);
+  gemm_mainloop<256, TA, TB>(P.A, P.B, m0, n0, 0, P.kend, acc, lds);
+  float* ctile = P.C + m0 * P.ldc + n0;
+  const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
+  const int cmax = static_cast<int>(min<int64_t>(kTile, P.n_lim - n0));
+  const uint32_t ldc = static_cast<uint32_t>(P.ldc);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = wm * 128 + acc_row(mb, i, lane);
+      if (r >= rmax) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int c = wn * 128 + acc_col(nb, lane);
+        if (c < cmax) {
+          float* dst = ctile + (static_cast<uint32_t>(r) * ldc + static_cast<uint32_t>(c));
+          const float v = acc[mb][nb][i];
+          *dst = P.beta ? *dst + v : v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Teacher-cache validation: one wave per row
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ t_idx,
+                                                  const float* __restrict__ t_logit, int64_t N,
+                                                  int64_t V, int32_t K, int32_t* bad_rows) {
+  __shared__ int32_t sidx[4][1024];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x * 4LL + wave;
+  const bool active = r < N;
+  int bad = 0;
+  if (active) {
+    for (int k = lane; k < K; k += 64) {
+      const int32_t v = t_idx[r * K + k];
+      sidx[wave][k] = v;
+      const float x = t_logit[r * K + k];
+      bad |= (v < 0) | (v >= V) | !isfinite(x);
+    }
+  }
+  __syncthreads();
+  if (active) {
+    for (int k = lane; k < K; k += 64) {
+      const int32_t key = sidx[wave][k];
+      for (int j = 0; j < k; ++j) bad |= (sidx[wave][j] == key);
+    }
+    const unsigned long long any = __ballot(bad);
+    if (lane == 0 && any) atomicAdd(bad_rows, 1);
+  }
+}
+
+__global__ void k_set_int(int32_t* p, int32_t v) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequences
+// ---------------------------------------------------------------------------
+
+static inline int splits_for(int64_t rbs, int64_t tiles) {
+  int64_t s = ceil_div(kTargetBlocks, rbs);
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
+  Scalars* sc = reinterpret_cast<Scalars*>(a.ws + p.off_scalars);
+  float* negent = reinterpret_cast<float*>(a.ws + p.off_negent);
+  int32_t* tidx = reinterpret_cast<int32_t*>(a.ws + p.off_tidx);
+  float* tp = reinterpret_cast<float*>(a.ws + p.off_tp);
+  f32x4* partial = reinterpret_cast<f32x4*>(a.ws + p.off_partial);
+  double* bsum = reinterpret_cast<double*>(a.ws + p.off_blocksum);
+  const float invT = 1.0f / p.T;
+  const float k2 = kLog2e / p.T;
+
+  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
+    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+    const int rbs = static_cast<int>(ceil_div(rows, kTile));
+    hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
+                       c0, rows, p.K, invT, tidx, tp, negent);
+    const int want = splits_for(rbs, p.n_vt);
+    const int tps = static_cast<int>(ceil_div(p.n_vt, want));
+    const int splits = static_cast<int>(ceil_div(p.n_vt, tps));
+    FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, tidx, tp,
+                      static_cast<int32_t>(p.n_vt), tps, partial};
+    hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs, splits), dim3(kThreads), 0, st, fp);
+    hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, splits, rows, c0, negent,
+                       a.mask, invT, a.row_lse, a.row_kl, bsum);
+    hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, rbs, sc);
+  }
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, sc, p.T, a.loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
+  Scalars* sc = reinterpret_cast<Scalars*>(a.ws + p.off_scalars);
+  float* negent = reinterpret_cast<float*>(a.ws + p.off_negent);
+  int32_t* tidx = reinterpret_cast<int32_t*>(a.ws + p.off_tidx);
+  float* tp = reinterpret_cast<float*>(a.ws + p.off_tp);
+  uint16_t* G = reinterpret_cast<uint16_t*>(a.ws + p.off_G);
+  const float invT = 1.0f / p.T;
+  const float k2 = kLog2e / p.T;
+  const int dblocks = static_cast<int>(ceil_div(p.d, kTile));
+
+  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
+  if (p.N == 0) {
+    hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, a.grad_W, p.V * p.d);
+    return hipGetLastError();
+  }
+  const int64_t n_slabs = ceil_div(p.V, p.vslab);
+  int64_t chunk_index = 0;
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk, ++chunk_index) {
+    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+    const int rbs = static_cast<int>(ceil_div(rows, kTile));
+    hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
+                       c0, rows, p.K, invT, tidx, tp, negent);
+    for (int64_t s = 0; s < n_slabs; ++s) {
+      const int64_t slab0 = s * p.vslab;
+      const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
+      const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
+      const int want = splits_for(rbs, nvt);
+      const int tps = static_cast<int>(ceil_div(nvt, want));
+      const int splits = static_cast<int>(ceil_div(nvt, tps));
+      BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
+                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, tps};
+      hipLaunchKernelGGL(k_bwd_g, dim3(rbs, splits), dim3(kThreads), 0, st, gp);
+
+      // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w]
+      GemmAccParams hp;
+      hp.A = Operand{G, p.vslab, p.chunk_alloc, p.vslab};
+      hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, p.V - slab0};
+      hp.kend = round_up(slab_w, kBK);
+      hp.C = a.grad_h + c0 * p.d;
+      hp.ldc = p.d;
+      hp.m_lim = rows;
+      hp.n_lim = p.d;
+      hp.beta = s > 0;
+      hipLaunchKernelGGL((k_gemm_acc<false, true>), dim3(rbs, dblocks), dim3(kThreads), 0, st, hp);
+
+      // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows]
+      GemmAccParams wp;
+      wp.A = Operand{G, p.vslab, p.vslab, rows};
+      wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
+      wp.kend = round_up(rows, kBK);
+      wp.C = a.grad_W + slab0 * p.d;
+      wp.ldc = p.d;
+      wp.m_lim = slab_w;
+      wp.n_lim = p.d;
+      wp.beta = chunk_index > 0;
+      hipLaunchKernelGGL((k_gemm_acc<true, true>), dim3(nvt, dblocks), dim3(kThreads), 0, st, wp);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx, const float* t_logit,
+                           int32_t* bad_rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, st, bad_rows, 0);
+  if (N > 0)
+    hipLaunchKernelGGL(k_validate, dim3(ceil_div(N, 4)), dim3(256), 0, st, t_idx, t_logit, N, V, K,
+                       bad_rows);
+  return hipGetLastError();
+}
+
+}  // namespace fkl

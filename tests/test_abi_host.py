@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, plans workspace, and rejects bad arguments before touching a
+device (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import output_projection_kl_amd as fkl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fkl.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fkl_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(fkl.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fkl.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fkl.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert L.fkl_version() >= 100
+
+
+def test_status_strings():
+    L = fkl.lib()
+    for code in range(6):
+        assert L.fkl_status_string(code)
+    assert L.fkl_status_string(99) == b"unknown status"
+
+
+def test_workspace_is_independent_of_rows():
+    a = fkl.workspace_size(65536, 2880, 201088, 100, 1.0, chunk=4096)
+    b = fkl.workspace_size(262144, 2880, 201088, 100, 1.0, chunk=4096)
+    assert a == b
+    fwd, bwd = a
+    # backward holds one bf16 gradient block of chunk x vslab (32 Mi elements by default)
+    assert 64 << 20 <= bwd <= (64 << 20) + (16 << 20)
+    assert fwd < 16 << 20
+
+
+def test_workspace_scales_with_chunk_and_slab():
+    _, b1 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096, vslab=4096)
+    _, b2 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096, vslab=8192)
+    assert b2 - b1 == 4096 * 4096 * 2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("N", -1, 1), ("d", 12, 1), ("d", 0, 1), ("V", 0, 1), ("K", 0, 1), ("K", 2000, 5),
+    ("T", 0.0, 1), ("T", -1.0, 1), ("T", float("inf"), 1), ("chunk", -3, 1), ("vslab", -1, 1),
+])
+def test_shape_errors(field, value, status):
+    s = fkl.make_shape(16, 64, 100, 5)
+    setattr(s, field, value)
+    f = ctypes.c_size_t(0)
+    b = ctypes.c_size_t(0)
+    assert fkl.lib().fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)) == status
+    assert fkl.lib().fkl_last_error()
+
+
+def test_k_larger_than_v_rejected():
+    s = fkl.make_shape(4, 64, 10, 11)
+    assert fkl.lib().fkl_workspace_size(ctypes.byref(s), None, None) == 1
+
+
+def _fwd(s, h=8192, W=16384, ti=4096, tl=4096, loss=256, lse=256, ws=1 << 20, ws_bytes=1 << 30):
+    vp = ctypes.c_void_p
+    return fkl.lib().fkl_forward(ctypes.byref(s), vp(h), vp(W), vp(ti), vp(tl), vp(0), vp(loss), vp(lse),
+                                 vp(0), vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
+
+
+def test_forward_argument_errors_before_any_device_work():
+    s = fkl.make_shape(16, 64, 100, 5)
+    assert _fwd(s, h=0) == 1            # NULL h
+    assert _fwd(s, W=8) == 1            # misaligned W (needs 16 bytes)
+    assert _fwd(s, lse=2) == 1          # misaligned row_lse
+    assert _fwd(s, loss=0) == 1         # NULL loss
+    assert _fwd(s, ws=0) == 2           # NULL workspace
+    assert _fwd(s, ws=1 << 20 | 16) == 2  # misaligned workspace
+    assert _fwd(s, ws_bytes=16) == 2    # workspace too small
+    assert b"workspace" in fkl.lib().fkl_last_error()
+
+
+def test_backward_argument_errors_before_any_device_work():
+    L = fkl.lib()
+    s = fkl.make_shape(16, 64, 100, 5)
+    vp = ctypes.c_void_p
+
+    def bwd(grad_h=8192, grad_W=16384, ws_bytes=1 << 30, grad_loss=0):
+        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(256),
+                              vp(grad_loss), vp(grad_h), vp(grad_W), vp(1 << 20), ctypes.c_size_t(ws_bytes),
+                              vp(0))
+    assert bwd(grad_h=0) == 1
+    assert bwd(grad_W=0) == 1
+    assert bwd(grad_W=2) == 1
+    assert bwd(grad_loss=6) == 1
+    assert bwd(ws_bytes=100) == 2
+
+
+def test_validate_argument_errors():
+    L = fkl.lib()
+    s = fkl.make_shape(16, 64, 100, 5)
+    vp = ctypes.c_void_p
+    assert L.fkl_validate_teacher(ctypes.byref(s), vp(4096), vp(4096), vp(0), vp(0)) == 1
+    assert L.fkl_validate_teacher(ctypes.byref(s), vp(0), vp(4096), vp(256), vp(0)) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fkl, "_lib", None)
+    monkeypatch.setenv("FKL_LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(fkl.FklError):
+        fkl.lib()

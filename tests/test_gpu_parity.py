@@ -1,0 +1,226 @@
+"""GPU parity of libfkl (through its C ABI) against the fp64 oracle.
+
+Tolerances, for bf16 inputs with fp32 accumulation:
+  loss:            |loss - loss_ref| / |loss_ref| <= 1e-3
+  grad_h, grad_W:  max |grad - grad_ref| / max |grad_ref| <= 2e-2 (each tensor)
+  row_lse:         max |row_lse - ref| <= 1e-3
+Both sides read the same bf16-exact h, W and the same teacher cache.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import output_projection_kl_amd as fkl
+from workloads import bf16_to_f32, make_workload
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-3
+GRAD_TOL = 2e-2
+LSE_ATOL = 1e-3
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _bits_to_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _upload(wl, dev):
+    h = _bits_to_dev(wl.h_bits, dev)
+    W = _bits_to_dev(wl.W_bits, dev)
+    ti = torch.from_numpy(wl.t_idx).to(dev)
+    tl = torch.from_numpy(wl.t_logit).to(dev)
+    m = torch.from_numpy(wl.mask).to(dev) if wl.mask is not None else None
+    return h, W, ti, tl, m
+
+
+def _rel_max(got, ref):
+    scale = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))
+
+
+def _run_gpu(h, W, ti, tl, m, T, chunk=0, vslab=0, grad_loss=None):
+    loss, lse, kl = fkl.forward(h, W, ti, tl, T=T, mask=m, chunk=chunk, vslab=vslab, return_row_kl=True)
+    gl = None if grad_loss is None else torch.tensor([grad_loss], dtype=torch.float32, device=h.device)
+    gh, gW = fkl.backward(h, W, ti, tl, lse, T=T, mask=m, grad_loss=gl, chunk=chunk, vslab=vslab)
+    torch.cuda.synchronize()
+    return (loss.item(), lse.cpu().numpy(), kl.cpu().numpy(), gh.cpu().numpy(), gW.cpu().numpy())
+
+
+def _check_full(wl, T=None, chunk=0, vslab=0, grad_loss=1.0, label=""):
+    dev = _dev()
+    T = wl.T if T is None else T
+    print(f"[parity] {label} N={wl.N} d={wl.d} V={wl.V} K={wl.K} T={T} chunk={chunk} vslab={vslab}",
+          flush=True)
+    h, W, ti, tl, m = _upload(wl, dev)
+    loss, lse, kl, gh, gW = _run_gpu(h, W, ti, tl, m, T, chunk, vslab,
+                                     None if grad_loss == 1.0 else grad_loss)
+    hf, Wf = wl.h(), wl.W()
+    r_loss, r_lse, r_kl = oracle.forward(hf, Wf, wl.t_idx, wl.t_logit, T, wl.mask)
+    r_gh, r_gW = oracle.backward(hf, Wf, wl.t_idx, wl.t_logit, T, wl.mask, grad_loss=grad_loss)
+    e_loss = abs(loss - r_loss) / max(abs(r_loss), 1e-30)
+    e_lse = float(np.abs(lse - r_lse).max()) if wl.N else 0.0
+    e_gh = _rel_max(gh, r_gh) if wl.N else 0.0
+    e_gW = _rel_max(gW, r_gW)
+    print(f"   loss {loss:.8g} ref {r_loss:.8g} rel {e_loss:.2e} | lse {e_lse:.2e} | "
+          f"grad_h {e_gh:.2e} | grad_W {e_gW:.2e}", flush=True)
+    assert e_loss <= LOSS_RTOL
+    assert e_lse <= LSE_ATOL
+    assert e_gh <= GRAD_TOL
+    assert e_gW <= GRAD_TOL
+    if wl.N:
+        valid = np.ones(wl.N, bool) if wl.mask is None else wl.mask.astype(bool)
+        assert np.abs(kl[valid] - r_kl[valid]).max() <= 1e-3 * max(1.0, np.abs(r_kl).max())
+        assert np.all(kl[~valid] == 0.0)
+        assert np.all(gh[~valid] == 0.0)
+    return loss, lse, gh, gW
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_tiny(seed, T):
+    wl = make_workload("tiny", seed_offset=seed)
+    _check_full(wl, T=T, chunk=wl.chunk, label="tiny")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_random_mask_multi_slab(seed):
+    wl = make_workload("tiny", seed_offset=seed, mask="random25")
+    _check_full(wl, chunk=64, vslab=1024, label="tiny-mask-slabs")
+
+
+def test_ragged_shapes():
+    """N, d and V off every tile size; several chunks and vocabulary slabs, and a ragged tail."""
+    wl = make_workload("tiny", N=300, d=136, V=5000, K=7, mask="random25")
+    _check_full(wl, T=0.7, chunk=128, vslab=768, grad_loss=2.5, label="ragged")
+
+
+def test_single_teacher_entry():
+    wl = make_workload("tiny", N=96, d=64, V=1000, K=1)
+    _check_full(wl, T=1.0, chunk=64, label="K=1")
+
+
+def test_teacher_covers_vocabulary():
+    wl = make_workload("tiny", N=40, d=64, V=64, K=64)
+    _check_full(wl, T=1.5, label="K=V")
+
+
+def test_zipf_teacher_reduced_vocab():
+    wl = make_workload("llama3b", N=512, d=192, V=9000)
+    _check_full(wl, chunk=256, vslab=2048, label="zipf")
+
+
+def test_empty_rows():
+    dev = _dev()
+    d, V, K = 64, 300, 5
+    h = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    W = torch.randn((V, d), device=dev).to(torch.bfloat16)
+    ti = torch.empty((0, K), dtype=torch.int32, device=dev)
+    tl = torch.empty((0, K), dtype=torch.float32, device=dev)
+    loss, lse = fkl.forward(h, W, ti, tl)
+    gh, gW = fkl.backward(h, W, ti, tl, lse)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0
+    assert gW.abs().max().item() == 0.0 and gh.numel() == 0
+
+
+def test_all_rows_masked():
+    wl = make_workload("tiny", N=100, d=64, V=700, K=4)
+    wl.mask = np.zeros(wl.N, np.uint8)
+    dev = _dev()
+    h, W, ti, tl, m = _upload(wl, dev)
+    loss, lse, kl, gh, gW = _run_gpu(h, W, ti, tl, m, 1.0)
+    assert loss == 0.0 and np.all(kl == 0) and np.all(gh == 0) and np.all(gW == 0)
+    r_lse = oracle.forward(wl.h(), wl.W(), wl.t_idx, wl.t_logit, 1.0, wl.mask)[1]
+    assert np.abs(lse - r_lse).max() <= LSE_ATOL
+
+
+def test_self_distillation_is_near_zero():
+    """Teacher = the student's own logits at K indices with a wide margin: KL ~ 0 (closed form).
+
+    h is the min-norm solution of W[idx] h = 400 + noise, so the other logits
+    spread with std 400 * sqrt(K/d) = 50 and stay ~200 below the teacher's.
+    """
+    dev = _dev()
+    rng = np.random.default_rng(2024)
+    N, d, V, K = 256, 1024, 4096, 16
+    W32 = (rng.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32)
+    from workloads import bf16_bits
+    Wb = bf16_bits(W32)
+    Wf = bf16_to_f32(Wb).astype(np.float64)
+    t_idx = np.stack([rng.choice(V, K, replace=False) for _ in range(N)]).astype(np.int32)
+    tgt = rng.standard_normal((N, K)) + 400.0
+    h64 = np.stack([np.linalg.lstsq(Wf[t_idx[r]], tgt[r], rcond=None)[0] for r in range(N)])
+    hb = bf16_bits(h64.astype(np.float32))
+    hf = bf16_to_f32(hb).astype(np.float64)
+    t_logit = np.take_along_axis(hf @ Wf.T, t_idx.astype(np.int64), axis=1).astype(np.float32)
+    r_loss = oracle.forward(hf, Wf, t_idx, t_logit, 1.0)[0]
+    h = _bits_to_dev(hb, dev)
+    W = _bits_to_dev(Wb, dev)
+    loss, lse = fkl.forward(h, W, torch.from_numpy(t_idx).to(dev), torch.from_numpy(t_logit).to(dev))
+    torch.cuda.synchronize()
+    print(f"[self-distill] gpu {loss.item():.3e} oracle {r_loss:.3e}", flush=True)
+    assert abs(r_loss) < 1e-3
+    assert abs(loss.item()) < 2e-3
+
+
+def test_chunk_invariance():
+    dev = _dev()
+    wl = make_workload("tiny", seed_offset=5, mask="random25")
+    h, W, ti, tl, m = _upload(wl, dev)
+    outs = [_run_gpu(h, W, ti, tl, m, 1.0, chunk=c) for c in (64, 100, 256)]
+    for o in outs[1:]:
+        assert abs(o[0] - outs[0][0]) <= 1e-6 * abs(outs[0][0])
+        assert np.abs(o[1] - outs[0][1]).max() <= 1e-5
+        assert _rel_max(o[3], outs[0][3]) <= 1e-3
+        assert _rel_max(o[4], outs[0][4]) <= 1e-3
+
+
+def test_bitwise_determinism():
+    dev = _dev()
+    wl = make_workload("tiny", seed_offset=7)
+    h, W, ti, tl, m = _upload(wl, dev)
+    a = _run_gpu(h, W, ti, tl, m, 1.0, chunk=64, vslab=1024)
+    b = _run_gpu(h, W, ti, tl, m, 1.0, chunk=64, vslab=1024)
+    assert a[0] == b[0]
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(x, y)
+
+
+def test_validate_teacher():
+    dev = _dev()
+    wl = make_workload("tiny", N=64, d=64, V=500, K=9)
+    ti = torch.from_numpy(wl.t_idx).to(dev)
+    tl = torch.from_numpy(wl.t_logit).to(dev)
+    assert fkl.validate_teacher(ti, tl, wl.V) == 0
+    bad_i = wl.t_idx.copy()
+    bad_l = wl.t_logit.copy()
+    bad_i[3, 2] = bad_i[3, 5]          # repeated index
+    bad_i[10, 0] = wl.V                # out of range
+    bad_i[11, 4] = -1                  # negative
+    bad_l[20, 1] = np.nan              # non-finite logit
+    n_bad = fkl.validate_teacher(torch.from_numpy(bad_i).to(dev), torch.from_numpy(bad_l).to(dev), wl.V)
+    assert n_bad == 4
+
+
+def test_caller_workspace_reuse():
+    """One workspace buffer serves repeated calls; results match fresh allocations."""
+    dev = _dev()
+    wl = make_workload("tiny", seed_offset=3)
+    h, W, ti, tl, m = _upload(wl, dev)
+    fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, 1.0, chunk=64)
+    ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
+    l1, lse1 = fkl.forward(h, W, ti, tl, chunk=64, workspace=ws)
+    g1 = fkl.backward(h, W, ti, tl, lse1, chunk=64, workspace=ws)
+    l2, lse2 = fkl.forward(h, W, ti, tl, chunk=64)
+    g2 = fkl.backward(h, W, ti, tl, lse2, chunk=64)
+    torch.cuda.synchronize()
+    assert l1.item() == l2.item()
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
