@@ -1,0 +1,212 @@
+"""Benchmark of the fused chunked KL loss (forward + backward with recompute) on one MI355X.
+
+One step = fkl_forward + fkl_backward over the whole GPT-OSS-20B-like head
+workload (N=32768 tokens, d=2880, V=201088, K=100 cached teacher entries,
+T=1, chunk=4096), inputs resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+
+Throughput: value = tokens/s = N / step time; TFLOP/s counts 8*N*d*V per step
+(2NdV forward logits, 2NdV recomputed logits, 2NdV grad_h, 2NdV grad_W).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused KL fwd+bwd tokens/s & TFLOP/s (V=201088,d=2880,N=32K); peak GiB"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "gptoss20b"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "output_projection_kl_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, rows: int):
+    """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    h = wl.h[:rows].float().cpu().numpy()
+    W = wl.W.float().cpu().numpy()
+    ti = wl.t_idx_np[:rows]
+    tl = wl.t_logit_np[:rows]
+    t0 = time.perf_counter()
+    oracle.forward(h, W, ti, tl, wl.T, None, chunk=rows)
+    oracle.backward(h, W, ti, tl, wl.T, None, chunk=rows)
+    dt = time.perf_counter() - t0
+    flops = 8.0 * rows * wl.d * wl.V
+    return {
+        "value": rows / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"first {rows} of {wl.N} rows of the same workload, forward + backward over the full "
+                   f"vocabulary in numpy fp64 (BLAS threads={threads}); {dt:.1f} s, "
+                   f"{flops / dt / 1e9:.1f} GFLOP/s"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the path is "
+              "single-GPU: no collectives or sharding)", file=sys.stderr)
+        return 2
+
+    import torch
+    import output_projection_kl_amd as fkl
+    from workloads.device import make_device_workload
+
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {WORKLOAD} inputs on {torch.cuda.get_device_name(dev)}", file=sys.stderr,
+          flush=True)
+    wl = make_device_workload(WORKLOAD, dev)
+    torch.cuda.synchronize()
+    fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, wl.T, chunk=wl.chunk)
+    ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    grad_h = torch.empty((wl.N, wl.d), dtype=torch.float32, device=dev)
+    grad_W = torch.empty((wl.V, wl.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    in_out_bytes = sum(t.numel() * t.element_size() for t in
+                       (wl.h, wl.W, wl.t_idx, wl.t_logit, row_lse, grad_h, grad_W))
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    def step():
+        fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, mask=wl.mask, chunk=wl.chunk, workspace=ws,
+                    loss=loss, row_lse=row_lse)
+        fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, row_lse, T=wl.T, mask=wl.mask, chunk=wl.chunk,
+                     workspace=ws, grad_h=grad_h, grad_W=grad_W)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    trace = not args.no_trace
+    if trace:
+        fkl.trace_read()
+        fkl.trace_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    if trace:
+        fkl.trace_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    peak = torch.cuda.max_memory_allocated(dev)
+    kstats = fkl.trace_read() if trace else []
+    flops_step = 8.0 * wl.N * wl.d * wl.V
+    tokens_s = wl.N / (ms / 1e3)
+    tflops = flops_step / (ms / 1e3) / 1e12
+
+    roofline = None
+    kernels = {}
+    for k in kstats:
+        avg = k["total_ms"] / max(k["launches"], 1)
+        kernels[k["name"]] = {
+            "launches_per_step": k["launches"] / args.steps,
+            "avg_ms": avg,
+            "share": k["total_ms"] / (ms * args.steps),
+            "tflops": (k["flops"] / k["launches"]) / (avg / 1e3) / 1e12 if k["flops"] else None,
+        }
+    mfma = [k for k in kstats if k["flops"] > 0]
+    if mfma:
+        dom = max(mfma, key=lambda k: k["total_ms"])
+        avg_s = dom["total_ms"] / dom["launches"] / 1e3
+        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        roofline = {
+            "bound": "mfma",
+            "kernel": dom["name"],
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(dom["name"]),
+            "avg_launch_ms": round(avg_s * 1e3, 4),
+            "flops_per_launch": dom["flops"] / dom["launches"],
+        }
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.describe(), "N": wl.N, "d": wl.d, "V": wl.V, "K": wl.K, "T": wl.T,
+                   "chunk": wl.chunk, "teacher": "zipf(1.1)+uniform top-100, logits N(0,9) sorted"},
+        "tflops": round(tflops, 1),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "peak_gib": round(peak / 2**30, 3),
+        "extra_gib": round((peak - in_out_bytes) / 2**30, 3),
+        "inputs_outputs_gib": round(in_out_bytes / 2**30, 3),
+        "loss": float(loss.item()),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

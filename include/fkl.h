@@ -112,6 +112,34 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
 fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx,
                                 const float* t_logit, int32_t* bad_rows, void* stream);
 
+/*
+ * Kernel timing. While enabled (a process-wide switch), every launch of the
+ * path's main kernels is bracketed by a pair of hipEvents recorded on the
+ * call's own stream, tagged with the kernel name and the launch's
+ * algorithmic work: FLOPs of its contractions (2 per multiply-add of the
+ * logits, grad_h or grad_W products) and the bytes it must move at least
+ * (its operands read once, its outputs written once). Costs a few
+ * microseconds per launch; off by default.
+ */
+typedef struct {
+  char name[32];     /* kernel name, e.g. "fwd_sweep" */
+  int64_t launches;  /* launches recorded since the last read */
+  double total_ms;   /* summed event-measured durations */
+  double min_ms;
+  double max_ms;
+  double flops;      /* summed algorithmic FLOPs */
+  double bytes;      /* summed algorithmic bytes */
+} fkl_kernel_stat;
+
+fkl_status fkl_trace_enable(int on);
+
+/*
+ * Waits for the recorded events, aggregates them per kernel name into
+ * stats[0 .. min(capacity, kinds)), sets *count to the number of kernel
+ * names seen, and clears the record. Host-synchronising.
+ */
+fkl_status fkl_trace_read(fkl_kernel_stat* stats, int capacity, int* count);
+
 /* Static description of a status code. */
 const char* fkl_status_string(fkl_status status);
 

@@ -27,6 +27,8 @@ __all__ = [
     "forward",
     "backward",
     "validate_teacher",
+    "trace_enable",
+    "trace_read",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,6 +41,8 @@ EXPORTED_SYMBOLS = (
     "fkl_forward",
     "fkl_backward",
     "fkl_validate_teacher",
+    "fkl_trace_enable",
+    "fkl_trace_read",
     "fkl_status_string",
     "fkl_last_error",
     "fkl_version",
@@ -49,6 +53,20 @@ class FklError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"libfkl status {status}: {message}")
         self.status = status
+
+
+class KernelStat(ctypes.Structure):
+    """Mirror of ``fkl_kernel_stat``."""
+
+    _fields_ = [
+        ("name", ctypes.c_char * 32),
+        ("launches", ctypes.c_int64),
+        ("total_ms", ctypes.c_double),
+        ("min_ms", ctypes.c_double),
+        ("max_ms", ctypes.c_double),
+        ("flops", ctypes.c_double),
+        ("bytes", ctypes.c_double),
+    ]
 
 
 class Shape(ctypes.Structure):
@@ -84,7 +102,10 @@ def lib() -> ctypes.CDLL:
     L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
-    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_version"):
+    L.fkl_trace_enable.argtypes = [ctypes.c_int]
+    L.fkl_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_version",
+              "fkl_trace_enable", "fkl_trace_read"):
         getattr(L, f).restype = ctypes.c_int
     L.fkl_status_string.argtypes = [ctypes.c_int]
     L.fkl_status_string.restype = ctypes.c_char_p
@@ -167,16 +188,26 @@ def _workspace(nbytes, device, workspace):
 
 
 def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vslab: int = 0,
-            workspace=None, return_row_kl: bool = False):
-    """Fused forward. Returns (loss [1], row_lse [N]) or (loss, row_lse, row_kl)."""
+            workspace=None, return_row_kl: bool = False, loss=None, row_lse=None, row_kl=None):
+    """Fused forward. Returns (loss [1], row_lse [N]) or (loss, row_lse, row_kl).
+
+    Output tensors may be passed in to be overwritten (no allocation)."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
     s = make_shape(N, d, V, K, T, chunk, vslab)
     fb, _ = workspace_size(N, d, V, K, T, chunk, vslab)
     ws = _workspace(fb, h.device, workspace)
-    loss = torch.empty(1, dtype=torch.float32, device=h.device)
-    row_lse = torch.empty(N, dtype=torch.float32, device=h.device)
-    row_kl = torch.empty(N, dtype=torch.float32, device=h.device) if return_row_kl else None
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    _need(loss, "loss", torch.float32, (1,))
+    if row_lse is None:
+        row_lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    _need(row_lse, "row_lse", torch.float32, (N,))
+    if return_row_kl and row_kl is None:
+        row_kl = torch.empty(N, dtype=torch.float32, device=h.device)
+    if row_kl is not None:
+        _need(row_kl, "row_kl", torch.float32, (N,))
+        return_row_kl = True
     _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
                              _ptr(loss), _ptr(row_lse), _ptr(row_kl), _ptr(ws),
                              ctypes.c_size_t(ws.numel()), _stream()))
@@ -218,3 +249,22 @@ def validate_teacher(t_idx, t_logit, V: int) -> int:
     bad = torch.empty(1, dtype=torch.int32, device=t_idx.device)
     _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad), _stream()))
     return int(bad.item())
+
+
+def trace_enable(on: bool = True) -> None:
+    """Switch the library's per-kernel event timing on or off (process-wide)."""
+    _check(lib().fkl_trace_enable(1 if on else 0))
+
+
+def trace_read() -> list:
+    """Per-kernel timing recorded since the last read (waits for the events)."""
+    cap = 64
+    buf = (KernelStat * cap)()
+    n = ctypes.c_int(0)
+    _check(lib().fkl_trace_read(buf, cap, ctypes.byref(n)))
+    out = []
+    for i in range(min(n.value, cap)):
+        k = buf[i]
+        out.append(dict(name=k.name.decode(), launches=int(k.launches), total_ms=k.total_ms,
+                        min_ms=k.min_ms, max_ms=k.max_ms, flops=k.flops, bytes=k.bytes))
+    return out

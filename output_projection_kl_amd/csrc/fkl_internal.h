@@ -61,6 +61,20 @@ struct BwdArgs {
   char* ws;
 };
 
+// Event-based kernel timing (enabled by fkl_trace_enable). A scope records a
+// start event on construction and a stop event on destruction, on `stream`.
+class TraceScope {
+ public:
+  TraceScope(hipStream_t stream, const char* name, double flops, double bytes);
+  ~TraceScope();
+  TraceScope(const TraceScope&) = delete;
+  TraceScope& operator=(const TraceScope&) = delete;
+
+ private:
+  hipStream_t stream_;
+  int slot_;
+};
+
 hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx,

@@ -540,16 +540,27 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
   for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
     const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
-    hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                       c0, rows, p.K, invT, tidx, tp, negent);
+    {
+      TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
+      hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
+                         c0, rows, p.K, invT, tidx, tp, negent);
+    }
     const int want = splits_for(rbs, p.n_vt);
     const int tps = static_cast<int>(ceil_div(p.n_vt, want));
     const int splits = static_cast<int>(ceil_div(p.n_vt, tps));
     FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, tidx, tp,
                       static_cast<int32_t>(p.n_vt), tps, partial};
-    hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs, splits), dim3(kThreads), 0, st, fp);
-    hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, splits, rows, c0, negent,
-                       a.mask, invT, a.row_lse, a.row_kl, bsum);
+    {
+      const double dd = static_cast<double>(p.d);
+      TraceScope ts(st, "fwd_sweep", 2.0 * rows * static_cast<double>(p.V) * dd,
+                    2.0 * rows * dd + 2.0 * p.V * dd + 8.0 * rows * p.K + 16.0 * splits * rows);
+      hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs, splits), dim3(kThreads), 0, st, fp);
+    }
+    {
+      TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
+      hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, splits, rows, c0, negent,
+                         a.mask, invT, a.row_lse, a.row_kl, bsum);
+    }
     hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, rbs, sc);
   }
   hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, sc, p.T, a.loss);
@@ -576,8 +587,12 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk, ++chunk_index) {
     const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
-    hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                       c0, rows, p.K, invT, tidx, tp, negent);
+    {
+      TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
+      hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
+                         c0, rows, p.K, invT, tidx, tp, negent);
+    }
+    const double dd = static_cast<double>(p.d);
     for (int64_t s = 0; s < n_slabs; ++s) {
       const int64_t slab0 = s * p.vslab;
       const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
@@ -587,7 +602,11 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int splits = static_cast<int>(ceil_div(nvt, tps));
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
                     a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, tps};
-      hipLaunchKernelGGL(k_bwd_g, dim3(rbs, splits), dim3(kThreads), 0, st, gp);
+      {
+        TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
+                      2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
+        hipLaunchKernelGGL(k_bwd_g, dim3(rbs, splits), dim3(kThreads), 0, st, gp);
+      }
 
       // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w]
       GemmAccParams hp;
@@ -599,7 +618,11 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       hp.m_lim = rows;
       hp.n_lim = p.d;
       hp.beta = s > 0;
-      hipLaunchKernelGGL((k_gemm_acc<false, true>), dim3(rbs, dblocks), dim3(kThreads), 0, st, hp);
+      {
+        TraceScope ts(st, "bwd_grad_h", 2.0 * rows * slab_w * dd,
+                      2.0 * rows * slab_w + 2.0 * slab_w * dd + (hp.beta ? 8.0 : 4.0) * rows * dd);
+        hipLaunchKernelGGL((k_gemm_acc<false, true>), dim3(rbs, dblocks), dim3(kThreads), 0, st, hp);
+      }
 
       // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows]
       GemmAccParams wp;
@@ -611,7 +634,11 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.m_lim = slab_w;
       wp.n_lim = p.d;
       wp.beta = chunk_index > 0;
-      hipLaunchKernelGGL((k_gemm_acc<true, true>), dim3(nvt, dblocks), dim3(kThreads), 0, st, wp);
+      {
+        TraceScope ts(st, "bwd_grad_W", 2.0 * rows * slab_w * dd,
+                      2.0 * rows * slab_w + 2.0 * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
+        hipLaunchKernelGGL((k_gemm_acc<true, true>), dim3(nvt, dblocks), dim3(kThreads), 0, st, wp);
+      }
     }
   }
   return hipGetLastError();
