@@ -18,16 +18,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;       // block rows
-constexpr int kBK = 64;        // contraction depth of one LDS stage
-constexpr int kLDK = kBK + 8;  // LDS row stride in bf16 elements (144 B: 16 B skew per row)
 constexpr int kThreads = 256;  // four wave64s
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Element (mn, k) of a GEMM operand. Plain: base[mn * ld + k] (k contiguous).
-// Transposed: base[k * ld + mn] (mn contiguous). Loads outside
-// [0, mn_lim) x [0, k_lim) read as zero. mn_lim and k_lim are multiples of 8
-// on the contiguous side, so a 16-byte chunk is either wholly in or out.
+// Transposed: base[k * ld + mn] (mn contiguous). Elements outside
+// [0, mn_lim) x [0, k_lim) read as zero. The contiguous extent (k_lim for a
+// plain operand, mn_lim for a transposed one) is a multiple of 8, so a
+// 16-byte chunk is either wholly inside or wholly outside.
 struct Operand {
   const uint16_t* base;
   int64_t ld;
@@ -35,170 +34,269 @@ struct Operand {
   int64_t k_lim;
 };
 
-// R x 64 tile of a plain operand: R*8 16-byte chunks, R/32 per thread.
-// Eight consecutive lanes read one 128-byte row segment. Addresses are a
-// uniform 64-bit tile base plus 32-bit per-lane offsets (element units).
-template <int R>
-struct PlainLoader {
-  static constexpr int kPer = R * 8 / kThreads;
-  u32x4 v[kPer];
+#define FKL_LDS __attribute__((address_space(3)))
 
-  __device__ __forceinline__ void load(const Operand& op, int64_t mn0, int64_t k0, int tid) {
-    const uint16_t* tile = op.base + mn0 * op.ld + k0;
-    const int row = tid >> 3;
-    const int kc = (tid & 7) * 8;
-    const uint32_t off0 = static_cast<uint32_t>(row * op.ld + kc);
-    const uint32_t step = static_cast<uint32_t>(32 * op.ld);
-    const bool k_ok = k0 + kc < op.k_lim;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (k_ok && mn0 + row + 32 * i < op.mn_lim) {
-        v[i] = *reinterpret_cast<const u32x4*>(tile + (off0 + i * step));
-      } else {
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int base = (tid >> 3) * kLDK + (tid & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(lds + base + i * 32 * kLDK) = v[i];
-  }
-};
+// ---------------------------------------------------------------------------
+// Mainloop: 256 x 256 block tile, contraction in stages of 32, a ring of four
+// LDS stages filled by direct global->LDS loads (buffer_load ... lds, 16 B per
+// lane), so each stage's loads are issued three stages ahead of their use and
+// no registers stage the operands.
+//
+// LDS layout of one stage (32 KiB): operand A then operand B, 16 KiB each.
+//  * plain operand: 256 rows x 32 k = 64 B per row (4 chunks of 16 B); chunk
+//    c of row r is stored at physical chunk c ^ swz_plain(r).
+//  * transposed operand: 32 k-rows x 256 mn = 512 B per k-row (32 chunks of
+//    8 mn); chunk c of k-row r is stored at physical chunk c ^ swz_trans(r).
+// The XOR swizzles keep the fragment reads (16 lanes per LDS cycle) on
+// distinct banks. MFMA fragments (32 mn x 16 k per lane group) are read with
+// ds_read_b128 from a plain stage and with two ds_read_b64_tr_b16 (4 x 16
+// transposes within each 16-lane group) from a transposed stage.
+// ---------------------------------------------------------------------------
 
-// R x 64 tile of a transposed operand. Thread t < R owns the 8 (k) x 8 (mn)
-// block (k-group t & 7, mn-group t >> 3): eight 16-byte row loads, an 8 x 8
-// transpose of 16-bit lanes in registers, eight 16-byte LDS stores that land
-// the tile k-contiguous like a plain one. Eight consecutive lanes cover one
-// 128-byte segment of each global row and one 128-byte LDS row segment.
-template <int R>
-struct TransLoader {
-  u32x4 v[8];
+constexpr int kStageK = 32;
+constexpr int kStages = 4;
+constexpr int kOperandStageBytes = 256 * kStageK * 2;        // 16 KiB
+constexpr int kStageBytes = 2 * kOperandStageBytes;           // 32 KiB
+constexpr int kMainloopLdsBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kDmaPerOperand = kOperandStageBytes / (kThreads * 16);  // 4 per lane per stage
+constexpr uint32_t kOob = 0x80000000u;                         // offset past every buffer
 
-  __device__ __forceinline__ void load(const Operand& op, int64_t mn0, int64_t k0, int tid) {
-    if (tid >= R) return;
-    const uint16_t* tile = op.base + k0 * op.ld + mn0;
-    const int kb = (tid & 7) * 8;
-    const int mg = (tid >> 3) * 8;
-    const uint32_t off0 = static_cast<uint32_t>(kb * op.ld + mg);
-    const uint32_t step = static_cast<uint32_t>(op.ld);
-    const bool mn_ok = mn0 + mg < op.mn_lim;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (mn_ok && k0 + kb + i < op.k_lim) {
-        v[i] = *reinterpret_cast<const u32x4*>(tile + (off0 + i * step));
-      } else {
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
+__device__ __forceinline__ int swz_plain(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+__device__ __forceinline__ int swz_trans(int r) { return (r & 3) << 2; }
 
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    if (tid >= R) return;
-    const int base = (tid >> 3) * 8 * kLDK + (tid & 7) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a = v[2 * q][j >> 1];
-        const uint32_t b = v[2 * q + 1][j >> 1];
-        o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      *reinterpret_cast<u32x4*>(lds + base + j * kLDK) = o;
-    }
-  }
-};
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <bool Trans, int R>
-struct LoaderSel {
-  using type = PlainLoader<R>;
-};
-template <int R>
-struct LoaderSel<true, R> {
-  using type = TransLoader<R>;
-};
-
-// LDS bytes of the double-buffered mainloop for a 256 x BN tile.
-template <int BN>
-constexpr int mainloop_lds_bytes() {
-  return 2 * (kBM + BN) * kLDK * 2;
+// Wait until at most n of this wave's vector-memory operations are in flight.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-template <int BN>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][BN / 64]) {
+__device__ __forceinline__ void block_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// Per-lane source offsets of one operand's stage loads.
+struct StageSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[kDmaPerOperand];  // byte offsets for stage 0 (kOob when masked for every stage)
+  uint32_t kstep;                 // byte advance per stage along k
+  int32_t kchunk[kDmaPerOperand]; // plain: first k of the lane's chunk (k tail mask); transposed: unused
+  int32_t klim;
+  bool trans;
+};
+
+// Plain operand tile rows [mn0, mn0 + 256): the buffer is based at row mn0
+// and sized to the valid rows, so rows past mn_lim read as zero; chunks past
+// k_lim are masked per stage.
+__device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn0, int tid) {
+  StageSrc s;
+  const int64_t rows = op.mn_lim - mn0 < 256 ? op.mn_lim - mn0 : 256;
+  const int64_t bytes = rows > 0 ? rows * op.ld * 2 : 0;
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0 * op.ld), 0,
+                                             static_cast<int>(bytes), 0x00020000);
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int j = 0; j < kDmaPerOperand; ++j) {
+    const int r = (wave * kDmaPerOperand + j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz_plain(r);
+    s.kchunk[j] = c * 8;
+    s.voff[j] = static_cast<uint32_t>((r * op.ld + c * 8) * 2);
+  }
+  s.kstep = kStageK * 2;
+  s.klim = static_cast<int32_t>(op.k_lim);
+  s.trans = false;
+  return s;
+}
+
+// Transposed operand tile columns [mn0, mn0 + 256): the buffer starts at
+// column mn0 of k-row 0 and ends after k-row k_lim - 1, so k-rows past k_lim
+// read as zero; columns past mn_lim are masked once.
+__device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn0, int tid) {
+  StageSrc s;
+  const int64_t bytes = op.k_lim * op.ld * 2 - mn0 * 2;
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0), 0,
+                                             static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int j = 0; j < kDmaPerOperand; ++j) {
+    const int r = (wave * kDmaPerOperand + j) * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ swz_trans(r);
+    const bool ok = mn0 + c * 8 < op.mn_lim;
+    s.voff[j] = ok ? static_cast<uint32_t>((r * op.ld + c * 8) * 2) : kOob;
+    s.kchunk[j] = 0;
+  }
+  s.kstep = static_cast<uint32_t>(kStageK * op.ld * 2);
+  s.klim = static_cast<int32_t>(op.k_lim);
+  s.trans = true;
+  return s;
+}
+
+// Issue one operand's loads of stage kt into LDS region dst (16 KiB).
+__device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, char* dst, int tid) {
+  const int wave = tid >> 6;
+  const uint32_t adv = static_cast<uint32_t>(kt) * s.kstep;
+  const int k0 = kt * kStageK;
+#pragma unroll
+  for (int j = 0; j < kDmaPerOperand; ++j) {
+    uint32_t off = s.voff[j];
+    if (!s.trans) off = (k0 + s.kchunk[j] < s.klim) ? off + adv : kOob;
+    else if (off != kOob) off += adv;
+    FKL_LDS void* p = (FKL_LDS void*)(dst + (wave * kDmaPerOperand + j) * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsrc, p, 16, static_cast<int>(off), 0, 0, 0);
+  }
+}
+
+// Fragment of 32 (mn) x 16 (k) for this lane from a stage region: lane l
+// receives mn = mn_base + (l & 31), k = kb + 8 * (l >> 5) .. + 7.
+__device__ __forceinline__ bf16x8 frag_plain(const char* region, int mn_base, int kb, int lane) {
+  const int r = mn_base + (lane & 31);
+  const int c = (kb >> 3) + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(region + r * (kStageK * 2) + ((c ^ swz_plain(r)) << 4));
+}
+
+// Transposed fragments are read with ds_read_b64_tr_b16 issued from inline
+// assembly: the compiler's builtin for it makes every such read wait for all
+// outstanding global->LDS loads, which would drain the load pipeline. Results
+// are settled explicitly (Frags::settle) before the MFMAs use them.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const char* p) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const FKL_LDS char*)p));
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+
+// Lane l receives mn = mn_base + (l & 31) and k = kb + 8 * (l >> 5) .. + 7 as
+// two halves of 4 k each: lanes 4j..4j+3 of each 16-lane group point at k-row j
+// (4 consecutive mn each) and lane i gets column i.
+__device__ __forceinline__ void frag_trans_issue(const char* region, int mn_base, int kb, int lane,
+                                                 u32x2& lo, u32x2& hi) {
+  const int g = lane >> 4;
+  const int i = lane & 15;
+  const int r = kb + 8 * (g >> 1) + (i >> 2);
+  const int mn = mn_base + 16 * (g & 1) + 4 * (i & 3);
+  const int c = mn >> 3;
+  const int half = (mn & 7) * 2;
+  lo = ds_read_tr16(region + r * 512 + ((c ^ swz_trans(r)) << 4) + half);
+  hi = ds_read_tr16(region + (r + 4) * 512 + ((c ^ swz_trans(r + 4)) << 4) + half);
+}
+
+__device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
+  const u32x4 w{lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Fragments of one 16-deep contraction step for a wave: 4 of A, 4 of B.
+template <bool TA, bool TB>
+struct Frags {
+  bf16x8 a[4], b[4];
+  u32x2 ta[4][2], tb[4][2];
+
+  __device__ __forceinline__ void issue(const char* ra, const char* rb, int wm, int wn, int kb, int lane) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if constexpr (TA) frag_trans_issue(ra, wm * 128 + x * 32, kb, lane, ta[x][0], ta[x][1]);
+      else a[x] = frag_plain(ra, wm * 128 + x * 32, kb, lane);
+      if constexpr (TB) frag_trans_issue(rb, wn * 128 + x * 32, kb, lane, tb[x][0], tb[x][1]);
+      else b[x] = frag_plain(rb, wn * 128 + x * 32, kb, lane);
+    }
+  }
+
+  // Wait for the transposed reads; the asm operands make every later use of
+  // these registers depend on the wait.
+  __device__ __forceinline__ void settle() {
+    if constexpr (TA && TB) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
+                     "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]), "+v"(tb[0][0]), "+v"(tb[0][1]),
+                     "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]), "+v"(tb[2][1]), "+v"(tb[3][0]),
+                     "+v"(tb[3][1]));
+    } else if constexpr (TA) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
+                     "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
+    } else if constexpr (TB) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
+                     "+v"(tb[2][1]), "+v"(tb[3][0]), "+v"(tb[3][1]));
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if constexpr (TA) a[x] = join_halves(ta[x][0], ta[x][1]);
+      if constexpr (TB) b[x] = join_halves(tb[x][0], tb[x][1]);
+    }
+  }
+
+  __device__ __forceinline__ void mma(f32x16 (&acc)[4][4]) const {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < BN / 64; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 }
 
-// acc += A[m0:m0+256, kbeg:kend] * B[n0:n0+BN, kbeg:kend]^T, contraction
-// length a multiple of 64 (the loaders zero-fill past k_lim). Ends with a
-// barrier, so the caller may reuse the LDS right away.
-template <int BN, bool TA, bool TB>
-__device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0,
-                                              int64_t n0, int64_t kbeg, int64_t kend,
-                                              f32x16 (&acc)[4][BN / 64], uint16_t* lds) {
-  constexpr int NB = BN / 64;
-  constexpr int kStage = (kBM + BN) * kLDK;
+// acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+256, 0 : 32*nk]^T.
+// Starts and ends with a block barrier; on return no load is in flight and
+// the LDS may be reused.
+template <bool TA, bool TB>
+__device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0,
+                                              int nk, f32x16 (&acc)[4][4], char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1;
   const int wn = wave & 1;
+  const StageSrc sa = TA ? make_trans_src(A, m0, tid) : make_plain_src(A, m0, tid);
+  const StageSrc sb = TB ? make_trans_src(B, n0, tid) : make_plain_src(B, n0, tid);
 
-  typename LoaderSel<TA, kBM>::type la;
-  typename LoaderSel<TB, BN>::type lb;
-
-  const int nk = static_cast<int>((kend - kbeg) / kBK);
-  if (nk <= 0) return;
-
-  la.load(A, m0, kbeg, tid);
-  lb.load(B, n0, kbeg, tid);
-  la.store(lds, tid);
-  lb.store(lds + kBM * kLDK, tid);
-  __syncthreads();
-
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = (kt + 1) < nk;
-    if (more) {
-      la.load(A, m0, kbeg + (kt + 1) * kBK, tid);
-      lb.load(B, n0, kbeg + (kt + 1) * kBK, tid);
+  block_barrier();  // the previous user of the LDS is done with it
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p) {
+    if (p < nk) {
+      issue_stage(sa, p, lds + p * kStageBytes, tid);
+      issue_stage(sb, p, lds + p * kStageBytes + kOperandStageBytes, tid);
     }
-    const uint16_t* sa = lds + (kt & 1) * kStage;
-    const uint16_t* sb = sa + kBM * kLDK;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[4];
-      bf16x8 bfr[NB];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8*>(
-            sa + (wm * 128 + mb * 32 + frag_row) * kLDK + ks * 16 + frag_k);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(
-            sb + (wn * (BN / 2) + nb * 32 + frag_row) * kLDK + ks * 16 + frag_k);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* da = lds + ((kt + 1) & 1) * kStage;
-      la.store(da, tid);
-      lb.store(da + kBM * kLDK, tid);
-    }
-    __syncthreads();
   }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 2 < nk) wait_vmcnt<4 * kDmaPerOperand>();
+    else if (kt + 1 < nk) wait_vmcnt<2 * kDmaPerOperand>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (kt + kStages - 1 < nk) {
+      const int s = (kt + kStages - 1) % kStages;
+      issue_stage(sa, kt + kStages - 1, lds + s * kStageBytes, tid);
+      issue_stage(sb, kt + kStages - 1, lds + s * kStageBytes + kOperandStageBytes, tid);
+    }
+    const char* ra = lds + (kt % kStages) * kStageBytes;
+    const char* rb = ra + kOperandStageBytes;
+    Frags<TA, TB> f0, f1;
+    f0.issue(ra, rb, wm, wn, 0, lane);
+    f0.settle();
+    f1.issue(ra, rb, wm, wn, 16, lane);
+    f0.mma(acc);
+    f1.settle();
+    f1.mma(acc);
+  }
+  block_barrier();
 }
 
 // Row / column of accumulator element i of block (mb, nb) for this lane,

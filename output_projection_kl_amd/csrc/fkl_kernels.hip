@@ -189,8 +189,23 @@ struct FwdSweepParams {
   f32x4* partial;  // [splits][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
 };
 
+// A wave's 128 x 128 accumulators -> rows [wm*128, wm*128+128) of a 256 x 128
+// fp32 LDS half tile (stride kStageLd floats).
+__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][4], float* stage, int wm, int lane) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + acc_col(nb, lane)] = acc[mb][nb][i];
+}
+
+constexpr int kStageFp32Bytes = kTile * kStageLd * 4;  // 256 x 128 fp32 half tile, padded
+constexpr int kKernelLdsBytes = kStageFp32Bytes > kMainloopLdsBytes ? kStageFp32Bytes : kMainloopLdsBytes;
+
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
-  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -209,25 +224,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
 
   const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
-  const int64_t kdepth = (P.d + kBK - 1) / kBK * kBK;  // loaders zero-fill past d
+  const int nk = static_cast<int>((P.d + kStageK - 1) / kStageK);  // chunks past d read as zero
   float* stage = reinterpret_cast<float*>(lds);
   float m2 = -INFINITY, se = 0.f, gz = 0.f;
 
   for (int vt = vt0; vt < vt1; ++vt) {
     f32x16 acc[4][4];
-    zero_acc<256>(acc);
-    gemm_mainloop<256, false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
-                                     static_cast<int64_t>(vt) * kTile, 0, kdepth, acc, lds);
+    zero_acc(acc);
+    gemm_mainloop<false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
+                                static_cast<int64_t>(vt) * kTile, nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
-      if (wn == half) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + acc_col(nb, lane)] = acc[mb][nb][i];
-      }
+      if (wn == half) stage_half_tile(acc, stage, wm, lane);
       __syncthreads();
       const int64_t col0 = static_cast<int64_t>(vt) * kTile + half * 128;
       const int nvalid = static_cast<int>(min<int64_t>(128, P.V - col0));
@@ -334,9 +341,7 @@ struct BwdGParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
-  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
-  __shared__ float s_lse2[kTile];
-  __shared__ float s_c[kTile];
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -356,53 +361,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
     c = (valid && n > 0) ? static_cast<float>(static_cast<double>(g) * P.T / static_cast<double>(n)) : 0.f;
     lse2 = P.row_lse[grow] * kLog2e;
   }
-  s_lse2[tid] = lse2;
-  s_c[tid] = c;
   Cursor cur;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
            P.K, static_cast<int>(P.slab0) + vt0 * kTile, c != 0.f && vt0 < vt1);
-  __syncthreads();
 
   const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
-  const int64_t kdepth = (P.d + kBK - 1) / kBK * kBK;
+  const int nk = static_cast<int>((P.d + kStageK - 1) / kStageK);
   float* stage = reinterpret_cast<float*>(lds);
   const int64_t slab_end = P.slab0 + P.slab_w;
 
   for (int vt = vt0; vt < vt1; ++vt) {
     f32x16 acc[4][4];
-    zero_acc<256>(acc);
+    zero_acc(acc);
     const int64_t vbase = P.slab0 + static_cast<int64_t>(vt) * kTile;
-    gemm_mainloop<256, false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, 0, kdepth,
-                                     acc, lds);
+    gemm_mainloop<false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
       const int64_t col0 = vbase + half * 128;
-      if (wn == half) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = wm * 128 + acc_row(mb, i, lane);
-            const float l2 = s_lse2[r];
-            const float cc = s_c[r];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const int col = acc_col(nb, lane);
-              float v = 0.f;
-              if (cc != 0.f && col0 + col < slab_end)
-                v = cc * __builtin_amdgcn_exp2f(fmaf(acc[mb][nb][i], P.k2, -l2));
-              stage[r * kStageLd + col] = v;
-            }
-          }
-        }
-      }
+      if (wn == half) stage_half_tile(acc, stage, wm, lane);
       __syncthreads();
       {
-        const int c0 = static_cast<int>(col0);
+        // Row owner: G = c * exp2(z * log2(e)/T - lse * log2(e)), then -c * p at the
+        // teacher indices of this row that fall in the half tile.
         float* sr = stage + tid * kStageLd;
-        while (cur.cur < c0 + 128) {
-          if (cur.cur >= c0) sr[cur.cur - c0] -= c * cur.cp;
-          cur.next();
+        const int nvalid = static_cast<int>(min<int64_t>(128, slab_end - col0));
+        if (c == 0.f || nvalid <= 0) {
+#pragma unroll 8
+          for (int cc = 0; cc < 128; cc += 4) *reinterpret_cast<f32x4*>(sr + cc) = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll 8
+          for (int cc = 0; cc < 128; cc += 4) {
+            f32x4 x = *reinterpret_cast<const f32x4*>(sr + cc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[e] = (cc + e < nvalid) ? c * __builtin_amdgcn_exp2f(fmaf(x[e], P.k2, -lse2)) : 0.f;
+            *reinterpret_cast<f32x4*>(sr + cc) = x;
+          }
+          const int c0 = static_cast<int>(col0);
+          while (cur.cur < c0 + 128) {
+            if (cur.cur >= c0) sr[cur.cur - c0] -= c * cur.cp;
+            cur.next();
+          }
         }
       }
       __syncthreads();
@@ -437,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
 
 struct GemmAccParams {
   Operand A, B;
-  int64_t kend;
+  int32_t nk;  // contraction stages of 32
   float* C;
   int64_t ldc, m_lim, n_lim;
   int32_t beta;  // 0: C = A B^T, 1: C += A B^T
@@ -445,7 +444,7 @@ struct GemmAccParams {
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
-  __shared__ __align__(16) uint16_t lds[mainloop_lds_bytes<256>() / 2];
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -454,28 +453,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTile;
   f32x16 acc[4][4];
-  zero_acc<256>(acc);
-  gemm_mainloop<256, TA, TB>(P.A, P.B, m0, n0, 0, P.kend, acc, lds);
-  float* ctile = P.C + m0 * P.ldc + n0;
+  zero_acc(acc);
+  gemm_mainloop<TA, TB>(P.A, P.B, m0, n0, P.nk, acc, lds);
+  // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
+  // 32 lanes per row move 512 contiguous bytes with 16-byte accesses.
+  float* stage = reinterpret_cast<float*>(lds);
   const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
-  const int cmax = static_cast<int>(min<int64_t>(kTile, P.n_lim - n0));
-  const uint32_t ldc = static_cast<uint32_t>(P.ldc);
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = wm * 128 + acc_row(mb, i, lane);
-      if (r >= rmax) continue;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int c = wn * 128 + acc_col(nb, lane);
-        if (c < cmax) {
-          float* dst = ctile + (static_cast<uint32_t>(r) * ldc + static_cast<uint32_t>(c));
-          const float v = acc[mb][nb][i];
-          *dst = P.beta ? *dst + v : v;
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) stage_half_tile(acc, stage, wm, lane);
+    __syncthreads();
+    const int64_t cbase = n0 + half * 128;
+    const int cmax = static_cast<int>(min<int64_t>(128, P.n_lim - cbase));
+    float* ctile = P.C + m0 * P.ldc + cbase;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int q = tid + i * kThreads;
+      const int r = q >> 5;
+      const int c4 = (q & 31) * 4;
+      if (r < rmax && c4 < cmax) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + c4);
+        f32x4* dst = reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4);
+        if (P.beta) {
+          const f32x4 o = *dst;
+          *dst = f32x4{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+        } else {
+          *dst = v;
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -611,8 +617,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w]
       GemmAccParams hp;
       hp.A = Operand{G, p.vslab, p.chunk_alloc, p.vslab};
-      hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, p.V - slab0};
-      hp.kend = round_up(slab_w, kBK);
+      hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
+      hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
       hp.C = a.grad_h + c0 * p.d;
       hp.ldc = p.d;
       hp.m_lim = rows;
@@ -628,7 +634,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       GemmAccParams wp;
       wp.A = Operand{G, p.vslab, p.vslab, rows};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
-      wp.kend = round_up(rows, kBK);
+      wp.nk = static_cast<int32_t>(ceil_div(rows, kStageK));
       wp.C = a.grad_W + slab0 * p.d;
       wp.ldc = p.d;
       wp.m_lim = slab_w;
