@@ -90,6 +90,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the path is "
@@ -115,6 +117,20 @@ def main() -> int:
     in_out_bytes = sum(t.numel() * t.element_size() for t in
                        (wl.h, wl.W, wl.t_idx, wl.t_logit, row_lse, grad_h, grad_W))
     torch.cuda.reset_peak_memory_stats(dev)
+
+    if args.calibrate_copy_mib > 0:
+        # A plain copy of n bytes whose source was written long enough ago to
+        # have left the 256 MiB last-level cache (a 2 GiB fill comes between).
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(2)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+        del src, dst, flush
+        torch.cuda.reset_peak_memory_stats(dev)
 
     def step():
         fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, mask=wl.mask, chunk=wl.chunk, workspace=ws,

@@ -67,7 +67,7 @@ typedef struct {
   float T;       /* temperature */
   int32_t chunk; /* rows per pass; 0 = 4096. Results do not depend on it. */
   int32_t vslab; /* vocabulary columns per backward pass; 0 = chosen so that
-                    a pass's gradient block holds about 32 Mi elements.
+                    a pass's gradient block holds about 64 Mi elements.
                     Rounded up to a multiple of 256. Results do not depend
                     on it beyond fp32 summation order of grad_h. */
 } fkl_shape;

@@ -94,9 +94,9 @@ struct StageSrc {
 // Plain operand tile rows [mn0, mn0 + 256): the buffer is based at row mn0
 // and sized to the valid rows, so rows past mn_lim read as zero; chunks past
 // k_lim are masked per stage.
-__device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn0, int tid) {
+__device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn0, int tid, int tile_rows = 256) {
   StageSrc s;
-  const int64_t rows = op.mn_lim - mn0 < 256 ? op.mn_lim - mn0 : 256;
+  const int64_t rows = op.mn_lim - mn0 < tile_rows ? op.mn_lim - mn0 : tile_rows;
   const int64_t bytes = rows > 0 ? rows * op.ld * 2 : 0;
   s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0 * op.ld), 0,
                                              static_cast<int>(bytes), 0x00020000);
@@ -118,7 +118,7 @@ __device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn
 // Transposed operand tile columns [mn0, mn0 + 256): the buffer starts at
 // column mn0 of k-row 0 and ends after k-row k_lim - 1, so k-rows past k_lim
 // read as zero; columns past mn_lim are masked once.
-__device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn0, int tid) {
+__device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn0, int tid, int tile_cols = 256) {
   StageSrc s;
   const int64_t bytes = op.k_lim * op.ld * 2 - mn0 * 2;
   s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0), 0,
@@ -129,7 +129,7 @@ __device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn
   for (int j = 0; j < kDmaPerOperand; ++j) {
     const int r = (wave * kDmaPerOperand + j) * 2 + (lane >> 5);
     const int c = (lane & 31) ^ swz_trans(r);
-    const bool ok = mn0 + c * 8 < op.mn_lim;
+    const bool ok = mn0 + c * 8 < op.mn_lim && c * 8 < tile_cols;
     s.voff[j] = ok ? static_cast<uint32_t>((r * op.ld + c * 8) * 2) : kOob;
     s.kchunk[j] = 0;
   }
@@ -139,9 +139,11 @@ __device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn
   return s;
 }
 
-// Issue one operand's loads of stage kt into LDS region dst (16 KiB).
-__device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, char* dst, int tid) {
-  const int wave = tid >> 6;
+// Issue one operand's loads of stage kt into LDS region dst (16 KiB). When
+// live is false every lane reads out of range, which fills zeros without a
+// memory access: the loop issues a stage every iteration so its wait counts
+// never depend on the trip count.
+__device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, bool live, char* dst, int wave) {
   const uint32_t adv = static_cast<uint32_t>(kt) * s.kstep;
   const int k0 = kt * kStageK;
 #pragma unroll
@@ -149,6 +151,7 @@ __device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, char* dst
     uint32_t off = s.voff[j];
     if (!s.trans) off = (k0 + s.kchunk[j] < s.klim) ? off + adv : kOob;
     else if (off != kOob) off += adv;
+    if (!live) off = kOob;
     FKL_LDS void* p = (FKL_LDS void*)(dst + (wave * kDmaPerOperand + j) * 1024);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsrc, p, 16, static_cast<int>(off), 0, 0, 0);
   }
@@ -196,7 +199,7 @@ __device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
 }
 
 // Fragments of one 16-deep contraction step for a wave: 4 of A, 4 of B.
-template <bool TA, bool TB>
+template <bool TA, bool TB, int NB = 4>
 struct Frags {
   bf16x8 a[4], b[4];
   u32x2 ta[4][2], tb[4][2];
@@ -206,8 +209,10 @@ struct Frags {
     for (int x = 0; x < 4; ++x) {
       if constexpr (TA) frag_trans_issue(ra, wm * 128 + x * 32, kb, lane, ta[x][0], ta[x][1]);
       else a[x] = frag_plain(ra, wm * 128 + x * 32, kb, lane);
-      if constexpr (TB) frag_trans_issue(rb, wn * 128 + x * 32, kb, lane, tb[x][0], tb[x][1]);
-      else b[x] = frag_plain(rb, wn * 128 + x * 32, kb, lane);
+      if (x < NB) {
+        if constexpr (TB) frag_trans_issue(rb, wn * NB * 32 + x * 32, kb, lane, tb[x][0], tb[x][1]);
+        else b[x] = frag_plain(rb, wn * NB * 32 + x * 32, kb, lane);
+      }
     }
   }
 
@@ -224,79 +229,128 @@ struct Frags {
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
                      "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
-    } else if constexpr (TB) {
+    } else if constexpr (TB && NB == 4) {
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
                      "+v"(tb[2][1]), "+v"(tb[3][0]), "+v"(tb[3][1]));
+    } else if constexpr (TB) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
+                     "+v"(tb[2][1]));
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       if constexpr (TA) a[x] = join_halves(ta[x][0], ta[x][1]);
-      if constexpr (TB) b[x] = join_halves(tb[x][0], tb[x][1]);
+      if constexpr (TB) if (x < NB) b[x] = join_halves(tb[x][0], tb[x][1]);
     }
   }
 
-  __device__ __forceinline__ void mma(f32x16 (&acc)[4][4]) const {
+  __device__ __forceinline__ void mma(f32x16 (&acc)[4][NB]) const {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
   }
 };
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+template <int NB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 }
 
 // acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+256, 0 : 32*nk]^T.
-// Starts and ends with a block barrier; on return no load is in flight and
-// the LDS may be reused.
-template <bool TA, bool TB>
+//
+// Schedule per stage kt (two 16-deep steps f0, f1):
+//   issue f1 reads (stage kt) | f0 MFMAs | settle f1
+//   wait for stage kt+1 + block barrier   (every wave is done reading stage kt)
+//   issue f0 reads of stage kt+1 | DMA stage kt+4 into stage kt's buffer
+//   f1 MFMAs | settle f0
+// so the barrier and the LDS latency of the next stage sit between two MFMA
+// bursts instead of in front of an idle pipe. The loop body has no branch
+// (the last stage is peeled and a stage is issued every iteration, out of
+// range past the end), so the compiler's wait counts hold on every path.
+// Starts with a block barrier (the previous user of the LDS is done) and ends
+// with one; on return no load is in flight and the LDS may be reused.
+// NB = 4: 256 x 256 block tile; NB = 3: 256 x 192 (each wave 128 x 96).
+template <bool TA, bool TB, int NB = 4>
 __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0,
-                                              int nk, f32x16 (&acc)[4][4], char* lds) {
+                                              int nk, f32x16 (&acc)[4][NB], char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const StageSrc sa = TA ? make_trans_src(A, m0, tid) : make_plain_src(A, m0, tid);
-  const StageSrc sb = TB ? make_trans_src(B, n0, tid) : make_plain_src(B, n0, tid);
+  const StageSrc sb = TB ? make_trans_src(B, n0, tid, NB * 64) : make_plain_src(B, n0, tid, NB * 64);
 
-  block_barrier();  // the previous user of the LDS is done with it
+  block_barrier();
+  if (nk <= 0) return;
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p) {
-    if (p < nk) {
-      issue_stage(sa, p, lds + p * kStageBytes, tid);
-      issue_stage(sb, p, lds + p * kStageBytes + kOperandStageBytes, tid);
-    }
+  for (int p = 0; p < kStages; ++p) {
+    issue_stage(sa, p, p < nk, lds + p * kStageBytes, wave);
+    issue_stage(sb, p, p < nk, lds + p * kStageBytes + kOperandStageBytes, wave);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 2 < nk) wait_vmcnt<4 * kDmaPerOperand>();
-    else if (kt + 1 < nk) wait_vmcnt<2 * kDmaPerOperand>();
-    else wait_vmcnt<0>();
+  wait_vmcnt<6 * kDmaPerOperand>();  // stage 0 landed; stages 1..3 may be in flight
+  block_barrier();
+  Frags<TA, TB, NB> f0, f1;
+  f0.issue(lds, lds + kOperandStageBytes, wm, wn, 0, lane);
+  f0.settle();
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    char* cur = lds + (kt % kStages) * kStageBytes;
+    const char* nxt = lds + ((kt + 1) % kStages) * kStageBytes;
+    f1.issue(cur, cur + kOperandStageBytes, wm, wn, 16, lane);
+    f0.mma(acc);
+    f1.settle();
+    wait_vmcnt<4 * kDmaPerOperand>();  // stage kt+1 landed; kt+2, kt+3 may be in flight
     block_barrier();
-    if (kt + kStages - 1 < nk) {
-      const int s = (kt + kStages - 1) % kStages;
-      issue_stage(sa, kt + kStages - 1, lds + s * kStageBytes, tid);
-      issue_stage(sb, kt + kStages - 1, lds + s * kStageBytes + kOperandStageBytes, tid);
-    }
-    const char* ra = lds + (kt % kStages) * kStageBytes;
-    const char* rb = ra + kOperandStageBytes;
-    Frags<TA, TB> f0, f1;
-    f0.issue(ra, rb, wm, wn, 0, lane);
+    f0.issue(nxt, nxt + kOperandStageBytes, wm, wn, 0, lane);
+    const bool live = kt + kStages < nk;
+    issue_stage(sa, kt + kStages, live, cur, wave);
+    issue_stage(sb, kt + kStages, live, cur + kOperandStageBytes, wave);
+    f1.mma(acc);
     f0.settle();
-    f1.issue(ra, rb, wm, wn, 16, lane);
+  }
+  {
+    char* cur = lds + ((nk - 1) % kStages) * kStageBytes;
+    f1.issue(cur, cur + kOperandStageBytes, wm, wn, 16, lane);
     f0.mma(acc);
     f1.settle();
     f1.mma(acc);
   }
+  wait_vmcnt<0>();
   block_barrier();
+}
+
+// Workgroup placement. The dispatcher hands workgroups to the eight XCDs
+// round-robin (workgroup w runs on XCD w % 8) and each XCD has its own L2.
+// xcd_contiguous renumbers workgroups so that every XCD owns one contiguous
+// range of tile indices; grouped_tile then rasters an R x S tile grid in
+// bands of `group` rows, so the tiles resident on one XCD at the same time
+// form a compact rectangle and share operand panels in that XCD's L2.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_contiguous(int w, int total) {
+  const int x = w % kXcds;
+  const int i = w / kXcds;
+  const int base = total / kXcds;
+  const int rem = total % kXcds;
+  return x * base + (x < rem ? x : rem) + i;
+}
+
+__device__ __forceinline__ void grouped_tile(int L, int R, int S, int group, int& r, int& s) {
+  const int per_group = group * S;
+  const int g = L / per_group;
+  const int first = g * group;
+  const int rows = R - first < group ? R - first : group;
+  const int in = L - g * per_group;
+  r = first + in % rows;
+  s = in / rows;
 }
 
 // Row / column of accumulator element i of block (mb, nb) for this lane,

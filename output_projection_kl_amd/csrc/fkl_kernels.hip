@@ -186,16 +186,18 @@ struct FwdSweepParams {
   const int32_t* tsort_idx;
   const float* tsort_p;
   int32_t n_vt, tiles_per_split;
+  int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits
   f32x4* partial;  // [splits][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
 };
 
 // A wave's 128 x 128 accumulators -> rows [wm*128, wm*128+128) of a 256 x 128
 // fp32 LDS half tile (stride kStageLd floats).
-__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][4], float* stage, int wm, int lane) {
+template <int NB>
+__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][NB], float* stage, int wm, int lane) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + acc_col(nb, lane)] = acc[mb][nb][i];
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
   const int wave = tid >> 6;
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int rb = blockIdx.x;
-  const int split = blockIdx.y;
+  int rb, split;
+  grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
   const int vt0 = split * P.tiles_per_split;
   const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
   const int row = rb * kTile + tid;  // chunk-local row whose statistics this thread keeps
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
       __syncthreads();
     }
   }
-  const int ld = gridDim.x * kTile;
+  const int ld = P.rbs * kTile;
   P.partial[static_cast<int64_t>(split) * ld + row] = f32x4{m2, se, gz, 0.f};
 }
 
@@ -338,6 +340,7 @@ struct BwdGParams {
   int64_t vslab;
   uint16_t* G;  // [chunk_alloc][vslab]
   int32_t n_vt, tiles_per_split;
+  int32_t rbs, splits;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
@@ -347,8 +350,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
   const int wave = tid >> 6;
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int rb = blockIdx.x;
-  const int vt0 = blockIdx.y * P.tiles_per_split;
+  int rb, split;
+  grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
+  const int vt0 = split * P.tiles_per_split;
   const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
   const int row = rb * kTile + tid;
   const int64_t grow = P.r0 + row;
@@ -440,9 +444,11 @@ struct GemmAccParams {
   float* C;
   int64_t ldc, m_lim, n_lim;
   int32_t beta;  // 0: C = A B^T, 1: C += A B^T
+  int32_t mblocks, nblocks;
 };
 
-template <bool TA, bool TB>
+// NB = 4: 256 x 256 output tiles; NB = 3: 256 x 192.
+template <bool TA, bool TB, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
@@ -450,11 +456,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
   const int wave = tid >> 6;
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTile;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTile;
-  f32x16 acc[4][4];
+  int mbi, nbi;
+  grouped_tile(xcd_contiguous(blockIdx.x, P.mblocks * P.nblocks), P.mblocks, P.nblocks, 8, mbi, nbi);
+  const int64_t m0 = static_cast<int64_t>(mbi) * kTile;
+  constexpr int kTileN = NB * 64;
+  const int64_t n0 = static_cast<int64_t>(nbi) * kTileN;
+  f32x16 acc[4][NB];
   zero_acc(acc);
-  gemm_mainloop<TA, TB>(P.A, P.B, m0, n0, P.nk, acc, lds);
+  gemm_mainloop<TA, TB, NB>(P.A, P.B, m0, n0, P.nk, acc, lds);
   // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
   // 32 lanes per row move 512 contiguous bytes with 16-byte accesses.
   float* stage = reinterpret_cast<float*>(lds);
@@ -462,14 +471,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
   for (int half = 0; half < 2; ++half) {
     if (wn == half) stage_half_tile(acc, stage, wm, lane);
     __syncthreads();
-    const int64_t cbase = n0 + half * 128;
-    const int cmax = static_cast<int>(min<int64_t>(128, P.n_lim - cbase));
+    constexpr int kHalfN = NB * 32;
+    const int64_t cbase = n0 + half * kHalfN;
+    const int cmax = static_cast<int>(min<int64_t>(kHalfN, P.n_lim - cbase));
     float* ctile = P.C + m0 * P.ldc + cbase;
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < NB * 8; ++i) {
       const int q = tid + i * kThreads;
-      const int r = q >> 5;
-      const int c4 = (q & 31) * 4;
+      const int r = q / (NB * 8);
+      const int c4 = (q % (NB * 8)) * 4;
       if (r < rmax && c4 < cmax) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + c4);
         f32x4* dst = reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4);
@@ -525,6 +535,36 @@ __global__ void k_set_int(int32_t* p, int32_t v) {
 // Launch sequences
 // ---------------------------------------------------------------------------
 
+// Output tile width for a backward contraction with M x N outputs: 256 or
+// 192 columns, whichever needs fewer workgroup-waves x tile width (the time
+// of one tile grows with its width); ties keep 256.
+static inline int pick_nb(int64_t M, int64_t N) {
+  int best = 4;
+  int64_t best_cost = 0;
+  for (int nb = 4; nb >= 3; --nb) {
+    const int64_t tn = 64 * nb;
+    const int64_t wgs = ceil_div(M, kTile) * ceil_div(N, tn);
+    const int64_t cost = ceil_div(wgs, kTargetBlocks) * tn;
+    if (nb == 4 || cost < best_cost) {
+      best = nb;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <bool TA, bool TB>
+static void launch_gemm_acc(GemmAccParams P, int64_t M, int64_t N, hipStream_t st) {
+  P.mblocks = static_cast<int32_t>(ceil_div(M, kTile));
+  if (pick_nb(M, N) == 3) {
+    P.nblocks = static_cast<int32_t>(ceil_div(N, 192));
+    hipLaunchKernelGGL((k_gemm_acc<TA, TB, 3>), dim3(P.mblocks * P.nblocks), dim3(kThreads), 0, st, P);
+  } else {
+    P.nblocks = static_cast<int32_t>(ceil_div(N, kTile));
+    hipLaunchKernelGGL((k_gemm_acc<TA, TB, 4>), dim3(P.mblocks * P.nblocks), dim3(kThreads), 0, st, P);
+  }
+}
+
 static inline int splits_for(int64_t rbs, int64_t tiles) {
   int64_t s = ceil_div(kTargetBlocks, rbs);
   if (s > tiles) s = tiles;
@@ -555,12 +595,12 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
     const int tps = static_cast<int>(ceil_div(p.n_vt, want));
     const int splits = static_cast<int>(ceil_div(p.n_vt, tps));
     FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, tidx, tp,
-                      static_cast<int32_t>(p.n_vt), tps, partial};
+                      static_cast<int32_t>(p.n_vt), tps, rbs, splits, partial};
     {
       const double dd = static_cast<double>(p.d);
       TraceScope ts(st, "fwd_sweep", 2.0 * rows * static_cast<double>(p.V) * dd,
                     2.0 * rows * dd + 2.0 * p.V * dd + 8.0 * rows * p.K + 16.0 * splits * rows);
-      hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs, splits), dim3(kThreads), 0, st, fp);
+      hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs * splits), dim3(kThreads), 0, st, fp);
     }
     {
       TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
@@ -581,7 +621,6 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   uint16_t* G = reinterpret_cast<uint16_t*>(a.ws + p.off_G);
   const float invT = 1.0f / p.T;
   const float k2 = kLog2e / p.T;
-  const int dblocks = static_cast<int>(ceil_div(p.d, kTile));
 
   hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
   if (p.N == 0) {
@@ -607,11 +646,11 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int tps = static_cast<int>(ceil_div(nvt, want));
       const int splits = static_cast<int>(ceil_div(nvt, tps));
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
-                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, tps};
+                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, tps, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
-        hipLaunchKernelGGL(k_bwd_g, dim3(rbs, splits), dim3(kThreads), 0, st, gp);
+        hipLaunchKernelGGL(k_bwd_g, dim3(rbs * splits), dim3(kThreads), 0, st, gp);
       }
 
       // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w]
@@ -627,7 +666,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       {
         TraceScope ts(st, "bwd_grad_h", 2.0 * rows * slab_w * dd,
                       2.0 * rows * slab_w + 2.0 * slab_w * dd + (hp.beta ? 8.0 : 4.0) * rows * dd);
-        hipLaunchKernelGGL((k_gemm_acc<false, true>), dim3(rbs, dblocks), dim3(kThreads), 0, st, hp);
+        launch_gemm_acc<false, true>(hp, rows, p.d, st);
       }
 
       // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows]
@@ -643,7 +682,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       {
         TraceScope ts(st, "bwd_grad_W", 2.0 * rows * slab_w * dd,
                       2.0 * rows * slab_w + 2.0 * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
-        hipLaunchKernelGGL((k_gemm_acc<true, true>), dim3(nvt, dblocks), dim3(kThreads), 0, st, wp);
+        launch_gemm_acc<true, true>(wp, slab_w, p.d, st);
       }
     }
   }

@@ -48,8 +48,8 @@ def test_workspace_is_independent_of_rows():
     b = fkl.workspace_size(262144, 2880, 201088, 100, 1.0, chunk=4096)
     assert a == b
     fwd, bwd = a
-    # backward holds one bf16 gradient block of chunk x vslab (32 Mi elements by default)
-    assert 64 << 20 <= bwd <= (64 << 20) + (16 << 20)
+    # backward holds one bf16 gradient block of chunk x vslab (64 Mi elements by default)
+    assert 128 << 20 <= bwd <= (128 << 20) + (16 << 20)
     assert fwd < 16 << 20
 
 
