@@ -30,7 +30,8 @@
  *   - Row-major, contiguous. h: bf16 [N, d]; W: bf16 [V, d]; t_idx: int32
  *     [N, K]; t_logit: fp32 [N, K]; row_mask: uint8 [N] (nonzero = valid) or
  *     NULL (all valid); fp32 outputs.
- *   - h and W must be 16-byte aligned; every other array 4-byte aligned.
+ *   - h, W, grad_h and grad_W must be 16-byte aligned; every other array
+ *     4-byte aligned.
  *   - d must be a multiple of 8; 1 <= K <= min(V, 1024); T > 0 and finite.
  *   - Teacher indices must lie in [0, V) and be distinct within each row
  *     (checked only by fkl_validate_teacher); t_logit finite.

@@ -68,9 +68,10 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_tp = off;
   off = align256(off + static_cast<size_t>(p->chunk_alloc) * p->K * 4);
   const size_t shared_end = off;
-  // forward: split partials for up to (256 + rbs) workgroups' rows, then block sums
+  // forward: split partials (two per row per workgroup) for up to (256 + rbs)
+  // workgroups' rows, then block sums
   p->off_partial = off;
-  off = align256(off + static_cast<size_t>(kTargetBlocks + rbs) * kTile * 16);
+  off = align256(off + static_cast<size_t>(kTargetBlocks + rbs) * 2 * kTile * 16);
   p->off_blocksum = off;
   off = align256(off + static_cast<size_t>(rbs) * 8);
   p->fwd_bytes = off;
@@ -130,14 +131,15 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   fkl_status st = fkl::make_plan(shape, &p);
   if (st != FKL_OK) return st;
   if (!grad_W) return fail(FKL_EINVAL, "grad_W is NULL");
-  if (!aligned(grad_W, 4)) return fail(FKL_EINVAL, "grad_W must be 4-byte aligned");
+  if (!aligned(grad_W, 16)) return fail(FKL_EINVAL, "grad_W must be 16-byte aligned");
   if (grad_loss && !aligned(grad_loss, 4)) return fail(FKL_EINVAL, "grad_loss must be 4-byte aligned");
   if (p.N > 0) {
     if (!h || !W || !t_idx || !t_logit || !row_lse || !grad_h)
       return fail(FKL_EINVAL, "h, W, t_idx, t_logit, row_lse and grad_h must not be NULL");
     if (!aligned(h, 16) || !aligned(W, 16)) return fail(FKL_EINVAL, "h and W must be 16-byte aligned");
-    if (!aligned(t_idx, 4) || !aligned(t_logit, 4) || !aligned(row_lse, 4) || !aligned(grad_h, 4))
-      return fail(FKL_EINVAL, "t_idx, t_logit, row_lse and grad_h must be 4-byte aligned");
+    if (!aligned(grad_h, 16)) return fail(FKL_EINVAL, "grad_h must be 16-byte aligned");
+    if (!aligned(t_idx, 4) || !aligned(t_logit, 4) || !aligned(row_lse, 4))
+      return fail(FKL_EINVAL, "t_idx, t_logit and row_lse must be 4-byte aligned");
   }
   if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");

@@ -56,12 +56,27 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 
 constexpr int kStageK = 32;
-constexpr int kStages = 4;
-constexpr int kOperandStageBytes = 256 * kStageK * 2;        // 16 KiB
-constexpr int kStageBytes = 2 * kOperandStageBytes;           // 32 KiB
-constexpr int kMainloopLdsBytes = kStages * kStageBytes;      // 128 KiB
-constexpr int kDmaPerOperand = kOperandStageBytes / (kThreads * 16);  // 4 per lane per stage
+constexpr int kARows = 256;                                    // A operand extent of a block tile
+constexpr int kAStageBytes = kARows * kStageK * 2;             // 16 KiB
 constexpr uint32_t kOob = 0x80000000u;                         // offset past every buffer
+
+// Block tile 256 x (WN * NBW * 32): 2 x WN waves, each 128 x NBW*32 of the
+// output. The B operand's LDS extent is the tile width rounded up to 128 or
+// 256 (a 192-wide tile keeps the 256 layout and masks the last quarter).
+template <int NBW, int WN = 2>
+struct TileCfg {
+  static constexpr int kWaves = 2 * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kTileN = WN * NBW * 32;
+  static constexpr int kBExtent = kTileN <= 128 ? 128 : 256;
+  static constexpr int kBStageBytes = kBExtent * kStageK * 2;
+  static constexpr int kStageBytes = kAStageBytes + kBStageBytes;
+  static constexpr int kStages = kStageBytes <= 24576 ? 3 : 4;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kDmaA = kAStageBytes / (kThreads * 16);  // 16-byte loads per lane per stage
+  static constexpr int kDmaB = kBStageBytes / (kThreads * 16);
+  static constexpr int kDmaStage = kDmaA + kDmaB;
+};
 
 __device__ __forceinline__ int swz_plain(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int swz_trans(int r) { return (r & 3) << 2; }
@@ -81,30 +96,34 @@ __device__ __forceinline__ void block_barrier() {
   compiler_fence();
 }
 
-// Per-lane source offsets of one operand's stage loads.
+// Per-lane source offsets of one operand's stage loads (extent R rows of a
+// plain operand or R columns of a transposed one; R / 64 loads per lane).
+template <int LW>
 struct StageSrc {
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[kDmaPerOperand];  // byte offsets for stage 0 (kOob when masked for every stage)
-  uint32_t kstep;                 // byte advance per stage along k
-  int32_t kchunk[kDmaPerOperand]; // plain: first k of the lane's chunk (k tail mask); transposed: unused
+  const uint16_t* base;     // buffer start (wave-uniform)
+  int32_t bytes;            // buffer size; offsets at or past it read as zero
+  uint32_t voff[LW];        // byte offsets for stage 0 (kOob when masked for every stage)
+  uint32_t kstep;           // byte advance per stage along k
+  int32_t kchunk[LW];       // plain: first k of the lane's chunk (k-tail mask)
   int32_t klim;
   bool trans;
 };
 
-// Plain operand tile rows [mn0, mn0 + 256): the buffer is based at row mn0
-// and sized to the valid rows, so rows past mn_lim read as zero; chunks past
-// k_lim are masked per stage.
-__device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn0, int tid, int tile_rows = 256) {
-  StageSrc s;
-  const int64_t rows = op.mn_lim - mn0 < tile_rows ? op.mn_lim - mn0 : tile_rows;
+// Plain operand rows [mn0, mn0 + R) (only the first `used` are loaded): the
+// buffer is based at row mn0 and sized to the valid rows, so rows past mn_lim
+// read as zero; chunks past k_lim are masked per stage. LDS: row r at r * 64
+// bytes, 16-byte chunk c at physical chunk c ^ swz_plain(r).
+template <int R, int LW>
+__device__ __forceinline__ StageSrc<LW> make_plain_src(const Operand& op, int64_t mn0, int wave, int lane,
+                                                       int used = R) {
+  StageSrc<LW> s;
+  const int64_t rows = op.mn_lim - mn0 < used ? op.mn_lim - mn0 : used;
   const int64_t bytes = rows > 0 ? rows * op.ld * 2 : 0;
-  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0 * op.ld), 0,
-                                             static_cast<int>(bytes), 0x00020000);
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  s.base = op.base + mn0 * op.ld;
+  s.bytes = static_cast<int32_t>(bytes);
 #pragma unroll
-  for (int j = 0; j < kDmaPerOperand; ++j) {
-    const int r = (wave * kDmaPerOperand + j) * 16 + (lane >> 2);
+  for (int j = 0; j < LW; ++j) {
+    const int r = (wave * LW + j) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz_plain(r);
     s.kchunk[j] = c * 8;
     s.voff[j] = static_cast<uint32_t>((r * op.ld + c * 8) * 2);
@@ -115,21 +134,25 @@ __device__ __forceinline__ StageSrc make_plain_src(const Operand& op, int64_t mn
   return s;
 }
 
-// Transposed operand tile columns [mn0, mn0 + 256): the buffer starts at
-// column mn0 of k-row 0 and ends after k-row k_lim - 1, so k-rows past k_lim
-// read as zero; columns past mn_lim are masked once.
-__device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn0, int tid, int tile_cols = 256) {
-  StageSrc s;
+// Transposed operand columns [mn0, mn0 + R) (only the first `used` are
+// loaded): the buffer starts at column mn0 of k-row 0 and ends after k-row
+// k_lim - 1, so k-rows past k_lim read as zero; columns past mn_lim are
+// masked once. LDS: k-row r at r * 2R bytes, 16-byte chunk c (8 columns) at
+// physical chunk c ^ swz_trans(r).
+template <int R, int LW>
+__device__ __forceinline__ StageSrc<LW> make_trans_src(const Operand& op, int64_t mn0, int wave, int lane,
+                                                       int used = R) {
+  StageSrc<LW> s;
   const int64_t bytes = op.k_lim * op.ld * 2 - mn0 * 2;
-  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.base + mn0), 0,
-                                             static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  s.base = op.base + mn0;
+  s.bytes = static_cast<int32_t>(bytes > 0 ? bytes : 0);
+  constexpr int kChunks = R / 8;          // 16-byte chunks per k-row
+  constexpr int kRowsPerLoad = 64 / kChunks;
 #pragma unroll
-  for (int j = 0; j < kDmaPerOperand; ++j) {
-    const int r = (wave * kDmaPerOperand + j) * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ swz_trans(r);
-    const bool ok = mn0 + c * 8 < op.mn_lim && c * 8 < tile_cols;
+  for (int j = 0; j < LW; ++j) {
+    const int r = (wave * LW + j) * kRowsPerLoad + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz_trans(r);
+    const bool ok = mn0 + c * 8 < op.mn_lim && c * 8 < used;
     s.voff[j] = ok ? static_cast<uint32_t>((r * op.ld + c * 8) * 2) : kOob;
     s.kchunk[j] = 0;
   }
@@ -139,26 +162,29 @@ __device__ __forceinline__ StageSrc make_trans_src(const Operand& op, int64_t mn
   return s;
 }
 
-// Issue one operand's loads of stage kt into LDS region dst (16 KiB). When
-// live is false every lane reads out of range, which fills zeros without a
-// memory access: the loop issues a stage every iteration so its wait counts
-// never depend on the trip count.
-__device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, bool live, char* dst, int wave) {
+// Issue one operand's loads of stage kt into its LDS region dst. When live
+// is false every lane reads out of range, which fills zeros without a memory
+// access: the loop issues a stage every iteration so its wait counts never
+// depend on the trip count.
+template <int LW>
+__device__ __forceinline__ void issue_stage(const StageSrc<LW>& s, int kt, bool live, char* dst, int wave) {
   const uint32_t adv = static_cast<uint32_t>(kt) * s.kstep;
   const int k0 = kt * kStageK;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s.base), 0, s.bytes, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < kDmaPerOperand; ++j) {
+  for (int j = 0; j < LW; ++j) {
     uint32_t off = s.voff[j];
     if (!s.trans) off = (k0 + s.kchunk[j] < s.klim) ? off + adv : kOob;
     else if (off != kOob) off += adv;
     if (!live) off = kOob;
-    FKL_LDS void* p = (FKL_LDS void*)(dst + (wave * kDmaPerOperand + j) * 1024);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsrc, p, 16, static_cast<int>(off), 0, 0, 0);
+    FKL_LDS void* p = (FKL_LDS void*)(dst + (wave * LW + j) * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, p, 16, static_cast<int>(off), 0, 0, 0);
   }
 }
 
-// Fragment of 32 (mn) x 16 (k) for this lane from a stage region: lane l
-// receives mn = mn_base + (l & 31), k = kb + 8 * (l >> 5) .. + 7.
+// Fragment of 32 (mn) x 16 (k) for this lane from a plain stage region: lane
+// l receives mn = mn_base + (l & 31), k = kb + 8 * (l >> 5) .. + 7.
 __device__ __forceinline__ bf16x8 frag_plain(const char* region, int mn_base, int kb, int lane) {
   const int r = mn_base + (lane & 31);
   const int c = (kb >> 3) + (lane >> 5);
@@ -181,6 +207,7 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const char* p) {
 // Lane l receives mn = mn_base + (l & 31) and k = kb + 8 * (l >> 5) .. + 7 as
 // two halves of 4 k each: lanes 4j..4j+3 of each 16-lane group point at k-row j
 // (4 consecutive mn each) and lane i gets column i.
+template <int R>
 __device__ __forceinline__ void frag_trans_issue(const char* region, int mn_base, int kb, int lane,
                                                  u32x2& lo, u32x2& hi) {
   const int g = lane >> 4;
@@ -189,8 +216,8 @@ __device__ __forceinline__ void frag_trans_issue(const char* region, int mn_base
   const int mn = mn_base + 16 * (g & 1) + 4 * (i & 3);
   const int c = mn >> 3;
   const int half = (mn & 7) * 2;
-  lo = ds_read_tr16(region + r * 512 + ((c ^ swz_trans(r)) << 4) + half);
-  hi = ds_read_tr16(region + (r + 4) * 512 + ((c ^ swz_trans(r + 4)) << 4) + half);
+  lo = ds_read_tr16(region + r * (2 * R) + ((c ^ swz_trans(r)) << 4) + half);
+  hi = ds_read_tr16(region + (r + 4) * (2 * R) + ((c ^ swz_trans(r + 4)) << 4) + half);
 }
 
 __device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
@@ -198,20 +225,21 @@ __device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Fragments of one 16-deep contraction step for a wave: 4 of A, 4 of B.
-template <bool TA, bool TB, int NB = 4>
+// Fragments of one 16-deep contraction step for a wave: 4 of A (128 rows),
+// NBW of B (NBW * 32 columns).
+template <bool TA, bool TB, int NBW, int RB>
 struct Frags {
-  bf16x8 a[4], b[4];
-  u32x2 ta[4][2], tb[4][2];
+  bf16x8 a[4], b[NBW];
+  u32x2 ta[4][2], tb[NBW][2];
 
   __device__ __forceinline__ void issue(const char* ra, const char* rb, int wm, int wn, int kb, int lane) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      if constexpr (TA) frag_trans_issue(ra, wm * 128 + x * 32, kb, lane, ta[x][0], ta[x][1]);
+      if constexpr (TA) frag_trans_issue<kARows>(ra, wm * 128 + x * 32, kb, lane, ta[x][0], ta[x][1]);
       else a[x] = frag_plain(ra, wm * 128 + x * 32, kb, lane);
-      if (x < NB) {
-        if constexpr (TB) frag_trans_issue(rb, wn * NB * 32 + x * 32, kb, lane, tb[x][0], tb[x][1]);
-        else b[x] = frag_plain(rb, wn * NB * 32 + x * 32, kb, lane);
+      if (x < NBW) {
+        if constexpr (TB) frag_trans_issue<RB>(rb, wn * NBW * 32 + x * 32, kb, lane, tb[x][0], tb[x][1]);
+        else b[x] = frag_plain(rb, wn * NBW * 32 + x * 32, kb, lane);
       }
     }
   }
@@ -219,37 +247,37 @@ struct Frags {
   // Wait for the transposed reads; the asm operands make every later use of
   // these registers depend on the wait.
   __device__ __forceinline__ void settle() {
-    if constexpr (TA && TB) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
-                     "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]), "+v"(tb[0][0]), "+v"(tb[0][1]),
-                     "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]), "+v"(tb[2][1]), "+v"(tb[3][0]),
-                     "+v"(tb[3][1]));
-    } else if constexpr (TA) {
+    if constexpr (TA) {
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
                      "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
-    } else if constexpr (TB && NB == 4) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
-                     "+v"(tb[2][1]), "+v"(tb[3][0]), "+v"(tb[3][1]));
-    } else if constexpr (TB) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
-                     "+v"(tb[2][1]));
+    }
+    if constexpr (TB) {
+      if constexpr (NBW == 4) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
+                       "+v"(tb[2][1]), "+v"(tb[3][0]), "+v"(tb[3][1]));
+      } else if constexpr (NBW == 3) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
+                       "+v"(tb[2][1]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]));
+      }
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       if constexpr (TA) a[x] = join_halves(ta[x][0], ta[x][1]);
-      if constexpr (TB) if (x < NB) b[x] = join_halves(tb[x][0], tb[x][1]);
+      if constexpr (TB) if (x < NBW) b[x] = join_halves(tb[x][0], tb[x][1]);
     }
   }
 
-  __device__ __forceinline__ void mma(f32x16 (&acc)[4][NB]) const {
+  __device__ __forceinline__ void mma(f32x16 (&acc)[4][NBW]) const {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NBW; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
   }
 };
@@ -264,12 +292,14 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 }
 
-// acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+256, 0 : 32*nk]^T.
+// acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+kTileN, 0 : 32*nk]^T over a
+// ring of TileCfg<NBW, WN>::kStages LDS stages (2 x WN waves, each 128 x
+// NBW*32 of the output; wave w sits at row block w / WN, column block w % WN).
 //
 // Schedule per stage kt (two 16-deep steps f0, f1):
 //   issue f1 reads (stage kt) | f0 MFMAs | settle f1
 //   wait for stage kt+1 + block barrier   (every wave is done reading stage kt)
-//   issue f0 reads of stage kt+1 | DMA stage kt+4 into stage kt's buffer
+//   issue f0 reads of stage kt+1 | DMA stage kt+S into stage kt's buffer
 //   f1 MFMAs | settle f0
 // so the barrier and the LDS latency of the next stage sit between two MFMA
 // bursts instead of in front of an idle pipe. The loop body has no branch
@@ -277,48 +307,56 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
 // range past the end), so the compiler's wait counts hold on every path.
 // Starts with a block barrier (the previous user of the LDS is done) and ends
 // with one; on return no load is in flight and the LDS may be reused.
-// NB = 4: 256 x 256 block tile; NB = 3: 256 x 192 (each wave 128 x 96).
-template <bool TA, bool TB, int NB = 4>
+template <bool TA, bool TB, int NBW, int WN = 2>
 __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0,
-                                              int nk, f32x16 (&acc)[4][NB], char* lds) {
+                                              int nk, f32x16 (&acc)[4][NBW], char* lds) {
+  using C = TileCfg<NBW, WN>;
+  constexpr int S = C::kStages;
+  constexpr int RB = C::kBExtent;
+  constexpr int LA = C::kDmaA;
+  constexpr int LB = C::kDmaB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const StageSrc sa = TA ? make_trans_src(A, m0, tid) : make_plain_src(A, m0, tid);
-  const StageSrc sb = TB ? make_trans_src(B, n0, tid, NB * 64) : make_plain_src(B, n0, tid, NB * 64);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  StageSrc<LA> sa;
+  StageSrc<LB> sb;
+  if constexpr (TA) sa = make_trans_src<kARows, LA>(A, m0, wave, lane);
+  else sa = make_plain_src<kARows, LA>(A, m0, wave, lane);
+  if constexpr (TB) sb = make_trans_src<RB, LB>(B, n0, wave, lane, C::kTileN);
+  else sb = make_plain_src<RB, LB>(B, n0, wave, lane, C::kTileN);
 
   block_barrier();
   if (nk <= 0) return;
 #pragma unroll
-  for (int p = 0; p < kStages; ++p) {
-    issue_stage(sa, p, p < nk, lds + p * kStageBytes, wave);
-    issue_stage(sb, p, p < nk, lds + p * kStageBytes + kOperandStageBytes, wave);
+  for (int p = 0; p < S; ++p) {
+    issue_stage<LA>(sa, p, p < nk, lds + p * C::kStageBytes, wave);
+    issue_stage<LB>(sb, p, p < nk, lds + p * C::kStageBytes + kAStageBytes, wave);
   }
-  wait_vmcnt<6 * kDmaPerOperand>();  // stage 0 landed; stages 1..3 may be in flight
+  wait_vmcnt<(S - 1) * C::kDmaStage>();  // stage 0 landed
   block_barrier();
-  Frags<TA, TB, NB> f0, f1;
-  f0.issue(lds, lds + kOperandStageBytes, wm, wn, 0, lane);
+  Frags<TA, TB, NBW, RB> f0, f1;
+  f0.issue(lds, lds + kAStageBytes, wm, wn, 0, lane);
   f0.settle();
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    char* cur = lds + (kt % kStages) * kStageBytes;
-    const char* nxt = lds + ((kt + 1) % kStages) * kStageBytes;
-    f1.issue(cur, cur + kOperandStageBytes, wm, wn, 16, lane);
+    char* cur = lds + (kt % S) * C::kStageBytes;
+    const char* nxt = lds + ((kt + 1) % S) * C::kStageBytes;
+    f1.issue(cur, cur + kAStageBytes, wm, wn, 16, lane);
     f0.mma(acc);
     f1.settle();
-    wait_vmcnt<4 * kDmaPerOperand>();  // stage kt+1 landed; kt+2, kt+3 may be in flight
+    wait_vmcnt<(S - 2) * C::kDmaStage>();  // stage kt+1 landed
     block_barrier();
-    f0.issue(nxt, nxt + kOperandStageBytes, wm, wn, 0, lane);
-    const bool live = kt + kStages < nk;
-    issue_stage(sa, kt + kStages, live, cur, wave);
-    issue_stage(sb, kt + kStages, live, cur + kOperandStageBytes, wave);
+    f0.issue(nxt, nxt + kAStageBytes, wm, wn, 0, lane);
+    const bool live = kt + S < nk;
+    issue_stage<LA>(sa, kt + S, live, cur, wave);
+    issue_stage<LB>(sb, kt + S, live, cur + kAStageBytes, wave);
     f1.mma(acc);
     f0.settle();
   }
   {
-    char* cur = lds + ((nk - 1) % kStages) * kStageBytes;
-    f1.issue(cur, cur + kOperandStageBytes, wm, wn, 16, lane);
+    char* cur = lds + ((nk - 1) % S) * C::kStageBytes;
+    f1.issue(cur, cur + kAStageBytes, wm, wn, 16, lane);
     f0.mma(acc);
     f1.settle();
     f1.mma(acc);

@@ -17,7 +17,8 @@
 // are recomputed rather than stored):
 //   k_bwd_g         logits tile again -> G = c (exp(s - lse) - p~) -> bf16
 //                   gradient block in the workspace
-//   k_gemm_acc      grad_h[chunk] (+)= G W_slab ; grad_W[slab] (+)= G^T h_chunk
+//   k_bwd_grads     grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk
+//                   in one launch
 #include <climits>
 #include <cmath>
 
@@ -187,37 +188,50 @@ struct FwdSweepParams {
   const float* tsort_p;
   int32_t n_vt, tiles_per_split;
   int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits
-  f32x4* partial;  // [splits][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
+  f32x4* partial;  // [splits][2][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
 };
 
-// A wave's 128 x 128 accumulators -> rows [wm*128, wm*128+128) of a 256 x 128
-// fp32 LDS half tile (stride kStageLd floats).
-template <int NB>
-__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][NB], float* stage, int wm, int lane) {
+// Block tiles are 256 x 256 with 8 waves (2 per SIMD), each 128 x 64.
+constexpr int kNBW = 2;
+constexpr int kWN = 4;
+using MainCfg = TileCfg<kNBW, kWN>;
+constexpr int kBlockThreads = MainCfg::kThreads;  // 512
+
+// Waves whose 64 columns fall in half `half` of the tile copy their 128 x 64
+// accumulators into a 256 x 128 fp32 LDS half tile (stride kStageLd floats).
+__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][kNBW], float* stage, int wm, int wn,
+                                                int lane) {
+  const int cbase = (wn & 1) * 64;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < kNBW; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + acc_col(nb, lane)] = acc[mb][nb][i];
+        stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + cbase + acc_col(nb, lane)] = acc[mb][nb][i];
 }
 
 constexpr int kStageFp32Bytes = kTile * kStageLd * 4;  // 256 x 128 fp32 half tile, padded
-constexpr int kKernelLdsBytes = kStageFp32Bytes > kMainloopLdsBytes ? kStageFp32Bytes : kMainloopLdsBytes;
+constexpr int kKernelLdsBytes =
+    kStageFp32Bytes > MainCfg::kLdsBytes ? kStageFp32Bytes : MainCfg::kLdsBytes;
 
-__global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
+// Each thread owns one row (tid & 255) of the block and one 64-column quarter
+// (tid >> 8) of every half tile: it keeps that quarter's online max / sum of
+// exp2 and picks up the logits at the row's teacher indices inside it.
+__global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / kWN;
+  const int wn = wave % kWN;
   int rb, split;
   grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
   const int vt0 = split * P.tiles_per_split;
   const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
-  const int row = rb * kTile + tid;  // chunk-local row whose statistics this thread keeps
+  const int rloc = tid & (kTile - 1);
+  const int sub = tid >> 8;
+  const int row = rb * kTile + rloc;  // chunk-local row whose statistics this thread keeps
   const bool row_ok = row < P.rows;
 
   Cursor cur;
@@ -231,21 +245,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
   float m2 = -INFINITY, se = 0.f, gz = 0.f;
 
   for (int vt = vt0; vt < vt1; ++vt) {
-    f32x16 acc[4][4];
+    f32x16 acc[4][kNBW];
     zero_acc(acc);
-    gemm_mainloop<false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
-                                static_cast<int64_t>(vt) * kTile, nk, acc, lds);
+    gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
+                                           static_cast<int64_t>(vt) * kTile, nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
-      if (wn == half) stage_half_tile(acc, stage, wm, lane);
+      if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
       __syncthreads();
       const int64_t col0 = static_cast<int64_t>(vt) * kTile + half * 128;
-      const int nvalid = static_cast<int>(min<int64_t>(128, P.V - col0));
+      const int64_t cs = col0 + sub * 64;
+      const int nvalid = static_cast<int>(min<int64_t>(64, P.V - cs));
+      const float* sr = stage + rloc * kStageLd + sub * 64;
       if (nvalid > 0) {
-        const float* sr = stage + tid * kStageLd;
         float mx = -INFINITY;
-        if (nvalid == 128) {
+        if (nvalid == 64) {
 #pragma unroll 8
-          for (int c = 0; c < 128; c += 4) {
+          for (int c = 0; c < 64; c += 4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
             mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
           }
@@ -254,9 +269,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
         }
         const float mnew = fmaxf(m2, mx * P.k2);
         float s = 0.f;
-        if (nvalid == 128) {
+        if (nvalid == 64) {
 #pragma unroll 8
-          for (int c = 0; c < 128; c += 4) {
+          for (int c = 0; c < 64; c += 4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
             s += __builtin_amdgcn_exp2f(fmaf(x[0], P.k2, -mnew));
             s += __builtin_amdgcn_exp2f(fmaf(x[1], P.k2, -mnew));
@@ -268,21 +283,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_sweep(FwdSweepParams P) {
         }
         se = se * __builtin_amdgcn_exp2f(m2 - mnew) + s;
         m2 = mnew;
-        const int c0 = static_cast<int>(col0);
-        while (cur.cur < c0 + 128) {
-          if (cur.cur >= c0) gz += cur.cp * sr[cur.cur - c0];
-          cur.next();
-        }
+      }
+      // Walk the row's sorted teacher list past this half tile, keeping the
+      // entries that fall in this thread's quarter.
+      const int c0 = static_cast<int>(col0);
+      const int c1 = static_cast<int>(cs);
+      while (cur.cur < c0 + 128) {
+        if (cur.cur >= c1 && cur.cur < c1 + 64) gz += cur.cp * sr[cur.cur - c1];
+        cur.next();
       }
       __syncthreads();
     }
   }
   const int ld = P.rbs * kTile;
-  P.partial[static_cast<int64_t>(split) * ld + row] = f32x4{m2, se, gz, 0.f};
+  P.partial[static_cast<int64_t>(split * 2 + sub) * ld + row] = f32x4{m2, se, gz, 0.f};
 }
 
 // One thread per row of the chunk: merge the split statistics.
-__global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int splits,
+__global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int parts,
                                                      int rows, int64_t r0,
                                                      const float* __restrict__ negent,
                                                      const uint8_t* __restrict__ mask, float invT,
@@ -295,9 +313,9 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
   double kl_d = 0.0;
   if (r < rows) {
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
+    for (int s = 0; s < parts; ++s) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
     float sum = 0.f, gz = 0.f;
-    for (int s = 0; s < splits; ++s) {
+    for (int s = 0; s < parts; ++s) {
       const f32x4 pr = partial[static_cast<int64_t>(s) * ld + r];
       if (pr[1] > 0.f) sum += pr[1] * exp2f(pr[0] - M);
       gz += pr[2];
@@ -343,18 +361,20 @@ struct BwdGParams {
   int32_t rbs, splits;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
+__global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / kWN;
+  const int wn = wave % kWN;
   int rb, split;
   grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
   const int vt0 = split * P.tiles_per_split;
   const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
-  const int row = rb * kTile + tid;
+  const int rloc = tid & (kTile - 1);
+  const int sub = tid >> 8;
+  const int row = rb * kTile + rloc;
   const int64_t grow = P.r0 + row;
 
   float c = 0.f, lse2 = 0.f;
@@ -376,44 +396,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdGParams P) {
   const int64_t slab_end = P.slab0 + P.slab_w;
 
   for (int vt = vt0; vt < vt1; ++vt) {
-    f32x16 acc[4][4];
+    f32x16 acc[4][kNBW];
     zero_acc(acc);
     const int64_t vbase = P.slab0 + static_cast<int64_t>(vt) * kTile;
-    gemm_mainloop<false, false>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc, lds);
+    gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc,
+                                           lds);
     for (int half = 0; half < 2; ++half) {
       const int64_t col0 = vbase + half * 128;
-      if (wn == half) stage_half_tile(acc, stage, wm, lane);
+      if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
       __syncthreads();
       {
-        // Row owner: G = c * exp2(z * log2(e)/T - lse * log2(e)), then -c * p at the
-        // teacher indices of this row that fall in the half tile.
-        float* sr = stage + tid * kStageLd;
-        const int nvalid = static_cast<int>(min<int64_t>(128, slab_end - col0));
+        // Row owner (one quarter of the half tile): G = c * exp2(z * log2(e)/T - lse * log2(e)),
+        // then -c * p at the row's teacher indices that fall in the quarter.
+        const int64_t cs = col0 + sub * 64;
+        float* sr = stage + rloc * kStageLd + sub * 64;
+        const int nvalid = static_cast<int>(min<int64_t>(64, slab_end - cs));
         if (c == 0.f || nvalid <= 0) {
 #pragma unroll 8
-          for (int cc = 0; cc < 128; cc += 4) *reinterpret_cast<f32x4*>(sr + cc) = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int cc = 0; cc < 64; cc += 4) *reinterpret_cast<f32x4*>(sr + cc) = f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
 #pragma unroll 8
-          for (int cc = 0; cc < 128; cc += 4) {
+          for (int cc = 0; cc < 64; cc += 4) {
             f32x4 x = *reinterpret_cast<const f32x4*>(sr + cc);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               x[e] = (cc + e < nvalid) ? c * __builtin_amdgcn_exp2f(fmaf(x[e], P.k2, -lse2)) : 0.f;
             *reinterpret_cast<f32x4*>(sr + cc) = x;
           }
-          const int c0 = static_cast<int>(col0);
-          while (cur.cur < c0 + 128) {
-            if (cur.cur >= c0) sr[cur.cur - c0] -= c * cur.cp;
-            cur.next();
-          }
+        }
+        const int c0 = static_cast<int>(col0);
+        const int c1 = static_cast<int>(cs);
+        while (cur.cur < c0 + 128) {
+          if (cur.cur >= c1 && cur.cur < c1 + 64) sr[cur.cur - c1] -= c * cur.cp;
+          cur.next();
         }
       }
       __syncthreads();
       uint16_t* gdst = P.G + static_cast<int64_t>(rb) * kTile * P.vslab + static_cast<int64_t>(vt) * kTile +
                        half * 128;
 #pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const int q = tid + i * kThreads;
+      for (int i = 0; i < (kTile * 128 / 8) / kBlockThreads; ++i) {
+        const int q = tid + i * kBlockThreads;
         const int r = q >> 4;
         const int cc8 = (q & 15) * 8;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + cc8);
@@ -447,39 +470,50 @@ struct GemmAccParams {
   int32_t mblocks, nblocks;
 };
 
-// NB = 4: 256 x 256 output tiles; NB = 3: 256 x 192.
-template <bool TA, bool TB, int NB>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
-  __shared__ __align__(16) char lds[kKernelLdsBytes];
+// Renumber workgroup w of the contiguous range [first, first + count) so that
+// the members of the range on each XCD take one contiguous block of indices.
+__device__ __forceinline__ int xcd_contiguous_range(int w, int first, int count) {
+  const int x = w % kXcds;
+  int before = 0;
+  for (int y = 0; y < x; ++y) {
+    const int f = first + ((y - first) % kXcds + kXcds) % kXcds;
+    before += f < first + count ? (first + count - 1 - f) / kXcds + 1 : 0;
+  }
+  const int fx = first + ((x - first) % kXcds + kXcds) % kXcds;
+  return before + (w - fx) / kXcds;
+}
+
+// One 256 x 256 output tile of C (+)= A B^T; `local` is this workgroup's
+// index among the problem's tiles (XCD-renumbered).
+template <bool TA, bool TB>
+__device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / kWN;
+  const int wn = wave % kWN;
   int mbi, nbi;
-  grouped_tile(xcd_contiguous(blockIdx.x, P.mblocks * P.nblocks), P.mblocks, P.nblocks, 8, mbi, nbi);
+  grouped_tile(local, P.mblocks, P.nblocks, 8, mbi, nbi);
   const int64_t m0 = static_cast<int64_t>(mbi) * kTile;
-  constexpr int kTileN = NB * 64;
-  const int64_t n0 = static_cast<int64_t>(nbi) * kTileN;
-  f32x16 acc[4][NB];
+  const int64_t n0 = static_cast<int64_t>(nbi) * kTile;
+  f32x16 acc[4][kNBW];
   zero_acc(acc);
-  gemm_mainloop<TA, TB, NB>(P.A, P.B, m0, n0, P.nk, acc, lds);
+  gemm_mainloop<TA, TB, kNBW, kWN>(P.A, P.B, m0, n0, P.nk, acc, lds);
   // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
   // 32 lanes per row move 512 contiguous bytes with 16-byte accesses.
   float* stage = reinterpret_cast<float*>(lds);
   const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
   for (int half = 0; half < 2; ++half) {
-    if (wn == half) stage_half_tile(acc, stage, wm, lane);
+    if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
     __syncthreads();
-    constexpr int kHalfN = NB * 32;
-    const int64_t cbase = n0 + half * kHalfN;
-    const int cmax = static_cast<int>(min<int64_t>(kHalfN, P.n_lim - cbase));
+    const int64_t cbase = n0 + half * 128;
+    const int cmax = static_cast<int>(min<int64_t>(128, P.n_lim - cbase));
     float* ctile = P.C + m0 * P.ldc + cbase;
 #pragma unroll 4
-    for (int i = 0; i < NB * 8; ++i) {
-      const int q = tid + i * kThreads;
-      const int r = q / (NB * 8);
-      const int c4 = (q % (NB * 8)) * 4;
+    for (int i = 0; i < (kTile * 32) / kBlockThreads; ++i) {
+      const int q = tid + i * kBlockThreads;
+      const int r = q >> 5;
+      const int c4 = (q & 31) * 4;
       if (r < rmax && c4 < cmax) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + c4);
         f32x4* dst = reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4);
@@ -492,6 +526,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_acc(GemmAccParams P) {
       }
     }
     __syncthreads();
+  }
+}
+
+// grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk in one
+// launch: the first h_tiles workgroups take grad_h tiles (the longer
+// contraction, dispatched first), the rest grad_W tiles.
+struct GradParams {
+  GemmAccParams gh, gw;
+  int32_t h_tiles, w_tiles;
+};
+
+__global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
+  const int w = blockIdx.x;
+  if (w < P.h_tiles) {
+    gemm_acc_tile<false, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
+  } else {
+    gemm_acc_tile<true, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
   }
 }
 
@@ -535,36 +587,6 @@ __global__ void k_set_int(int32_t* p, int32_t v) {
 // Launch sequences
 // ---------------------------------------------------------------------------
 
-// Output tile width for a backward contraction with M x N outputs: 256 or
-// 192 columns, whichever needs fewer workgroup-waves x tile width (the time
-// of one tile grows with its width); ties keep 256.
-static inline int pick_nb(int64_t M, int64_t N) {
-  int best = 4;
-  int64_t best_cost = 0;
-  for (int nb = 4; nb >= 3; --nb) {
-    const int64_t tn = 64 * nb;
-    const int64_t wgs = ceil_div(M, kTile) * ceil_div(N, tn);
-    const int64_t cost = ceil_div(wgs, kTargetBlocks) * tn;
-    if (nb == 4 || cost < best_cost) {
-      best = nb;
-      best_cost = cost;
-    }
-  }
-  return best;
-}
-
-template <bool TA, bool TB>
-static void launch_gemm_acc(GemmAccParams P, int64_t M, int64_t N, hipStream_t st) {
-  P.mblocks = static_cast<int32_t>(ceil_div(M, kTile));
-  if (pick_nb(M, N) == 3) {
-    P.nblocks = static_cast<int32_t>(ceil_div(N, 192));
-    hipLaunchKernelGGL((k_gemm_acc<TA, TB, 3>), dim3(P.mblocks * P.nblocks), dim3(kThreads), 0, st, P);
-  } else {
-    P.nblocks = static_cast<int32_t>(ceil_div(N, kTile));
-    hipLaunchKernelGGL((k_gemm_acc<TA, TB, 4>), dim3(P.mblocks * P.nblocks), dim3(kThreads), 0, st, P);
-  }
-}
-
 static inline int splits_for(int64_t rbs, int64_t tiles) {
   int64_t s = ceil_div(kTargetBlocks, rbs);
   if (s > tiles) s = tiles;
@@ -600,11 +622,11 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
       const double dd = static_cast<double>(p.d);
       TraceScope ts(st, "fwd_sweep", 2.0 * rows * static_cast<double>(p.V) * dd,
                     2.0 * rows * dd + 2.0 * p.V * dd + 8.0 * rows * p.K + 16.0 * splits * rows);
-      hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs * splits), dim3(kThreads), 0, st, fp);
+      hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs * splits), dim3(kBlockThreads), 0, st, fp);
     }
     {
       TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
-      hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, splits, rows, c0, negent,
+      hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, 2 * splits, rows, c0, negent,
                          a.mask, invT, a.row_lse, a.row_kl, bsum);
     }
     hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, rbs, sc);
@@ -650,11 +672,13 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
-        hipLaunchKernelGGL(k_bwd_g, dim3(rbs * splits), dim3(kThreads), 0, st, gp);
+        hipLaunchKernelGGL(k_bwd_g, dim3(rbs * splits), dim3(kBlockThreads), 0, st, gp);
       }
 
-      // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w]
-      GemmAccParams hp;
+      // grad_h[c0 : c0 + rows] (+)= G[:, :slab_w] @ W[slab0 : slab0 + slab_w] and
+      // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows], one launch.
+      GradParams gp2;
+      GemmAccParams& hp = gp2.gh;
       hp.A = Operand{G, p.vslab, p.chunk_alloc, p.vslab};
       hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
       hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
@@ -663,14 +687,9 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       hp.m_lim = rows;
       hp.n_lim = p.d;
       hp.beta = s > 0;
-      {
-        TraceScope ts(st, "bwd_grad_h", 2.0 * rows * slab_w * dd,
-                      2.0 * rows * slab_w + 2.0 * slab_w * dd + (hp.beta ? 8.0 : 4.0) * rows * dd);
-        launch_gemm_acc<false, true>(hp, rows, p.d, st);
-      }
-
-      // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows]
-      GemmAccParams wp;
+      hp.mblocks = rbs;
+      hp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
+      GemmAccParams& wp = gp2.gw;
       wp.A = Operand{G, p.vslab, p.vslab, rows};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
       wp.nk = static_cast<int32_t>(ceil_div(rows, kStageK));
@@ -679,10 +698,15 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.m_lim = slab_w;
       wp.n_lim = p.d;
       wp.beta = chunk_index > 0;
+      wp.mblocks = nvt;
+      wp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
+      gp2.h_tiles = hp.mblocks * hp.nblocks;
+      gp2.w_tiles = wp.mblocks * wp.nblocks;
       {
-        TraceScope ts(st, "bwd_grad_W", 2.0 * rows * slab_w * dd,
-                      2.0 * rows * slab_w + 2.0 * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
-        launch_gemm_acc<true, true>(wp, slab_w, p.d, st);
+        TraceScope ts(st, "bwd_grads", 4.0 * rows * slab_w * dd,
+                      4.0 * rows * slab_w + 2.0 * slab_w * dd + 2.0 * rows * dd +
+                          (hp.beta ? 8.0 : 4.0) * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
+        hipLaunchKernelGGL(k_bwd_grads, dim3(gp2.h_tiles + gp2.w_tiles), dim3(kBlockThreads), 0, st, gp2);
       }
     }
   }

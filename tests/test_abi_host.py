@@ -107,6 +107,8 @@ def test_backward_argument_errors_before_any_device_work():
     assert bwd(grad_h=0) == 1
     assert bwd(grad_W=0) == 1
     assert bwd(grad_W=2) == 1
+    assert bwd(grad_W=16384 + 4) == 1   # grad_W needs 16-byte alignment
+    assert bwd(grad_h=8192 + 8) == 1    # so does grad_h
     assert bwd(grad_loss=6) == 1
     assert bwd(ws_bytes=100) == 2
 
