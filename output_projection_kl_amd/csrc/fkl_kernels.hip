@@ -136,40 +136,74 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 // Per-row sorted teacher cursor
 // ---------------------------------------------------------------------------
 
+// Walk over one row's teacher entries sorted by vocabulary index. A window of
+// four entries sits in registers and every step loads the entry four ahead,
+// so a row that meets several entries in one half tile does not stall on
+// memory; the refill of the last slot has three steps (normally a whole
+// tile) to arrive.
 struct Cursor {
   const int32_t* idx;
   const float* p;
-  int pos, K;
-  int cur;    // current index, INT_MAX when exhausted
-  float cp;   // its probability
+  int K, pos;  // pos: index of entry e0
+  int e0, e1, e2, e3;
+  float p0, p1, p2, p3;
 
+  __device__ __forceinline__ void load_at(int k, int& e, float& q) const {
+    if (k < K) {
+      e = idx[k];
+      q = p[k];
+    } else {
+      e = INT_MAX;
+      q = 0.f;
+    }
+  }
+
+  // Position at the first entry >= target: 16 evenly spaced samples locate
+  // the segment, then that segment is counted (two rounds of independent
+  // loads instead of a chain of dependent ones).
   __device__ __forceinline__ void init(const int32_t* i, const float* pp, int k, int target, bool on) {
     idx = i;
     p = pp;
     K = k;
-    cur = INT_MAX;
-    cp = 0.f;
     pos = k;
+    e0 = e1 = e2 = e3 = INT_MAX;
+    p0 = p1 = p2 = p3 = 0.f;
     if (!on) return;
-    int lo = 0, hi = k;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (idx[mid] < target) lo = mid + 1; else hi = mid;
+    const int seg = (K + 15) / 16;
+    int c1 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = j * seg;
+      if (kk < K) c1 += idx[kk] < target;
     }
-    pos = lo;
-    if (pos < K) {
-      cur = idx[pos];
-      cp = p[pos];
+    int start = 0;
+    if (c1 > 0) {
+      const int lo = (c1 - 1) * seg + 1;
+      const int hi = min(c1 * seg, K);
+      int c2 = 0;
+#pragma unroll 8
+      for (int kk = lo; kk < hi; ++kk) c2 += idx[kk] < target;
+      start = lo + c2;
     }
+    pos = start;
+    load_at(pos, e0, p0);
+    load_at(pos + 1, e1, p1);
+    load_at(pos + 2, e2, p2);
+    load_at(pos + 3, e3, p3);
   }
+
+  __device__ __forceinline__ int cur() const { return e0; }
+  __device__ __forceinline__ float cp() const { return p0; }
+
   __device__ __forceinline__ void next() {
+    e0 = e1;
+    p0 = p1;
+    e1 = e2;
+    p1 = p2;
+    e2 = e3;
+    p2 = p3;
     ++pos;
-    if (pos < K) {
-      cur = idx[pos];
-      cp = p[pos];
-    } else {
-      cur = INT_MAX;
-    }
+    load_at(pos + 3, e3, p3);
   }
 };
 
@@ -188,7 +222,7 @@ struct FwdSweepParams {
   const float* tsort_p;
   int32_t n_vt, tiles_per_split;
   int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits
-  f32x4* partial;  // [splits][2][rbs * 256]: (running max in log2 units, sum of exp2, sum p*z)
+  f32x4* partial;  // [splits][2][rbs * 256]: (offset m2 in log2 units, sum of exp2(s log2 e - m2), sum p*z)
 };
 
 // Block tiles are 256 x 256 with 8 waves (2 per SIMD), each 128 x 64.
@@ -257,39 +291,47 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
       const int nvalid = static_cast<int>(min<int64_t>(64, P.V - cs));
       const float* sr = stage + rloc * kStageLd + sub * 64;
       if (nvalid > 0) {
+        // Running sum of exp2(s * log2 e - m2) with an offset m2 that only
+        // moves when the new values would exceed it by more than 2^64, so the
+        // block's sum and its max come out of one pass over the LDS row.
         float mx = -INFINITY;
+        float s = 0.f;
+        const float off = m2 == -INFINITY ? 0.f : m2;
         if (nvalid == 64) {
 #pragma unroll 8
           for (int c = 0; c < 64; c += 4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
             mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            s += __builtin_amdgcn_exp2f(fmaf(x[0], P.k2, -off));
+            s += __builtin_amdgcn_exp2f(fmaf(x[1], P.k2, -off));
+            s += __builtin_amdgcn_exp2f(fmaf(x[2], P.k2, -off));
+            s += __builtin_amdgcn_exp2f(fmaf(x[3], P.k2, -off));
           }
         } else {
-          for (int c = 0; c < nvalid; ++c) mx = fmaxf(mx, sr[c]);
-        }
-        const float mnew = fmaxf(m2, mx * P.k2);
-        float s = 0.f;
-        if (nvalid == 64) {
-#pragma unroll 8
-          for (int c = 0; c < 64; c += 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
-            s += __builtin_amdgcn_exp2f(fmaf(x[0], P.k2, -mnew));
-            s += __builtin_amdgcn_exp2f(fmaf(x[1], P.k2, -mnew));
-            s += __builtin_amdgcn_exp2f(fmaf(x[2], P.k2, -mnew));
-            s += __builtin_amdgcn_exp2f(fmaf(x[3], P.k2, -mnew));
+          for (int c = 0; c < nvalid; ++c) {
+            mx = fmaxf(mx, sr[c]);
+            s += __builtin_amdgcn_exp2f(fmaf(sr[c], P.k2, -off));
           }
-        } else {
-          for (int c = 0; c < nvalid; ++c) s += __builtin_amdgcn_exp2f(fmaf(sr[c], P.k2, -mnew));
         }
-        se = se * __builtin_amdgcn_exp2f(m2 - mnew) + s;
-        m2 = mnew;
+        const float mb = mx * P.k2;
+        if (m2 == -INFINITY || mb > m2 + 64.f) {
+          // First block of this thread, or values far above the offset:
+          // redo the block relative to its own max.
+          s = 0.f;
+          for (int c = 0; c < nvalid; ++c) s += __builtin_amdgcn_exp2f(fmaf(sr[c], P.k2, -mb));
+          se = (m2 == -INFINITY) ? s : se * __builtin_amdgcn_exp2f(m2 - mb) + s;
+          m2 = mb;
+        } else {
+          se += s;
+        }
       }
       // Walk the row's sorted teacher list past this half tile, keeping the
       // entries that fall in this thread's quarter.
       const int c0 = static_cast<int>(col0);
       const int c1 = static_cast<int>(cs);
-      while (cur.cur < c0 + 128) {
-        if (cur.cur >= c1 && cur.cur < c1 + 64) gz += cur.cp * sr[cur.cur - c1];
+      while (cur.cur() < c0 + 128) {
+        const int e = cur.cur();
+        if (e >= c1 && e < c1 + 64) gz += cur.cp() * sr[e - c1];
         cur.next();
       }
       __syncthreads();
@@ -426,8 +468,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
         }
         const int c0 = static_cast<int>(col0);
         const int c1 = static_cast<int>(cs);
-        while (cur.cur < c0 + 128) {
-          if (cur.cur >= c1 && cur.cur < c1 + 64) sr[cur.cur - c1] -= c * cur.cp;
+        while (cur.cur() < c0 + 128) {
+          const int e = cur.cur();
+          if (e >= c1 && e < c1 + 64) sr[e - c1] -= c * cur.cp();
           cur.next();
         }
       }

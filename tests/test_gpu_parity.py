@@ -224,3 +224,23 @@ def test_caller_workspace_reuse():
     torch.cuda.synchronize()
     assert l1.item() == l2.item()
     assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0])
+def test_wide_logit_range(T):
+    """Logit scale grows ~400x across the vocabulary (row maxima in the last
+    tiles far above the first tiles'), exercising the online max offset."""
+    from workloads import bf16_bits
+    wl = make_workload("tiny", N=256, d=64, V=3000, K=12, seed_offset=11)
+    scale = np.linspace(0.1, 40.0, wl.V, dtype=np.float32)[:, None]
+    wl.W_bits = bf16_bits(bf16_to_f32(wl.W_bits) * scale)
+    _check_full(wl, T=T, chunk=128, vslab=1024, label="wide-range")
+
+
+def test_large_logits_do_not_overflow():
+    """Logits around 10^3 in magnitude: exp must never be taken unshifted."""
+    from workloads import bf16_bits
+    wl = make_workload("tiny", N=128, d=64, V=1500, K=6, seed_offset=12)
+    wl.h_bits = bf16_bits(bf16_to_f32(wl.h_bits) * 64.0)
+    wl.W_bits = bf16_bits(bf16_to_f32(wl.W_bits) * 16.0)
+    _check_full(wl, T=1.0, label="large-logits")
