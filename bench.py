@@ -53,6 +53,77 @@ def traffic_for(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def _read_counter_csv(path: str):
+    """{dispatch id: (kernel name, value)} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            did = int(r["Dispatch_Id"])
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            prev = out.get(did)
+            out[did] = (name, val + (prev[1] if prev else 0.0))
+    return out
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, command: str) -> dict:
+    """HBM bytes per launch of each path kernel from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
+    one plain device copy of copy_mib MiB (the largest copy-kernel dispatch of the
+    same run), so the result is in true bytes.
+    """
+    fetch = _read_counter_csv(fetch_csv)
+    write = _read_counter_csv(write_csv)
+    n = copy_mib << 20
+
+    def copy_kib(d):
+        cands = [v for name, v in d.values() if "copyBuffer" in name or "copy" in name.lower()]
+        if not cands:
+            raise SystemExit("no copy kernel found in the counter run")
+        return max(cands)
+
+    rscale = n / (copy_kib(fetch) * 1024.0)
+    wscale = n / (copy_kib(write) * 1024.0)
+    kernels = {}
+    for tag, d, scale in (("fetch", fetch, rscale), ("write", write, wscale)):
+        for name, v in d.values():
+            short = name.split("(")[0].split("::")[-1].replace("void ", "").strip()
+            if not short.startswith("k_"):
+                continue
+            k = kernels.setdefault(short[2:], {"launches_fetch": 0, "launches_write": 0,
+                                               "fetch_bytes": 0.0, "write_bytes": 0.0})
+            k[f"launches_{tag}"] += 1
+            k[f"{tag}_bytes"] += v * 1024.0 * scale
+    for k in kernels.values():
+        fb = k["fetch_bytes"] / max(k["launches_fetch"], 1)
+        wb = k["write_bytes"] / max(k["launches_write"], 1)
+        k.update(fetch_bytes=fb, write_bytes=wb, bytes_per_launch=fb + wb)
+        del k["launches_write"]
+        k["launches"] = k.pop("launches_fetch")
+    return {
+        "source_sha256": kernel_source_hash(),
+        "command": command,
+        "copy_calibration": {"bytes": n, "fetch_scale": rscale, "write_scale": wscale},
+        "kernels": kernels,
+    }
+
+
+def summarize_stats(stats_csv: str, command: str) -> str:
+    """Markdown table from a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"Command: `{command}`", "",
+             "| kernel | calls | total ms | avg us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| {name} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(wl, rows: int):
     """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
     import numpy as np
@@ -87,12 +158,26 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM counters)")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit (no GPU)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE counter runs (no GPU)")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     args = ap.parse_args()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats, args.command), end="")
+        return 0
+    if args.summarize_traffic:
+        t = summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib or 1024, args.command)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the path is "
               "single-GPU: no collectives or sharding)", file=sys.stderr)

@@ -220,8 +220,8 @@ struct FwdSweepParams {
   float k2;  // log2(e) / T
   const int32_t* tsort_idx;
   const float* tsort_p;
-  int32_t n_vt, tiles_per_split;
-  int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits
+  int32_t n_vt;
+  int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits (splits <= n_vt)
   f32x4* partial;  // [splits][2][rbs * 256]: (offset m2 in log2 units, sum of exp2(s log2 e - m2), sum p*z)
 };
 
@@ -261,8 +261,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
   const int wn = wave % kWN;
   int rb, split;
   grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
-  const int vt0 = split * P.tiles_per_split;
-  const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
+  // Vocabulary tiles split as evenly as possible (sizes differ by at most one).
+  const int vt0 = static_cast<int>(static_cast<int64_t>(split) * P.n_vt / P.splits);
+  const int vt1 = static_cast<int>(static_cast<int64_t>(split + 1) * P.n_vt / P.splits);
   const int rloc = tid & (kTile - 1);
   const int sub = tid >> 8;
   const int row = rb * kTile + rloc;  // chunk-local row whose statistics this thread keeps
@@ -399,8 +400,8 @@ struct BwdGParams {
   int32_t slab_w;
   int64_t vslab;
   uint16_t* G;  // [chunk_alloc][vslab]
-  int32_t n_vt, tiles_per_split;
-  int32_t rbs, splits;
+  int32_t n_vt;
+  int32_t rbs, splits;  // splits <= n_vt
 };
 
 __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
@@ -412,8 +413,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
   const int wn = wave % kWN;
   int rb, split;
   grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
-  const int vt0 = split * P.tiles_per_split;
-  const int vt1 = min(P.n_vt, vt0 + P.tiles_per_split);
+  // Vocabulary tiles split as evenly as possible (sizes differ by at most one).
+  const int vt0 = static_cast<int>(static_cast<int64_t>(split) * P.n_vt / P.splits);
+  const int vt1 = static_cast<int>(static_cast<int64_t>(split + 1) * P.n_vt / P.splits);
   const int rloc = tid & (kTile - 1);
   const int sub = tid >> 8;
   const int row = rb * kTile + rloc;
@@ -656,11 +658,9 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
                          c0, rows, p.K, invT, tidx, tp, negent);
     }
-    const int want = splits_for(rbs, p.n_vt);
-    const int tps = static_cast<int>(ceil_div(p.n_vt, want));
-    const int splits = static_cast<int>(ceil_div(p.n_vt, tps));
+    const int splits = splits_for(rbs, p.n_vt);
     FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, tidx, tp,
-                      static_cast<int32_t>(p.n_vt), tps, rbs, splits, partial};
+                      static_cast<int32_t>(p.n_vt), rbs, splits, partial};
     {
       const double dd = static_cast<double>(p.d);
       TraceScope ts(st, "fwd_sweep", 2.0 * rows * static_cast<double>(p.V) * dd,
@@ -707,11 +707,9 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int64_t slab0 = s * p.vslab;
       const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
-      const int want = splits_for(rbs, nvt);
-      const int tps = static_cast<int>(ceil_div(nvt, want));
-      const int splits = static_cast<int>(ceil_div(nvt, tps));
+      const int splits = splits_for(rbs, nvt);
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
-                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, tps, rbs, splits};
+                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
