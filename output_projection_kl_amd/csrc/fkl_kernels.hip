@@ -398,14 +398,27 @@ struct BwdGParams {
   const Scalars* sc;
   int64_t slab0;
   int32_t slab_w;
-  int64_t vslab;
-  uint16_t* G;  // [chunk_alloc][vslab]
+  int64_t ld_g;  // row stride of G^T (chunk_alloc)
+  uint16_t* G;   // G^T [vslab][chunk_alloc]
   int32_t n_vt;
   int32_t rbs, splits;  // splits <= n_vt
 };
 
+// LDS of the gradient-block kernel: the operand ring during the contraction,
+// then the tile's G values as bf16 stored column-major (kGtLd rows per
+// column, padded), plus the per-row constants of the block's 256 rows.
+constexpr int kGtLd = kTile + 8;
+constexpr int kGtStageBytes = kTile * kGtLd * 2;
+constexpr int kBwdGConstOff = kGtStageBytes > MainCfg::kLdsBytes ? kGtStageBytes : MainCfg::kLdsBytes;
+constexpr int kBwdGLdsBytes = kBwdGConstOff + 2 * kTile * 4;
+
+// One 256 x 256 tile of G = c_r (softmax(z/T) - p~) per step: each wave turns
+// its accumulators into c_r * exp2(z log2(e)/T - lse_r log2(e)) in registers,
+// stores them as bf16 into a column-major LDS tile, the row owners subtract
+// c_r p_k at the teacher entries inside the tile, and the tile is written to
+// the transposed gradient block G^T [vslab][chunk_alloc] with 16-byte stores.
 __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
-  __shared__ __align__(16) char lds[kKernelLdsBytes];
+  __shared__ __align__(16) char lds[kBwdGLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -429,75 +442,75 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
     c = (valid && n > 0) ? static_cast<float>(static_cast<double>(g) * P.T / static_cast<double>(n)) : 0.f;
     lse2 = P.row_lse[grow] * kLog2e;
   }
+  float* row_lse2 = reinterpret_cast<float*>(lds + kBwdGConstOff);
+  float* row_c = row_lse2 + kTile;
+  if (sub == 0) {
+    row_lse2[rloc] = lse2;
+    row_c[rloc] = c;
+  }
   Cursor cur;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
-           P.K, static_cast<int>(P.slab0) + vt0 * kTile, c != 0.f && vt0 < vt1);
+           P.K, static_cast<int>(P.slab0) + vt0 * kTile + sub * 128, c != 0.f && vt0 < vt1);
 
   const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
   const int nk = static_cast<int>((P.d + kStageK - 1) / kStageK);
-  float* stage = reinterpret_cast<float*>(lds);
+  uint16_t* gt = reinterpret_cast<uint16_t*>(lds);
   const int64_t slab_end = P.slab0 + P.slab_w;
 
   for (int vt = vt0; vt < vt1; ++vt) {
     f32x16 acc[4][kNBW];
     zero_acc(acc);
     const int64_t vbase = P.slab0 + static_cast<int64_t>(vt) * kTile;
+    // (the mainloop's opening barrier also publishes row_lse2 / row_c)
     gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc,
                                            lds);
-    for (int half = 0; half < 2; ++half) {
-      const int64_t col0 = vbase + half * 128;
-      if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
-      __syncthreads();
-      {
-        // Row owner (one quarter of the half tile): G = c * exp2(z * log2(e)/T - lse * log2(e)),
-        // then -c * p at the row's teacher indices that fall in the quarter.
-        const int64_t cs = col0 + sub * 64;
-        float* sr = stage + rloc * kStageLd + sub * 64;
-        const int nvalid = static_cast<int>(min<int64_t>(64, slab_end - cs));
-        if (c == 0.f || nvalid <= 0) {
-#pragma unroll 8
-          for (int cc = 0; cc < 64; cc += 4) *reinterpret_cast<f32x4*>(sr + cc) = f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-#pragma unroll 8
-          for (int cc = 0; cc < 64; cc += 4) {
-            f32x4 x = *reinterpret_cast<const f32x4*>(sr + cc);
+    // Registers -> G values -> bf16 column-major LDS tile. Elements i = 4j..4j+3
+    // of a block are 4 consecutive rows of one column: one 8-byte store.
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[e] = (cc + e < nvalid) ? c * __builtin_amdgcn_exp2f(fmaf(x[e], P.k2, -lse2)) : 0.f;
-            *reinterpret_cast<f32x4*>(sr + cc) = x;
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r4 = wm * 128 + acc_row(mb, 4 * j, lane);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r4);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(row_c + r4);
+#pragma unroll
+        for (int nb = 0; nb < kNBW; ++nb) {
+          const int col = wn * (kNBW * 32) + acc_col(nb, lane);
+          const bool col_ok = vbase + col < slab_end;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[mb][nb][4 * j + e];
+            const float gv = c4[e] * __builtin_amdgcn_exp2f(fmaf(x, P.k2, -l4[e]));
+            o[e] = static_cast<__bf16>((col_ok && c4[e] != 0.f) ? gv : 0.f);
           }
-        }
-        const int c0 = static_cast<int>(col0);
-        const int c1 = static_cast<int>(cs);
-        while (cur.cur() < c0 + 128) {
-          const int e = cur.cur();
-          if (e >= c1 && e < c1 + 64) sr[e - c1] -= c * cur.cp();
-          cur.next();
+          *reinterpret_cast<bf16x4*>(gt + col * kGtLd + r4) = o;
         }
       }
-      __syncthreads();
-      uint16_t* gdst = P.G + static_cast<int64_t>(rb) * kTile * P.vslab + static_cast<int64_t>(vt) * kTile +
-                       half * 128;
+    }
+    __syncthreads();
+    // Row owners: subtract c * p at the teacher entries of their half of the tile.
+    {
+      const int c_lo = static_cast<int>(vbase) + sub * 128;
+      while (cur.cur() < c_lo + 128) {
+        const int e = cur.cur();
+        __bf16* q = reinterpret_cast<__bf16*>(gt + (e - static_cast<int>(vbase)) * kGtLd + rloc);
+        *q = static_cast<__bf16>(static_cast<float>(*q) - c * cur.cp());
+        cur.next();
+      }
+      // skip the other half's entries up to the next tile's range
+      while (cur.cur() < c_lo + 256) cur.next();
+    }
+    __syncthreads();
+    uint16_t* gdst = P.G + (static_cast<int64_t>(vt) * kTile) * P.ld_g + static_cast<int64_t>(rb) * kTile;
 #pragma unroll 4
-      for (int i = 0; i < (kTile * 128 / 8) / kBlockThreads; ++i) {
-        const int q = tid + i * kBlockThreads;
-        const int r = q >> 4;
-        const int cc8 = (q & 15) * 8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + cc8);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + cc8 + 4);
-        bf16x8 o;
-        o[0] = static_cast<__bf16>(x0[0]);
-        o[1] = static_cast<__bf16>(x0[1]);
-        o[2] = static_cast<__bf16>(x0[2]);
-        o[3] = static_cast<__bf16>(x0[3]);
-        o[4] = static_cast<__bf16>(x1[0]);
-        o[5] = static_cast<__bf16>(x1[1]);
-        o[6] = static_cast<__bf16>(x1[2]);
-        o[7] = static_cast<__bf16>(x1[3]);
-        *reinterpret_cast<bf16x8*>(gdst + static_cast<int64_t>(r) * P.vslab + cc8) = o;
-      }
-      __syncthreads();
+    for (int i = 0; i < (kTile * kTile / 8) / kBlockThreads; ++i) {
+      const int q = tid + i * kBlockThreads;
+      const int cc = q >> 5;
+      const int r8 = (q & 31) * 8;
+      *reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(cc) * P.ld_g + r8) =
+          *reinterpret_cast<const u32x4*>(gt + cc * kGtLd + r8);
     }
   }
 }
@@ -545,29 +558,42 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
   zero_acc(acc);
   gemm_mainloop<TA, TB, kNBW, kWN>(P.A, P.B, m0, n0, P.nk, acc, lds);
   // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
-  // 32 lanes per row move 512 contiguous bytes with 16-byte accesses.
+  // 32 lanes per row move 512 contiguous bytes with 16-byte accesses. When
+  // accumulating, all of a thread's old values for the half are loaded before
+  // the staging, so their latency is paid once per half.
   float* stage = reinterpret_cast<float*>(lds);
   const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
+  constexpr int kPer = (kTile * 32) / kBlockThreads;  // 16-byte pieces per thread per half
   for (int half = 0; half < 2; ++half) {
-    if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
-    __syncthreads();
     const int64_t cbase = n0 + half * 128;
     const int cmax = static_cast<int>(min<int64_t>(128, P.n_lim - cbase));
     float* ctile = P.C + m0 * P.ldc + cbase;
-#pragma unroll 4
-    for (int i = 0; i < (kTile * 32) / kBlockThreads; ++i) {
+    f32x4 old[kPer];
+    if (P.beta) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = tid + i * kBlockThreads;
+        const int r = q >> 5;
+        const int c4 = (q & 31) * 4;
+        old[i] = (r < rmax && c4 < cmax)
+                     ? *reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) old[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
       const int q = tid + i * kBlockThreads;
       const int r = q >> 5;
       const int c4 = (q & 31) * 4;
       if (r < rmax && c4 < cmax) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + c4);
-        f32x4* dst = reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4);
-        if (P.beta) {
-          const f32x4 o = *dst;
-          *dst = f32x4{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
-        } else {
-          *dst = v;
-        }
+        *reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4) =
+            f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]};
       }
     }
     __syncthreads();
@@ -586,9 +612,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int w = blockIdx.x;
   if (w < P.h_tiles) {
-    gemm_acc_tile<false, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
+    gemm_acc_tile<true, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
   } else {
-    gemm_acc_tile<true, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
+    gemm_acc_tile<false, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
   }
 }
 
@@ -709,7 +735,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
       const int splits = splits_for(rbs, nvt);
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
-                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, rbs, splits};
+                    a.grad_loss, sc, slab0, slab_w, p.chunk_alloc, G, nvt, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
@@ -720,7 +746,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows], one launch.
       GradParams gp2;
       GemmAccParams& hp = gp2.gh;
-      hp.A = Operand{G, p.vslab, p.chunk_alloc, p.vslab};
+      const int64_t rows_written = static_cast<int64_t>(rbs) * kTile;  // G^T columns this chunk wrote
+      hp.A = Operand{G, p.chunk_alloc, rows_written, slab_w};
       hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
       hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
       hp.C = a.grad_h + c0 * p.d;
@@ -731,7 +758,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       hp.mblocks = rbs;
       hp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
       GemmAccParams& wp = gp2.gw;
-      wp.A = Operand{G, p.vslab, p.vslab, rows};
+      wp.A = Operand{G, p.chunk_alloc, slab_w, rows_written};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
       wp.nk = static_cast<int32_t>(ceil_div(rows, kStageK));
       wp.C = a.grad_W + slab0 * p.d;
