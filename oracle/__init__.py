@@ -12,5 +12,6 @@ from .fkl_oracle import (  # noqa: F401
     backward,
     forward_rows,
     grad_h_rows,
+    grad_W_rows,
     dense_teacher_grid,
 )

@@ -61,6 +61,7 @@ __all__ = [
     "backward",
     "forward_rows",
     "grad_h_rows",
+    "grad_W_rows",
     "dense_teacher_grid",
 ]
 
@@ -226,6 +227,34 @@ def grad_h_rows(h, W, t_idx, t_logit, T: float, n_valid: int, rows, grad_loss: f
         return np.zeros((len(rows), W.shape[1]))
     G = (float(grad_loss) * T / n_valid) * m[:, None] * (q - p_tilde)
     return G @ W
+
+
+def grad_W_rows(h, W, t_idx, t_logit, T: float, vocab_rows, row_lse, grad_loss: float = 1.0,
+                mask=None):
+    """grad_W for selected vocabulary rows: sum_r G[r, v] h_r.
+
+    Column v of G needs every row's logit s[r, v] = h_r . W_v / T and every
+    row's normaliser; ``row_lse`` must be the oracle's own forward result
+    for all rows. Returns [len(vocab_rows), d] float64.
+    """
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    h = _f64(h)
+    N = h.shape[0]
+    valid = _valid_rows(mask, N)
+    n = int(valid.sum())
+    if n == 0:
+        return np.zeros((len(vocab_rows), h.shape[1]))
+    Wv = _f64(np.asarray(W)[vocab_rows])
+    s = (h @ Wv.T) / T                                   # [N, len(vocab_rows)]
+    q = np.exp(s - _f64(row_lse)[:, None])
+    p, _ = teacher_distribution(t_logit, T)
+    t_idx = np.asarray(t_idx, dtype=np.int64)
+    p_tilde = np.zeros_like(q)
+    for j, v in enumerate(vocab_rows):
+        hit_r, hit_k = np.nonzero(t_idx == v)
+        p_tilde[hit_r, j] = p[hit_r, hit_k]
+    G = (float(grad_loss) * T / n) * valid[:, None] * (q - p_tilde)
+    return G.T @ h
 
 
 def dense_teacher_grid(t_idx, t_logit, T: float, V: int) -> np.ndarray:

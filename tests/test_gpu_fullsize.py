@@ -1,0 +1,181 @@
+"""Parity at the full sizes of the named workloads, in the launch configuration
+bench.py times (the workload's own chunk, the default vocabulary slab).
+
+The oracle cannot recompute a whole 32K x 201K problem in fp64 within a test,
+so each size is checked where the oracle's cost stays at a few of its rows:
+
+* sampled rows of an unmasked (or packed-mask) run: row_lse, row KL and the
+  grad_h row are functions of that row's logits alone; the loss equals
+  T^2/n times the sum of the valid rows' KL;
+* a masked-subset run: the same launch with only a spread set of rows valid,
+  whose loss, grad_h and the ENTIRE grad_W the oracle computes exactly from
+  those rows (masked rows contribute nothing, n counts the valid ones);
+* the 3B-like head, small enough for the oracle's full forward: every row's
+  row_lse and KL, the loss, and sampled vocabulary rows of grad_W.
+
+Tolerances as in the small-size parity tests: loss relative 1e-3, row_lse
+absolute 1e-3, grad_h / grad_W max error 2e-2 of the compared entries' max-abs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import output_projection_kl_amd as fkl
+from workloads.device import make_device_workload
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-3
+GRAD_TOL = 2e-2
+LSE_ATOL = 1e-3
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _run(wl, mask, grad_loss=None):
+    gl = None if grad_loss is None else torch.tensor([grad_loss], dtype=torch.float32, device=wl.h.device)
+    loss, lse, kl = fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, mask=mask, chunk=wl.chunk,
+                                return_row_kl=True)
+    gh, gW = fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, lse, T=wl.T, mask=mask, grad_loss=gl,
+                          chunk=wl.chunk)
+    torch.cuda.synchronize()
+    return loss.item(), lse, kl, gh, gW
+
+
+def _sample_rows(N, chunk, seed, n_random=24):
+    """Chunk and row-block edges, the first and last rows, and random rows."""
+    fixed = {0, 1, 255, 256, chunk - 1, chunk, N // 2, N - 257, N - 256, N - 1}
+    rng = np.random.default_rng(seed)
+    fixed |= set(int(r) for r in rng.choice(N, n_random, replace=False))
+    return np.array(sorted(r for r in fixed if 0 <= r < N), dtype=np.int64)
+
+
+def _rel_max(got, ref):
+    scale = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))
+
+
+def _W64(wl):
+    return wl.W.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["gptoss20b", "long64k", "temp"])
+def test_fullsize_sampled_rows(name):
+    dev = _dev()
+    wl = make_device_workload(name, dev)
+    print(f"[fullsize] {wl.describe()} mask={'packed' if wl.mask is not None else 'none'}", flush=True)
+    loss, lse, kl, gh, _ = _run(wl, wl.mask)
+    m = np.ones(wl.N, np.uint8) if wl.mask_np is None else wl.mask_np
+    n_valid = int(m.sum())
+    rows = _sample_rows(wl.N, wl.chunk, wl.seed)
+    if wl.mask_np is not None:  # every masked row (the document ends) is checked too
+        rows = np.union1d(rows, np.nonzero(m == 0)[0])
+    Wd = _W64(wl)
+    hr = wl.h[rows].float().cpu().numpy()
+    ti, tl, mr = wl.t_idx_np[rows], wl.t_logit_np[rows], m[rows]
+    sub = np.arange(len(rows))
+    r_lse, r_kl = oracle.forward_rows(hr, Wd, ti, tl, wl.T, sub)
+    r_gh = oracle.grad_h_rows(hr, Wd, ti, tl, wl.T, n_valid, sub, grad_loss=1.0, mask=mr)
+    g_lse = lse.cpu().numpy()[rows]
+    g_kl = kl.cpu().numpy()[rows]
+    g_gh = gh[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    valid = mr.astype(bool)
+    e_lse = float(np.abs(g_lse - r_lse).max())
+    e_kl = float(np.abs(g_kl[valid] - r_kl[valid]).max())
+    e_gh = _rel_max(g_gh[valid], r_gh[valid])
+    print(f"   {len(rows)} rows: lse {e_lse:.2e} kl {e_kl:.2e} grad_h {e_gh:.2e}", flush=True)
+    assert e_lse <= LSE_ATOL
+    assert e_kl <= 1e-3 * max(1.0, np.abs(r_kl).max())
+    assert e_gh <= GRAD_TOL
+    assert np.all(g_gh[~valid] == 0.0) and np.all(g_kl[~valid] == 0.0)
+    # loss = T^2 / n * sum of the valid rows' KL (the rows themselves are sampled above)
+    kl_all = kl.cpu().numpy().astype(np.float64)
+    assert loss == pytest.approx(wl.T ** 2 * kl_all[m.astype(bool)].sum() / n_valid, rel=1e-5)
+    assert np.isfinite(lse.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("name", ["gptoss20b", "long256k", "temp"])
+def test_fullsize_masked_subset(name):
+    """Same launch with a spread subset of valid rows: exact loss, grad_h and all of grad_W."""
+    dev = _dev()
+    wl = make_device_workload(name, dev, mask="none")
+    rows = _sample_rows(wl.N, wl.chunk, wl.seed + 7, n_random=30)
+    mask_np = np.zeros(wl.N, np.uint8)
+    mask_np[rows] = 1
+    mask = torch.from_numpy(mask_np).to(dev)
+    print(f"[fullsize-subset] {wl.describe()} valid rows {len(rows)}", flush=True)
+    before = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    loss, lse, kl, gh, gW = _run(wl, mask, grad_loss=0.75)
+    out_bytes = 4 * (1 + 2 * wl.N + wl.N * wl.d + wl.V * wl.d)
+    extra = torch.cuda.max_memory_allocated(dev) - before - out_bytes
+    fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, wl.T, chunk=wl.chunk)
+    print(f"   extra device memory {extra / 2**20:.1f} MiB, workspace {max(fb, bb) / 2**20:.1f} MiB", flush=True)
+    assert extra <= max(fb, bb) + (4 << 20)
+
+    Wd = _W64(wl)
+    hs = wl.h[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    ti, tl = wl.t_idx_np[rows], wl.t_logit_np[rows]
+    r_loss, r_lse, _ = oracle.forward(hs, Wd, ti, tl, wl.T)
+    r_gh, r_gW = oracle.backward(hs, Wd, ti, tl, wl.T, grad_loss=0.75)
+    del Wd
+    e_loss = abs(loss - r_loss) / abs(r_loss)
+    e_lse = float(np.abs(lse.cpu().numpy()[rows] - r_lse).max())
+    g_gh = gh[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    e_gh = _rel_max(g_gh, r_gh)
+    gh[torch.from_numpy(rows).to(dev)] = 0.0
+    masked_rows_zero = bool((gh == 0).all().item())  # every masked row is exactly zero
+    del gh
+    ref = torch.from_numpy(r_gW.astype(np.float32)).to(dev)
+    del r_gW
+    e_gW = float((gW - ref).abs().max().item() / ref.abs().max().item())
+    print(f"   loss {loss:.7g} ref {r_loss:.7g} rel {e_loss:.2e} | lse {e_lse:.2e} | grad_h {e_gh:.2e} | "
+          f"grad_W (all {wl.V} rows) {e_gW:.2e}", flush=True)
+    assert e_loss <= LOSS_RTOL
+    assert e_lse <= LSE_ATOL
+    assert e_gh <= GRAD_TOL
+    assert e_gW <= GRAD_TOL
+    assert masked_rows_zero
+
+
+def test_fullsize_3b_full_forward_and_grad_W_rows():
+    """3B-like head (chunk 1024): the oracle's full forward fits, so every row and
+    sampled vocabulary rows of grad_W (teacher hits, slab edges, tail) are checked."""
+    dev = _dev()
+    wl = make_device_workload("llama3b", dev)
+    print(f"[fullsize] {wl.describe()}", flush=True)
+    loss, lse, kl, gh, gW = _run(wl, None)
+    Wd = _W64(wl)
+    hd = wl.h.float().cpu().numpy().astype(np.float64)
+    r_loss, r_lse, r_kl = oracle.forward(hd, Wd, wl.t_idx_np, wl.t_logit_np, wl.T, chunk=wl.chunk)
+    e_loss = abs(loss - r_loss) / abs(r_loss)
+    e_lse = float(np.abs(lse.cpu().numpy() - r_lse).max())
+    e_kl = float(np.abs(kl.cpu().numpy() - r_kl).max())
+    # default vocabulary slab: 64 Mi gradient elements per chunk (65536 columns at chunk 1024)
+    slab = (64 << 20) // ((wl.chunk + 255) // 256 * 256)
+    hits, counts = np.unique(wl.t_idx_np, return_counts=True)
+    vrows = {0, 1, wl.V - 1, wl.V - 2, slab - 1, slab, 2 * slab - 1, int(hits[np.argmax(counts)])}
+    rng = np.random.default_rng(wl.seed)
+    vrows |= set(int(v) for v in rng.choice(hits, 8, replace=False))
+    vrows |= set(int(v) for v in rng.choice(wl.V, 8, replace=False))
+    vrows = np.array(sorted(v for v in vrows if 0 <= v < wl.V), dtype=np.int64)
+    r_gWr = oracle.grad_W_rows(hd, Wd, wl.t_idx_np, wl.t_logit_np, wl.T, vrows, r_lse)
+    g_gWr = gW[torch.from_numpy(vrows).to(dev)].cpu().numpy()
+    e_gW = _rel_max(g_gWr, r_gWr)
+    rows = _sample_rows(wl.N, wl.chunk, wl.seed)
+    r_gh = oracle.grad_h_rows(hd[rows], Wd, wl.t_idx_np[rows], wl.t_logit_np[rows], wl.T, wl.N,
+                              np.arange(len(rows)))
+    e_gh = _rel_max(gh[torch.from_numpy(rows).to(dev)].cpu().numpy(), r_gh)
+    print(f"   loss {loss:.7g} ref {r_loss:.7g} rel {e_loss:.2e} | lse {e_lse:.2e} | kl {e_kl:.2e} | "
+          f"grad_h rows {e_gh:.2e} | grad_W {len(vrows)} rows {e_gW:.2e}", flush=True)
+    assert e_loss <= LOSS_RTOL
+    assert e_lse <= LSE_ATOL
+    assert e_kl <= 1e-3 * max(1.0, np.abs(r_kl).max())
+    assert e_gh <= GRAD_TOL
+    assert e_gW <= GRAD_TOL

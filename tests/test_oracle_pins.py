@@ -341,6 +341,21 @@ def test_sampled_row_helpers_match_full():
     np.testing.assert_allclose(gh_r, gh[rows], rtol=1e-12, atol=1e-16)
 
 
+@pytest.mark.parametrize("T,mask_frac", [(1.0, 0.0), (1.7, 0.4)])
+def test_sampled_grad_W_rows_match_autograd(T, mask_frac):
+    """grad_W_rows (used at full size, where only some vocabulary rows are
+    checked) against torch autograd of the dense loss and the full backward."""
+    h, W, t_idx, t_logit, mask = _rand_problem(131, N=12, d=8, V=40, K=6, mask_frac=mask_frac)
+    _, _, _, gW_t, _ = _torch_dense_loss(h, W, t_idx, t_logit, T, mask)
+    _, lse, _ = oracle.forward(h, W, t_idx, t_logit, T, mask)
+    rows = np.array([0, 5, int(t_idx[0, 0]), int(t_idx[3, 2]), 39])
+    got = oracle.grad_W_rows(h, W, t_idx, t_logit, T, rows, lse, grad_loss=1.0, mask=mask)
+    np.testing.assert_allclose(got, gW_t[rows], rtol=1e-10, atol=1e-15)
+    _, gW = oracle.backward(h, W, t_idx, t_logit, T, mask, grad_loss=0.3)
+    got3 = oracle.grad_W_rows(h, W, t_idx, t_logit, T, rows, lse, grad_loss=0.3, mask=mask)
+    np.testing.assert_allclose(got3, gW[rows], rtol=1e-12, atol=1e-16)
+
+
 def test_oracle_rejects_bad_teacher():
     h, W, t_idx, t_logit, _ = _rand_problem(121)
     bad = t_idx.copy()

@@ -44,6 +44,45 @@ def _seed_of(ss: np.random.SeedSequence) -> int:
     return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
 
 
+def perturbed_head_teacher(h, W, K: int, seed: int, device, rows_per_pass: int = 1024):
+    """Teacher cache from a perturbed copy of the student head.
+
+    W_t = bf16(float32(W) + 0.1 * N(0, 1/d)); the teacher keeps the exact
+    top-K of its fp32 logits h W_t^T per row (values descending), computed in
+    float32 on the device without TF32, in passes of rows_per_pass rows.
+    Input generation only: the same arrays feed the library and the oracle.
+    """
+    import torch
+
+    d = W.shape[1]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    Wt = torch.empty_like(W)
+    block = 16384
+    for v0 in range(0, W.shape[0], block):
+        v1 = min(W.shape[0], v0 + block)
+        noise = torch.randn((v1 - v0, d), generator=g, device=device, dtype=torch.float32)
+        Wt[v0:v1] = W[v0:v1].float() + noise * float(0.1 / np.sqrt(d))
+    Wt32 = Wt.float()
+    del Wt
+    prev = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    try:
+        idx = torch.empty((h.shape[0], K), dtype=torch.int64, device=device)
+        val = torch.empty((h.shape[0], K), dtype=torch.float32, device=device)
+        for r0 in range(0, h.shape[0], rows_per_pass):
+            r1 = min(h.shape[0], r0 + rows_per_pass)
+            z = h[r0:r1].float() @ Wt32.t()
+            v, i = torch.topk(z, K, dim=1, largest=True, sorted=True)
+            idx[r0:r1] = i
+            val[r0:r1] = v
+            del z
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = prev
+    del Wt32
+    return idx.to(torch.int32).cpu().numpy(), val.cpu().numpy()
+
+
 def make_device_workload(name: str, device, seed_offset: int = 0, *, N: int | None = None,
                          mask: str | None = None, **overrides) -> DeviceWorkload:
     import torch
@@ -75,11 +114,14 @@ def make_device_workload(name: str, device, seed_offset: int = 0, *, N: int | No
     rng_idx = np.random.default_rng(s_idx)
     if cfg["teacher"] == "uniform":
         t_idx = uniform_teacher(rng_idx, Nr, V, K)
+        t_logit = sorted_teacher_logits(np.random.default_rng(s_logit), Nr, K)
     elif cfg["teacher"] == "zipf_uniform":
         t_idx = zipf_uniform_teacher(rng_idx, Nr, V, K)
+        t_logit = sorted_teacher_logits(np.random.default_rng(s_logit), Nr, K)
+    elif cfg["teacher"] == "perturbed_head":
+        t_idx, t_logit = perturbed_head_teacher(h, W, K, _seed_of(s_idx), device)
     else:
         raise ValueError(f"teacher recipe {cfg['teacher']} is not available for device workloads")
-    t_logit = sorted_teacher_logits(np.random.default_rng(s_logit), Nr, K)
     rng_mask = np.random.default_rng(s_mask)
     if cfg["mask"] == "none":
         m = None

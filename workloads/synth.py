@@ -123,43 +123,56 @@ def uniform_teacher(rng: np.random.Generator, N: int, V: int, K: int) -> np.ndar
     return out.astype(np.int32)
 
 
+def _zipf_cdf(V: int, a: float) -> np.ndarray:
+    """CDF of ranks 1..V with P(rank = k) proportional to k^-a (truncated Zipf)."""
+    w = np.arange(1, V + 1, dtype=np.float64) ** (-a)
+    c = np.cumsum(w)
+    return c / c[-1]
+
+
 def zipf_uniform_teacher(rng: np.random.Generator, N: int, V: int, K: int,
-                         zipf_a: float = 1.1) -> np.ndarray:
+                         zipf_a: float = 1.1, block: int = 8192) -> np.ndarray:
     """[N, K] int32: the Zipf half in columns [0, ceil(K/2)), then the uniform half.
 
-    Zipf half: ceil(K/2) distinct indices pi[rank-1], rank ~ Zipf(zipf_a)
-    truncated to [1, V]; uniform half: the remaining indices uniform in
-    [0, V), distinct from each other and from the Zipf half.
+    Zipf half: the first ceil(K/2) distinct values pi[rank-1] of a stream of
+    ranks drawn from Zipf(zipf_a) truncated to [1, V] (inverse CDF), pi a
+    vocabulary permutation drawn once; uniform half: the remaining indices
+    uniform in [0, V), distinct from each other and from the Zipf half. Rows
+    are generated in blocks of ``block`` rows from the one stream ``rng``.
     """
     if K > V:
         raise ValueError("K > V")
     kz = (K + 1) // 2
     ku = K - kz
     perm = rng.permutation(V).astype(np.int64)
-    zipf_part = np.empty((N, kz), dtype=np.int64)
-    todo = np.arange(N)
-    m = 4 * kz
-    while todo.size:
-        ranks = rng.zipf(zipf_a, size=(todo.size, m))
-        valid = ranks <= V
-        cand = perm[np.minimum(ranks, V) - 1]
-        ok, picked = _first_distinct(cand, valid, kz)
-        zipf_part[todo[ok]] = picked
-        todo = todo[~ok]
-        m *= 2
-    out = np.empty((N, K), dtype=np.int64)
-    out[:, :kz] = zipf_part
-    if ku:
-        todo = np.arange(N)
-        m = 2 * ku + 8
+    cdf = _zipf_cdf(V, zipf_a)
+    out = np.empty((N, K), dtype=np.int32)
+    for b0 in range(0, N, block):
+        n = min(N, b0 + block) - b0
+        zipf_part = np.empty((n, kz), dtype=np.int64)
+        todo = np.arange(n)
+        m = 4 * kz
         while todo.size:
-            cand = np.concatenate(
-                [zipf_part[todo], rng.integers(0, V, size=(todo.size, m), dtype=np.int64)], axis=1)
-            ok, picked = _first_distinct(cand, np.ones_like(cand, dtype=bool), K)
-            out[todo[ok], kz:] = picked[:, kz:]
+            ranks = np.searchsorted(cdf, rng.random((todo.size, m)), side="right")
+            cand = perm[np.minimum(ranks, V - 1)]
+            ok, picked = _first_distinct(cand, np.ones_like(cand, dtype=bool), kz)
+            zipf_part[todo[ok]] = picked
             todo = todo[~ok]
             m *= 2
-    return out.astype(np.int32)
+        blk = np.empty((n, K), dtype=np.int64)
+        blk[:, :kz] = zipf_part
+        if ku:
+            todo = np.arange(n)
+            m = 2 * ku + 8
+            while todo.size:
+                cand = np.concatenate(
+                    [zipf_part[todo], rng.integers(0, V, size=(todo.size, m), dtype=np.int64)], axis=1)
+                ok, picked = _first_distinct(cand, np.ones_like(cand, dtype=bool), K)
+                blk[todo[ok], kz:] = picked[:, kz:]
+                todo = todo[~ok]
+                m *= 2
+        out[b0:b0 + n] = blk
+    return out
 
 
 def sorted_teacher_logits(rng: np.random.Generator, N: int, K: int, std: float = 3.0) -> np.ndarray:
