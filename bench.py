@@ -4,7 +4,12 @@ One step = fkl_forward + fkl_backward over the whole GPT-OSS-20B-like head
 workload (N=32768 tokens, d=2880, V=201088, K=100 cached teacher entries,
 T=1, chunk=4096), inputs resident in HBM. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+  python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload gptoss20b]
+
+--workload picks one of the other synthetic workloads instead (llama3b: N=8192,
+d=3072, V=128256, chunk 1024; long64k / long256k: N=65536 / 262144 packed rows
+with the document ends masked; temp: N=16384, d=4096, V=128256, T=2 with a
+perturbed-head teacher).
 
 Throughput: value = tokens/s = N / step time; TFLOP/s counts 8*N*d*V per step
 (2NdV forward logits, 2NdV recomputed logits, 2NdV grad_h, 2NdV grad_W).
@@ -27,6 +32,13 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "gptoss20b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TEACHER_RECIPES = {
+    "gptoss20b": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
+    "llama3b": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
+    "long64k": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
+    "long256k": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
+    "temp": "exact top-100 of h W_t^T, W_t = W + 0.1 N(0,1/d) (bf16)",
+}
 
 
 def kernel_source_hash() -> str:
@@ -158,6 +170,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["gptoss20b", "llama3b", "long64k", "long256k", "temp"],
+                    help="synthetic workload (default: the GPT-OSS-20B-like head)")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
@@ -188,9 +203,9 @@ def main() -> int:
     from workloads.device import make_device_workload
 
     dev = torch.device("cuda", 0)
-    print(f"[bench] generating {WORKLOAD} inputs on {torch.cuda.get_device_name(dev)}", file=sys.stderr,
+    print(f"[bench] generating {args.workload} inputs on {torch.cuda.get_device_name(dev)}", file=sys.stderr,
           flush=True)
-    wl = make_device_workload(WORKLOAD, dev)
+    wl = make_device_workload(args.workload, dev)
     torch.cuda.synchronize()
     fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, wl.T, chunk=wl.chunk)
     ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
@@ -291,7 +306,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.describe(), "N": wl.N, "d": wl.d, "V": wl.V, "K": wl.K, "T": wl.T,
-                   "chunk": wl.chunk, "teacher": "zipf(1.1)+uniform top-100, logits N(0,9) sorted"},
+                   "chunk": wl.chunk, "teacher": TEACHER_RECIPES[args.workload],
+                   "mask": "packed: last token of each of 8 documents" if wl.mask is not None else "none"},
         "tflops": round(tflops, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "peak_gib": round(peak / 2**30, 3),

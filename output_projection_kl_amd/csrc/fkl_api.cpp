@@ -75,9 +75,20 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_blocksum = off;
   off = align256(off + static_cast<size_t>(rbs) * 8);
   p->fwd_bytes = off;
-  // backward: the bf16 gradient block of chunk_alloc x vslab
+  // backward: the bf16 gradient block of chunk_alloc x vslab, then grad_h
+  // partial sums when a full chunk needs a vocabulary split (sized for a full
+  // chunk; a shorter last chunk takes at most as many partial rows)
   p->off_G = shared_end;
-  p->bwd_bytes = align256(shared_end + static_cast<size_t>(p->chunk_alloc) * p->vslab * 2);
+  off = align256(shared_end + static_cast<size_t>(p->chunk_alloc) * p->vslab * 2);
+  int splits = 1;
+  for (int64_t slab_w : {p->vslab, s->V - (ceil_div(s->V, p->vslab) - 1) * p->vslab}) {
+    const int sp = grad_h_splits(chunk, slab_w, s->d);
+    if (sp > splits) splits = sp;
+  }
+  p->ghp_rows = splits > 1 ? splits * p->chunk_alloc : 0;
+  p->off_ghp = off;
+  off = align256(off + static_cast<size_t>(p->ghp_rows) * s->d * 4);
+  p->bwd_bytes = off;
   return FKL_OK;
 }
 

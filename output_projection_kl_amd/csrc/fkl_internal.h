@@ -31,7 +31,18 @@ struct Plan {
   // workspace offsets (bytes)
   size_t off_scalars, off_negent, off_tidx, off_tp, off_partial, off_blocksum, fwd_bytes;
   size_t off_G, bwd_bytes;
+  // grad_h split along the vocabulary: partial sums for up to ghp_rows
+  // (= splits x rows) rows of d fp32 each, reduced in a fixed order
+  int64_t ghp_rows;
+  size_t off_ghp;
 };
+
+constexpr int kMaxGradHSplits = 8;
+
+// Vocabulary splits for the grad_h tiles of one backward launch (rows of the
+// chunk, slab_w columns of the slab) so that no grad_h tile is much longer than
+// the launch's average work per CU; 1 when the launch is balanced without.
+int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d);
 
 fkl_status make_plan(const fkl_shape* s, Plan* p);
 

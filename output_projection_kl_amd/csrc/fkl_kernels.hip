@@ -526,7 +526,20 @@ struct GemmAccParams {
   int64_t ldc, m_lim, n_lim;
   int32_t beta;  // 0: C = A B^T, 1: C += A B^T
   int32_t mblocks, nblocks;
+  // Split of the contraction: split s covers stages [s * kper, (s + 1) * kper)
+  // and writes its own C + s * c_split (splits = 1: no split).
+  int32_t splits, kper;
+  int64_t c_split;
 };
+
+// Operand restricted to contraction indices [k0, k0 + klen).
+template <bool TRANS>
+__device__ __forceinline__ Operand k_window(const Operand& op, int64_t k0, int64_t klen) {
+  Operand o = op;
+  o.base = op.base + (TRANS ? k0 * op.ld : k0);
+  o.k_lim = min(klen, op.k_lim - k0);
+  return o;
+}
 
 // Renumber workgroup w of the contiguous range [first, first + count) so that
 // the members of the range on each XCD take one contiguous block of indices.
@@ -550,13 +563,20 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
   const int wave = tid >> 6;
   const int wm = wave / kWN;
   const int wn = wave % kWN;
+  const int tiles = P.mblocks * P.nblocks;
+  const int split = local / tiles;
   int mbi, nbi;
-  grouped_tile(local, P.mblocks, P.nblocks, 8, mbi, nbi);
+  grouped_tile(local - split * tiles, P.mblocks, P.nblocks, 8, mbi, nbi);
   const int64_t m0 = static_cast<int64_t>(mbi) * kTile;
   const int64_t n0 = static_cast<int64_t>(nbi) * kTile;
+  const int64_t k0 = static_cast<int64_t>(split) * P.kper * kStageK;
+  const int64_t klen = static_cast<int64_t>(P.kper) * kStageK;
+  const int nk = min(P.kper, P.nk - split * P.kper);
+  float* C = P.C + split * P.c_split;
   f32x16 acc[4][kNBW];
   zero_acc(acc);
-  gemm_mainloop<TA, TB, kNBW, kWN>(P.A, P.B, m0, n0, P.nk, acc, lds);
+  gemm_mainloop<TA, TB, kNBW, kWN>(k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk,
+                                   acc, lds);
   // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
   // 32 lanes per row move 512 contiguous bytes with 16-byte accesses. When
   // accumulating, all of a thread's old values for the half are loaded before
@@ -567,7 +587,7 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
   for (int half = 0; half < 2; ++half) {
     const int64_t cbase = n0 + half * 128;
     const int cmax = static_cast<int>(min<int64_t>(128, P.n_lim - cbase));
-    float* ctile = P.C + m0 * P.ldc + cbase;
+    float* ctile = C + m0 * P.ldc + cbase;
     f32x4 old[kPer];
     if (P.beta) {
 #pragma unroll
@@ -602,7 +622,8 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
 
 // grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk in one
 // launch: the first h_tiles workgroups take grad_h tiles (the longer
-// contraction, dispatched first), the rest grad_W tiles.
+// contraction, dispatched first; h_tiles counts tiles x vocabulary splits),
+// the rest grad_W tiles.
 struct GradParams {
   GemmAccParams gh, gw;
   int32_t h_tiles, w_tiles;
@@ -615,6 +636,20 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
     gemm_acc_tile<true, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
   } else {
     gemm_acc_tile<false, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
+  }
+}
+
+// grad_h[rows] (+)= sum over s of the split partial sums, in split order.
+__global__ __launch_bounds__(256) void k_reduce_grad_h(const f32x4* __restrict__ part, int splits,
+                                                       int64_t split_stride4, int64_t n4,
+                                                       f32x4* __restrict__ out, int beta) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
+    f32x4 a = beta ? out[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) {
+      const f32x4 v = part[sp * split_stride4 + i];
+      a = f32x4{a[0] + v[0], a[1] + v[1], a[2] + v[2], a[3] + v[3]};
+    }
+    out[i] = a;
   }
 }
 
@@ -657,6 +692,20 @@ __global__ void k_set_int(int32_t* p, int32_t v) {
 // ---------------------------------------------------------------------------
 // Launch sequences
 // ---------------------------------------------------------------------------
+
+int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d) {
+  if (rows <= 0 || slab_w <= 0) return 1;
+  const int64_t nb = ceil_div(d, kTile);
+  const int64_t h_tiles = ceil_div(rows, kTile) * nb;
+  const int64_t nk_h = ceil_div(slab_w, kStageK);
+  const int64_t w_tiles = ceil_div(slab_w, kTile) * nb;
+  const int64_t nk_w = ceil_div(rows, kStageK);
+  const int64_t per_cu = ceil_div(h_tiles * nk_h + w_tiles * nk_w, kTargetBlocks);
+  int64_t sp = ceil_div(nk_h, per_cu > 0 ? per_cu : 1);
+  if (sp < 1) sp = 1;
+  if (sp > kMaxGradHSplits) sp = kMaxGradHSplits;
+  return static_cast<int>(sp);
+}
 
 static inline int splits_for(int64_t rbs, int64_t tiles) {
   int64_t s = ceil_div(kTargetBlocks, rbs);
@@ -747,16 +796,29 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       GradParams gp2;
       GemmAccParams& hp = gp2.gh;
       const int64_t rows_written = static_cast<int64_t>(rbs) * kTile;  // G^T columns this chunk wrote
+      int hsplits = grad_h_splits(rows, slab_w, p.d);
+      if (hsplits > 1 && hsplits * rows_written > p.ghp_rows)
+        hsplits = static_cast<int>(p.ghp_rows / rows_written);
+      if (hsplits < 1) hsplits = 1;
       hp.A = Operand{G, p.chunk_alloc, rows_written, slab_w};
       hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
       hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
-      hp.C = a.grad_h + c0 * p.d;
       hp.ldc = p.d;
       hp.m_lim = rows;
       hp.n_lim = p.d;
-      hp.beta = s > 0;
       hp.mblocks = rbs;
       hp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
+      hp.splits = hsplits;
+      hp.kper = static_cast<int32_t>(ceil_div(hp.nk, hsplits));
+      if (hsplits > 1) {  // partial sums, reduced into grad_h after the launch
+        hp.C = reinterpret_cast<float*>(a.ws + p.off_ghp);
+        hp.beta = 0;
+        hp.c_split = rows_written * p.d;
+      } else {
+        hp.C = a.grad_h + c0 * p.d;
+        hp.beta = s > 0;
+        hp.c_split = 0;
+      }
       GemmAccParams& wp = gp2.gw;
       wp.A = Operand{G, p.chunk_alloc, slab_w, rows_written};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
@@ -768,13 +830,25 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.beta = chunk_index > 0;
       wp.mblocks = nvt;
       wp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
-      gp2.h_tiles = hp.mblocks * hp.nblocks;
+      wp.splits = 1;
+      wp.kper = wp.nk;
+      wp.c_split = 0;
+      gp2.h_tiles = hp.mblocks * hp.nblocks * hsplits;
       gp2.w_tiles = wp.mblocks * wp.nblocks;
       {
         TraceScope ts(st, "bwd_grads", 4.0 * rows * slab_w * dd,
                       4.0 * rows * slab_w + 2.0 * slab_w * dd + 2.0 * rows * dd +
                           (hp.beta ? 8.0 : 4.0) * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
         hipLaunchKernelGGL(k_bwd_grads, dim3(gp2.h_tiles + gp2.w_tiles), dim3(kBlockThreads), 0, st, gp2);
+      }
+      if (hsplits > 1) {
+        const int64_t n4 = static_cast<int64_t>(rows) * p.d / 4;
+        const int64_t rgrid = ceil_div(n4, 256) < 2048 ? ceil_div(n4, 256) : 2048;
+        TraceScope ts(st, "grad_h_reduce", 0.0, 4.0 * rows * p.d * (hsplits + (s > 0 ? 2 : 1)));
+        hipLaunchKernelGGL(k_reduce_grad_h, dim3(static_cast<unsigned>(rgrid)),
+                           dim3(256), 0, st, reinterpret_cast<const f32x4*>(a.ws + p.off_ghp), hsplits,
+                           rows_written * p.d / 4, n4, reinterpret_cast<f32x4*>(a.grad_h + c0 * p.d),
+                           static_cast<int>(s > 0));
       }
     }
   }
