@@ -2,9 +2,10 @@
 // staged through LDS, with loaders for operands stored contraction-contiguous
 // ("plain") or contraction-strided ("transposed").
 //
-// Block tile: 256 (M) x BN (N) x 64 (K) per LDS stage, 256 threads = 4 waves
-// in a 2 x 2 arrangement; each wave owns 128 x BN/2 of the output as
-// 4 x (BN/64) accumulators of v_mfma_f32_32x32x16_bf16 (32 x 32, fp32).
+// Block tile: 256 (M) x (WN * NBW * 32) (N), contraction in LDS stages of 32,
+// 2 x WN waves; each wave owns 128 x NBW*32 of the output as 4 x NBW
+// accumulators of v_mfma_f32_32x32x16_bf16 (32 x 32, fp32). The path's
+// kernels use WN = 4, NBW = 2: a 256 x 256 tile on 8 waves (2 per SIMD).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,8 +18,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256;       // block rows
-constexpr int kThreads = 256;  // four wave64s
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

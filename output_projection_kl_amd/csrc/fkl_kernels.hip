@@ -15,10 +15,13 @@
 //   k_accumulate    fixed-order fp64 running loss
 // Backward, per chunk and vocabulary slab (same section: each chunk's logits
 // are recomputed rather than stored):
-//   k_bwd_g         logits tile again -> G = c (exp(s - lse) - p~) -> bf16
-//                   gradient block in the workspace
+//   k_bwd_g         logits tile again -> G = c (exp(s - lse) - p~) in
+//                   registers -> bf16 transposed gradient block G^T in the
+//                   workspace (the teacher entries subtracted in LDS)
 //   k_bwd_grads     grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk
-//                   in one launch
+//                   in one launch (grad_h tiles optionally split along the
+//                   vocabulary into partial sums)
+//   k_reduce_grad_h grad_h[chunk] (+)= the partial sums, in split order
 #include <climits>
 #include <cmath>
 
