@@ -165,6 +165,61 @@ def cpu_baseline(wl, rows: int):
     }
 
 
+def bench_builder(args, torch, fkl, make_device_workload, dev) -> int:
+    """fkl_topk on the large-head shape: N=16384 rows, d=4096, V=128256, K=100,
+    teacher head W_t = W + 0.1 N(0, 1/d). One step = one full cache build."""
+    from workloads.device import perturbed_head
+    wl = make_device_workload("temp", dev, teacher="uniform")
+    Wt = perturbed_head(wl.W, 4242, dev)
+    K = 100
+    ws = torch.empty(fkl.topk_workspace_size(wl.N, wl.d, wl.V, K), dtype=torch.uint8, device=dev)
+    ti = torch.empty((wl.N, K), dtype=torch.int32, device=dev)
+    tl = torch.empty((wl.N, K), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        fkl.topk(wl.h, Wt, K, workspace=ws, t_idx=ti, t_logit=tl)
+    torch.cuda.synchronize()
+    fkl.trace_read()
+    fkl.trace_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        fkl.topk(wl.h, Wt, K, workspace=ws, t_idx=ti, t_logit=tl)
+    stop.record()
+    torch.cuda.synchronize()
+    fkl.trace_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    kernels = {k["name"]: {"launches_per_step": k["launches"] / args.steps,
+                           "avg_ms": k["total_ms"] / k["launches"],
+                           "tflops": (k["flops"] / k["launches"]) / (k["total_ms"] / k["launches"] / 1e3) / 1e12
+                           if k["flops"] else None} for k in fkl.trace_read()}
+    # context: torch fp32 GEMM (no TF32) + torch.topk over the same rows, in 1024-row passes
+    prev = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    Wt32 = Wt.float()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r0 in range(0, wl.N, 1024):
+        torch.topk(wl.h[r0:r0 + 1024].float() @ Wt32.t(), K, dim=1)
+    e1.record()
+    torch.cuda.synchronize()
+    torch.backends.cuda.matmul.allow_tf32 = prev
+    flops = 2.0 * wl.N * wl.d * wl.V
+    out = {
+        "metric": "teacher top-100 cache build rows/s (N=16384, d=4096, V=128256)",
+        "value": round(wl.N / (ms / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"teacher cache: N={wl.N} d={wl.d} V={wl.V} K={K}, W_t = W + 0.1 N(0,1/d)"},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+        "frac_of_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "torch_fp32_matmul_topk_ms": round(e0.elapsed_time(e1), 3),
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +233,8 @@ def main() -> int:
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM counters)")
+    ap.add_argument("--builder", action="store_true",
+                    help="time the teacher-cache builder (fkl_topk) on the large-head shape instead")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit (no GPU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -203,6 +260,8 @@ def main() -> int:
     from workloads.device import make_device_workload
 
     dev = torch.device("cuda", 0)
+    if args.builder:
+        return bench_builder(args, torch, fkl, make_device_workload, dev)
     print(f"[bench] generating {args.workload} inputs on {torch.cuda.get_device_name(dev)}", file=sys.stderr,
           flush=True)
     wl = make_device_workload(args.workload, dev)

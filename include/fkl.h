@@ -114,6 +114,41 @@ fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx,
                                 const float* t_logit, int32_t* bad_rows, void* stream);
 
 /*
+ * Offline teacher-cache builder: the step before the fused loss. The blog
+ * post (section "Two systems changes") caches each position's top-100
+ * teacher logits once, offline, and keeps nothing else of the teacher's
+ * distribution; this computes such a cache on the GPU.
+ *
+ * For every row r of h [N,d] (bf16, row-major) and a teacher head
+ * W [V,d] (bf16, row-major), the K largest logits z[r,v] = sum_j h[r,j] W[v,j]
+ * (bf16 products, fp32 accumulation) with their indices:
+ *   t_idx   int32 [N,K]  vocabulary indices, row-major
+ *   t_logit fp32  [N,K]  the logits, in descending order; equal logits are
+ *                        ordered by the lower index first, and the K-th place
+ *                        goes to the lowest indices among equal logits.
+ * The output is in the layout fkl_forward / fkl_backward read.
+ *
+ * Rows are processed `chunk` at a time (0: enough rows for a 512 MiB fp32
+ * logits block, at least 256): the logits of a chunk are formed in the
+ * workspace, chunk (rounded up to 256) x V (rounded up to 256) fp32, and the
+ * top-K of each row is selected exactly. Constraints: d a multiple of 8
+ * (<= 65536), 1 <= K <= min(V, 1024); h and W 16-byte aligned; the
+ * workspace 256-byte aligned. Argument errors return before any HIP call.
+ */
+typedef struct {
+  int64_t N, d, V;
+  int32_t K;
+  int32_t chunk;  /* rows per pass; 0 = default */
+} fkl_topk_shape;
+
+/* Workspace bytes of fkl_topk for this shape (host only). */
+fkl_status fkl_topk_workspace_size(const fkl_topk_shape* shape, size_t* bytes);
+
+fkl_status fkl_topk(const fkl_topk_shape* shape, const void* h, const void* W,
+                    int32_t* t_idx, float* t_logit,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing. While enabled (a process-wide switch), every launch of the
  * path's main kernels is bracketed by a pair of hipEvents recorded on the
  * call's own stream, tagged with the kernel name and the launch's

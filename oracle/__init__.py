@@ -14,4 +14,5 @@ from .fkl_oracle import (  # noqa: F401
     grad_h_rows,
     grad_W_rows,
     dense_teacher_grid,
+    topk_teacher,
 )

@@ -63,6 +63,7 @@ __all__ = [
     "grad_h_rows",
     "grad_W_rows",
     "dense_teacher_grid",
+    "topk_teacher",
 ]
 
 
@@ -267,3 +268,29 @@ def dense_teacher_grid(t_idx, t_logit, T: float, V: int) -> np.ndarray:
     grid = np.zeros((p.shape[0], V))
     np.put_along_axis(grid, np.asarray(t_idx, dtype=np.int64), p, axis=1)
     return grid
+
+
+def topk_teacher(h, W, K: int):
+    """The offline teacher cache: per row, the K largest logits z = h W^T.
+
+    The cache keeps each position's top-K (index, logit) pairs and nothing
+    else of the teacher's distribution [BLOG "Two systems changes"; AIX last
+    paragraph]. Logits are exact fp64 dot products of the given values. Order:
+    value descending; equal values by the lower vocabulary index first (the
+    reading taken for ties, which the pages do not discuss). Returns
+    (idx int64 [N, K], val float64 [N, K]).
+    """
+    h = _f64(h)
+    W = _f64(W)
+    N, V = h.shape[0], W.shape[0]
+    if not 1 <= K <= V:
+        raise ValueError("need 1 <= K <= V")
+    idx = np.empty((N, K), dtype=np.int64)
+    val = np.empty((N, K))
+    cols = np.arange(V)
+    for r in range(N):
+        z = W @ h[r]
+        order = np.lexsort((cols, -z))[:K]   # primary key -z, then the index
+        idx[r] = order
+        val[r] = z[order]
+    return idx, val

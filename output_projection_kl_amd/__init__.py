@@ -27,6 +27,9 @@ __all__ = [
     "forward",
     "backward",
     "validate_teacher",
+    "TopkShape",
+    "topk_workspace_size",
+    "topk",
     "trace_enable",
     "trace_read",
     "EXPORTED_SYMBOLS",
@@ -41,6 +44,8 @@ EXPORTED_SYMBOLS = (
     "fkl_forward",
     "fkl_backward",
     "fkl_validate_teacher",
+    "fkl_topk_workspace_size",
+    "fkl_topk",
     "fkl_trace_enable",
     "fkl_trace_read",
     "fkl_status_string",
@@ -83,6 +88,18 @@ class Shape(ctypes.Structure):
     ]
 
 
+class TopkShape(ctypes.Structure):
+    """Mirror of ``fkl_topk_shape``."""
+
+    _fields_ = [
+        ("N", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("K", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+    ]
+
+
 def library_path() -> str:
     return os.environ.get("FKL_LIBRARY", os.path.join(_PKG_DIR, _LIB_NAME))
 
@@ -102,10 +119,13 @@ def lib() -> ctypes.CDLL:
     L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
+    tshp = ctypes.POINTER(TopkShape)
+    L.fkl_topk_workspace_size.argtypes = [tshp, ctypes.POINTER(sz)]
+    L.fkl_topk.argtypes = [tshp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_trace_enable.argtypes = [ctypes.c_int]
     L.fkl_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_version",
-              "fkl_trace_enable", "fkl_trace_read"):
+              "fkl_topk_workspace_size", "fkl_topk", "fkl_trace_enable", "fkl_trace_read"):
         getattr(L, f).restype = ctypes.c_int
     L.fkl_status_string.argtypes = [ctypes.c_int]
     L.fkl_status_string.restype = ctypes.c_char_p
@@ -249,6 +269,40 @@ def validate_teacher(t_idx, t_logit, V: int) -> int:
     bad = torch.empty(1, dtype=torch.int32, device=t_idx.device)
     _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad), _stream()))
     return int(bad.item())
+
+
+def topk_workspace_size(N, d, V, K, chunk=0) -> int:
+    """Workspace bytes of topk() for this shape."""
+    s = TopkShape(N, d, V, K, chunk)
+    b = ctypes.c_size_t(0)
+    _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
+    return b.value
+
+
+def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None):
+    """Offline teacher cache: per row of h (bf16 [N,d]), the K largest logits of
+    h W^T (W bf16 [V,d]), descending, ties by the lower index.
+    Returns (t_idx int32 [N,K], t_logit fp32 [N,K])."""
+    torch = _torch()
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h and W must be 2-D")
+    N, d = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, (N, d))
+    _need(W, "W", torch.bfloat16, (V, d))
+    s = TopkShape(N, d, V, K, chunk)
+    b = ctypes.c_size_t(0)
+    _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
+    ws = _workspace(b.value, h.device, workspace)
+    if t_idx is None:
+        t_idx = torch.empty((N, K), dtype=torch.int32, device=h.device)
+    _need(t_idx, "t_idx", torch.int32, (N, K))
+    if t_logit is None:
+        t_logit = torch.empty((N, K), dtype=torch.float32, device=h.device)
+    _need(t_logit, "t_logit", torch.float32, (N, K))
+    _check(lib().fkl_topk(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(ws),
+                          ctypes.c_size_t(ws.numel()), _stream()))
+    return t_idx, t_logit
 
 
 def trace_enable(on: bool = True) -> None:

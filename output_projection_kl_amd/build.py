@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfkl.so")
 
-SOURCES = ["fkl_kernels.hip", "fkl_api.cpp", "fkl_trace.cpp"]
+SOURCES = ["fkl_kernels.hip", "fkl_topk.hip", "fkl_api.cpp", "fkl_trace.cpp"]
 ARCH = "gfx950"
 
 

@@ -92,6 +92,34 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   return FKL_OK;
 }
 
+fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
+  if (!s) return fail(FKL_EINVAL, "shape is NULL");
+  if (s->N < 0) return fail(FKL_EINVAL, "N must be >= 0");
+  if (s->N > (int64_t(1) << 31) - 1) return fail(FKL_EUNSUPPORTED, "N must be < 2^31");
+  if (s->d < 8 || s->d % 8 != 0) return fail(FKL_EINVAL, "d must be a positive multiple of 8");
+  if (s->d > 65536) return fail(FKL_EUNSUPPORTED, "d must be <= 65536");
+  if (s->V < 1) return fail(FKL_EINVAL, "V must be >= 1");
+  if (s->V > (int64_t(1) << 31) - 1024) return fail(FKL_EUNSUPPORTED, "V must be < 2^31 - 1024");
+  if (s->K < 1) return fail(FKL_EINVAL, "K must be >= 1");
+  if (s->K > 1024) return fail(FKL_EUNSUPPORTED, "K must be <= 1024");
+  if (s->K > s->V) return fail(FKL_EINVAL, "K must be <= V");
+  if (s->chunk < 0) return fail(FKL_EINVAL, "chunk must be >= 0");
+  p->N = s->N;
+  p->d = s->d;
+  p->V = s->V;
+  p->K = s->K;
+  p->ld = round_up(s->V, kTile);
+  int64_t chunk = s->chunk;
+  if (chunk == 0) {
+    chunk = kTopkDefaultBlockElems / p->ld / kTile * kTile;
+    if (chunk < kTile) chunk = kTile;
+  }
+  if (s->N > 0 && chunk > s->N) chunk = s->N;
+  p->chunk = chunk;
+  p->bytes = align256(static_cast<size_t>(round_up(chunk, kTile)) * p->ld * 4);
+  return FKL_OK;
+}
+
 }  // namespace fkl
 
 extern "C" {
@@ -178,6 +206,35 @@ fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx, co
       fkl::launch_validate(p.N, p.V, p.K, t_idx, t_logit, bad_rows, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("validate launch failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return FKL_OK;
+}
+
+fkl_status fkl_topk_workspace_size(const fkl_topk_shape* shape, size_t* bytes) {
+  fkl::TopkPlan p;
+  const fkl_status st = fkl::make_topk_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (bytes) *bytes = p.bytes;
+  return FKL_OK;
+}
+
+fkl_status fkl_topk(const fkl_topk_shape* shape, const void* h, const void* W, int32_t* t_idx, float* t_logit,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  fkl::TopkPlan p;
+  const fkl_status st = fkl::make_topk_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (p.N == 0) return FKL_OK;
+  if (!h || !W || !t_idx || !t_logit) return fail(FKL_EINVAL, "h, W, t_idx and t_logit must not be NULL");
+  if (!aligned(h, 16) || !aligned(W, 16)) return fail(FKL_EINVAL, "h and W must be 16-byte aligned");
+  if (!aligned(t_idx, 4) || !aligned(t_logit, 4)) return fail(FKL_EINVAL, "t_idx and t_logit must be 4-byte aligned");
+  if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_topk_workspace_size()");
+  const hipError_t e = fkl::launch_topk(p, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx,
+                                        t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("top-k launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
   return FKL_OK;

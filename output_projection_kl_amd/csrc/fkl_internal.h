@@ -86,7 +86,22 @@ class TraceScope {
   int slot_;
 };
 
+// Teacher-cache builder (fkl_topk): rows per pass and the fp32 logits block.
+struct TopkPlan {
+  int64_t N, d, V;
+  int32_t K;
+  int64_t chunk;  // rows per pass
+  int64_t ld;     // row stride of the logits block (V rounded up to 256)
+  size_t bytes;   // workspace: chunk rounded up to 256 rows x ld fp32
+};
+
+constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logits block (512 MiB)
+
+fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p);
+
 hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx, float* t_logit,
+                       char* ws, hipStream_t stream);
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx,
                            const float* t_logit, int32_t* bad_rows, hipStream_t stream);

@@ -1,0 +1,194 @@
+// Offline teacher-cache builder: per row of h, the K largest logits of
+// h W^T with their vocabulary indices (blog post on the page "Efficient
+// Offline Top-K Logits and Fused Chunked KL Loss Enable Scalable LLM
+// Distillation", section "Two systems changes": the teacher's top-100
+// logits per position are cached once, offline, and nothing else of its
+// distribution is kept).
+//
+// Per chunk of rows:
+//   k_topk_logits  256 x 256 MFMA tiles of z = h_chunk W^T (fp32 accumulation)
+//                  written to an fp32 logits block in the workspace
+//   k_topk_select  one workgroup per row: exact radix selection of the K
+//                  largest keys, then a bitonic sort in LDS
+//
+// Keys make every element distinct: key = (order-preserving bits of z) << 32
+// | (0xFFFFFFFF - index), so larger keys are larger logits and, for equal
+// logits, lower indices. The selection walks 12-bit digits of the key from the
+// top, keeping only the elements that share the digits chosen so far, until
+// the digit bin at the K-th key is taken whole.
+#include <climits>
+
+#include "fkl_device.h"
+#include "fkl_internal.h"
+#include "fkl_tiles.h"
+
+namespace fkl {
+
+__global__ __launch_bounds__(kBlockThreads, 1) void k_topk_logits(GemmAccParams P) {
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
+  const int tiles = P.mblocks * P.nblocks;
+  gemm_acc_tile<false, false>(P, xcd_contiguous(blockIdx.x, tiles), lds);
+}
+
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t topk_key(float v, int i) {
+  return (static_cast<uint64_t>(ordered_bits(v)) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - i);
+}
+
+constexpr int kSelThreads = 256;
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kMaxK = 1024;
+
+__global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __restrict__ logits, int64_t ld,
+                                                             int V, int K, int Kp, int64_t r0,
+                                                             int32_t* __restrict__ t_idx,
+                                                             float* __restrict__ t_logit) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t keys[kMaxK];
+  __shared__ uint32_t above_of[kSelThreads];
+  __shared__ uint32_t s_digit, s_above, s_count, s_fill;
+  const int tid = threadIdx.x;
+  const float* row = logits + static_cast<int64_t>(blockIdx.x) * ld;
+
+  // Digits of the key from the most significant end; `prefix` holds the
+  // chosen digits (pbits of them), `need` how many keys below the elements
+  // already known to be above still have to be taken.
+  uint64_t prefix = 0;
+  int pbits = 0;
+  uint32_t need = static_cast<uint32_t>(K);
+  while (true) {
+    const int w = 64 - pbits < kDigitBits ? 64 - pbits : kDigitBits;
+    const int nb = 1 << w;
+    const int shift = 64 - pbits - w;
+    for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < V; i += kSelThreads) {
+      const uint64_t key = topk_key(row[i], i);
+      if (pbits == 0 || (key >> (64 - pbits)) == prefix)
+        atomicAdd(&hist[static_cast<uint32_t>(key >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    // Counts of the bins above each thread's contiguous range of bins.
+    const int per = (nb + kSelThreads - 1) / kSelThreads;
+    const int b0 = tid * per;
+    const int b1 = b0 + per < nb ? b0 + per : nb;
+    uint32_t mine = 0;
+    for (int b = b0; b < b1; ++b) mine += hist[b];
+    above_of[tid] = mine;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      for (int t = kSelThreads - 1; t >= 0; --t) {
+        const uint32_t v = above_of[t];
+        above_of[t] = acc;
+        acc += v;
+      }
+    }
+    __syncthreads();
+    uint32_t above = above_of[tid];
+    if (above < need && above + mine >= need) {
+      for (int b = b1 - 1; b >= b0; --b) {
+        const uint32_t c = hist[b];
+        if (above + c >= need) {
+          s_digit = static_cast<uint32_t>(b);
+          s_above = above;
+          s_count = c;
+          break;
+        }
+        above += c;
+      }
+    }
+    __syncthreads();
+    need -= s_above;
+    prefix = (prefix << w) | s_digit;
+    pbits += w;
+    const uint32_t in_bin = s_count;
+    __syncthreads();  // every thread has read s_*
+    // The whole bin is taken; keys are distinct, so this holds at the latest
+    // once all 64 bits are fixed.
+    if (in_bin == need || pbits >= 64) break;
+  }
+
+  // Exactly K keys have their top pbits >= prefix.
+  if (tid == 0) s_fill = 0;
+  for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kSelThreads) {
+    const uint64_t key = topk_key(row[i], i);
+    if ((key >> (64 - pbits)) >= prefix) {
+      const uint32_t slot = atomicAdd(&s_fill, 1u);
+      if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+    }
+  }
+  __syncthreads();
+  // Bitonic sort of Kp keys, descending.
+  for (int size = 2; size <= Kp; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < Kp; i += kSelThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t a = keys[i];
+          const uint64_t b = keys[j];
+          const bool desc = (i & size) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            keys[i] = b;
+            keys[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t out = (r0 + blockIdx.x) * static_cast<int64_t>(K);
+  for (int k = tid; k < K; k += kSelThreads) {
+    const uint64_t key = keys[k];
+    t_logit[out + k] = from_ordered_bits(static_cast<uint32_t>(key >> 32));
+    t_idx[out + k] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+  }
+}
+
+hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx, float* t_logit,
+                       char* ws, hipStream_t st) {
+  float* z = reinterpret_cast<float*>(ws);
+  int Kp = 1;
+  while (Kp < p.K) Kp <<= 1;
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
+    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+    GemmAccParams g;
+    g.A = Operand{h + c0 * p.d, p.d, rows, p.d};
+    g.B = Operand{W, p.d, p.V, p.d};
+    g.nk = static_cast<int32_t>(ceil_div(p.d, kStageK));
+    g.C = z;
+    g.ldc = p.ld;
+    g.m_lim = rows;
+    g.n_lim = p.V;
+    g.beta = 0;
+    g.mblocks = static_cast<int32_t>(ceil_div(rows, kTile));
+    g.nblocks = static_cast<int32_t>(ceil_div(p.V, kTile));
+    g.splits = 1;
+    g.kper = g.nk;
+    g.c_split = 0;
+    {
+      TraceScope ts(st, "topk_logits", 2.0 * rows * static_cast<double>(p.V) * p.d,
+                    2.0 * rows * p.d + 2.0 * p.V * p.d + 4.0 * rows * p.V);
+      hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g);
+    }
+    {
+      TraceScope ts(st, "topk_select", 0.0, 3.0 * 4.0 * rows * p.V + 8.0 * rows * p.K);
+      hipLaunchKernelGGL(k_topk_select, dim3(rows), dim3(kSelThreads), 0, st, z, p.ld, static_cast<int>(p.V),
+                         p.K, Kp, c0, t_idx, t_logit);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fkl

@@ -126,3 +126,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("FKL_LIBRARY", str(tmp_path / "missing.so"))
     with pytest.raises(fkl.FklError):
         fkl.lib()
+
+
+def test_topk_argument_errors_before_any_device_work():
+    L = fkl.lib()
+    vp = ctypes.c_void_p
+
+    def call(N=16, d=64, V=100, K=5, chunk=0, h=8192, W=16384, ti=4096, tl=4096, ws=1 << 20, ws_bytes=1 << 30):
+        s = fkl.TopkShape(N, d, V, K, chunk)
+        return L.fkl_topk(ctypes.byref(s), vp(h), vp(W), vp(ti), vp(tl), vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
+    assert call(d=12) == 1
+    assert call(K=0) == 1
+    assert call(K=101) == 1       # K > V
+    assert call(K=2000, V=5000) == 5
+    assert call(chunk=-1) == 1
+    assert call(h=0) == 1
+    assert call(W=8) == 1         # misaligned
+    assert call(ti=2) == 1
+    assert call(ws=0) == 2
+    assert call(ws_bytes=16) == 2
+    assert call(N=0, h=0, W=0, ti=0, tl=0, ws=0) == 0   # nothing to do
+
+
+def test_topk_workspace_is_one_logits_block():
+    b = fkl.topk_workspace_size(16384, 4096, 128256, 100)
+    assert b <= 512 << 20 and b >= 256 * 128256 * 4
+    assert fkl.topk_workspace_size(16384, 4096, 128256, 100, chunk=256) == 256 * 128256 * 4
+    assert fkl.topk_workspace_size(1000, 64, 1000, 10, chunk=300) == 512 * 1024 * 4

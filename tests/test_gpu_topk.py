@@ -1,0 +1,135 @@
+"""GPU parity of the teacher-cache builder (fkl_topk) against the oracle's
+top-K (numpy fp64 logits, order: value descending, lower index first).
+
+The GPU forms the logits from the same bf16 values with fp32 accumulation,
+so its values differ from the fp64 ones by rounding. Accepted:
+  * values at the returned indices within VAL_TOL (relative to the row's
+    largest logit) of the exact fp64 logits;
+  * returned index sets equal to the oracle's except for near-ties: every
+    index in the symmetric difference has an exact logit within VAL_TOL of
+    the oracle's K-th value;
+  * the returned order is value-descending with ties by the lower index.
+With integer-valued inputs every logit is exact in fp32, and the output must
+equal the oracle's exactly, tie-breaks included.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import output_projection_kl_amd as fkl
+from workloads import bf16_to_f32, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+VAL_TOL = 2e-6
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _to_dev_bf16(x_f32, dev):
+    bits = bf16_bits(np.asarray(x_f32, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16), bf16_to_f32(bits)
+
+
+def _check(gi, gv, hf, Wf, K, exact=False):
+    ri, rv = oracle.topk_teacher(hf, Wf, K)
+    z_all = hf.astype(np.float64) @ Wf.astype(np.float64).T
+    N = hf.shape[0]
+    if exact:
+        np.testing.assert_array_equal(gi, ri)
+        np.testing.assert_array_equal(gv.astype(np.float64), rv)
+        return
+    scale = np.abs(z_all).max(axis=1, keepdims=True)
+    zg = np.take_along_axis(z_all, gi.astype(np.int64), axis=1)
+    assert np.all(np.abs(gv - zg) <= VAL_TOL * scale), float(np.abs(gv - zg).max())
+    for r in range(N):
+        a, b = set(gi[r].tolist()), set(ri[r].tolist())
+        diff = a ^ b
+        if diff:
+            kth = rv[r, -1]
+            assert all(abs(z_all[r, v] - kth) <= VAL_TOL * scale[r, 0] for v in diff), (r, sorted(diff))
+        assert len(a) == K
+    # returned order: descending values, equal values by lower index
+    assert np.all(np.diff(gv, axis=1) <= 0)
+    eq = np.diff(gv, axis=1) == 0
+    assert np.all(np.diff(gi, axis=1)[eq] > 0)
+
+
+@pytest.mark.parametrize("N,d,V,K,chunk", [
+    (300, 136, 5000, 7, 128),      # ragged rows, columns, several chunks
+    (257, 64, 4096, 100, 0),       # default chunk
+    (64, 256, 777, 1, 32),         # K = 1
+    (40, 64, 1500, 1024, 0),       # largest K
+    (33, 32, 300, 300, 16),        # K = V: the whole row sorted
+])
+def test_topk_random_logits(N, d, V, K, chunk):
+    dev = _dev()
+    rng = np.random.default_rng(N * 7 + V)
+    h, hf = _to_dev_bf16(rng.standard_normal((N, d)), dev)
+    W, Wf = _to_dev_bf16(rng.standard_normal((V, d)) / np.sqrt(d), dev)
+    print(f"[topk] N={N} d={d} V={V} K={K} chunk={chunk}", flush=True)
+    ti, tl = fkl.topk(h, W, K, chunk=chunk)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K)
+
+
+@pytest.mark.parametrize("K", [5, 50, 129])
+def test_topk_integer_logits_exact_with_ties(K):
+    """Small integers: every logit is exact, ties are everywhere, the K-th place
+    falls inside tie groups; the result must match the oracle bit for bit."""
+    dev = _dev()
+    rng = np.random.default_rng(1000 + K)
+    N, d, V = 70, 64, 3000
+    h, hf = _to_dev_bf16(rng.integers(-2, 3, size=(N, d)).astype(np.float32), dev)
+    W, Wf = _to_dev_bf16(rng.integers(-2, 3, size=(V, d)).astype(np.float32), dev)
+    print(f"[topk-exact] N={N} d={d} V={V} K={K}", flush=True)
+    ti, tl = fkl.topk(h, W, K, chunk=32)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
+
+
+def test_topk_all_equal_logits():
+    """W = 0: every logit is 0; the K lowest indices in order."""
+    dev = _dev()
+    h = torch.ones((9, 16), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((500, 16), dtype=torch.bfloat16, device=dev)
+    ti, tl = fkl.topk(h, W, 37)
+    torch.cuda.synchronize()
+    assert (ti.cpu().numpy() == np.arange(37)[None, :]).all()
+    assert (tl.cpu().numpy() == 0).all()
+
+
+def test_topk_feeds_the_loss():
+    """The builder's output is a valid teacher cache for fkl_forward."""
+    dev = _dev()
+    rng = np.random.default_rng(5)
+    h, _ = _to_dev_bf16(rng.standard_normal((128, 64)), dev)
+    W, _ = _to_dev_bf16(rng.standard_normal((2000, 64)) / 8.0, dev)
+    ti, tl = fkl.topk(h, W, 20)
+    assert fkl.validate_teacher(ti, tl, 2000) == 0
+    loss, _ = fkl.forward(h, W, ti, tl, T=1.0)
+    torch.cuda.synchronize()
+    assert np.isfinite(loss.item()) and loss.item() >= -1e-5
+
+
+def test_topk_fullsize_sampled_rows():
+    """The large-head workload's shape (N=16384, d=4096, V=128256, K=100) with a
+    perturbed teacher head: sampled rows against the oracle."""
+    from workloads.device import make_device_workload, perturbed_head
+    dev = _dev()
+    wl = make_device_workload("temp", dev, N=16384)
+    Wt = perturbed_head(wl.W, 4242, dev)
+    print(f"[topk-fullsize] N={wl.N} d={wl.d} V={wl.V} K=100", flush=True)
+    ti, tl = fkl.topk(wl.h, Wt, 100)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 1023, 1024, wl.N - 1], rng.choice(wl.N, 27, replace=False)]))
+    hf = wl.h[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    Wf = Wt.float().cpu().numpy()
+    _check(ti.cpu().numpy()[rows], tl.cpu().numpy()[rows], hf, Wf, 100)

@@ -356,6 +356,38 @@ def test_sampled_grad_W_rows_match_autograd(T, mask_frac):
     np.testing.assert_allclose(got3, gW[rows], rtol=1e-12, atol=1e-16)
 
 
+# ---------------------------------------------------------------------------
+# Teacher-cache builder: top-K of the teacher's logits
+# ---------------------------------------------------------------------------
+
+def test_topk_teacher_matches_torch_topk():
+    """Continuous random logits (no ties): same index sets, values and order as
+    torch.topk in fp64."""
+    rng = np.random.default_rng(141)
+    h = rng.standard_normal((7, 12))
+    W = rng.standard_normal((300, 12))
+    idx, val = oracle.topk_teacher(h, W, 17)
+    tv, ti = torch.topk(torch.tensor(h @ W.T), 17, dim=1, largest=True, sorted=True)
+    np.testing.assert_array_equal(idx, ti.numpy())
+    np.testing.assert_allclose(val, tv.numpy(), rtol=1e-15)
+
+
+def test_topk_teacher_brute_force_with_ties():
+    """Integer logits with many ties against a plain sorted() of (-value, index)."""
+    rng = np.random.default_rng(142)
+    h = rng.integers(-2, 3, size=(5, 4)).astype(np.float64)
+    W = rng.integers(-2, 3, size=(40, 4)).astype(np.float64)
+    K = 11
+    idx, val = oracle.topk_teacher(h, W, K)
+    for r in range(5):
+        z = [float(sum(h[r, j] * W[v, j] for j in range(4))) for v in range(40)]
+        want = sorted(range(40), key=lambda v: (-z[v], v))[:K]
+        assert list(idx[r]) == want
+        assert list(val[r]) == [z[v] for v in want]
+    with pytest.raises(ValueError):
+        oracle.topk_teacher(h, W, 41)
+
+
 def test_oracle_rejects_bad_teacher():
     h, W, t_idx, t_logit, _ = _rand_problem(121)
     bad = t_idx.copy()

@@ -44,14 +44,8 @@ def _seed_of(ss: np.random.SeedSequence) -> int:
     return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
 
 
-def perturbed_head_teacher(h, W, K: int, seed: int, device, rows_per_pass: int = 1024):
-    """Teacher cache from a perturbed copy of the student head.
-
-    W_t = bf16(float32(W) + 0.1 * N(0, 1/d)); the teacher keeps the exact
-    top-K of its fp32 logits h W_t^T per row (values descending), computed in
-    float32 on the device without TF32, in passes of rows_per_pass rows.
-    Input generation only: the same arrays feed the library and the oracle.
-    """
+def perturbed_head(W, seed: int, device):
+    """W_t = bf16(float32(W) + 0.1 * N(0, 1/d)), noise from torch's seeded device generator."""
     import torch
 
     d = W.shape[1]
@@ -63,6 +57,20 @@ def perturbed_head_teacher(h, W, K: int, seed: int, device, rows_per_pass: int =
         v1 = min(W.shape[0], v0 + block)
         noise = torch.randn((v1 - v0, d), generator=g, device=device, dtype=torch.float32)
         Wt[v0:v1] = W[v0:v1].float() + noise * float(0.1 / np.sqrt(d))
+    return Wt
+
+
+def perturbed_head_teacher(h, W, K: int, seed: int, device, rows_per_pass: int = 1024):
+    """Teacher cache from a perturbed copy of the student head.
+
+    W_t = bf16(float32(W) + 0.1 * N(0, 1/d)); the teacher keeps the exact
+    top-K of its fp32 logits h W_t^T per row (values descending), computed in
+    float32 on the device without TF32, in passes of rows_per_pass rows.
+    Input generation only: the same arrays feed the library and the oracle.
+    """
+    import torch
+
+    Wt = perturbed_head(W, seed, device)
     Wt32 = Wt.float()
     del Wt
     prev = torch.backends.cuda.matmul.allow_tf32
