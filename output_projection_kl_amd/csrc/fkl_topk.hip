@@ -15,7 +15,10 @@
 // | (0xFFFFFFFF - index), so larger keys are larger logits and, for equal
 // logits, lower indices. The selection walks 12-bit digits of the key from the
 // top, keeping only the elements that share the digits chosen so far, until
-// the digit bin at the K-th key is taken whole.
+// the digit bin at the K-th key is taken whole. After the first digit the
+// row is read once more: keys above the boundary bin are taken, and the
+// boundary bin is copied to LDS where the remaining digits are resolved (or,
+// if it does not fit, resolved by further passes over the row).
 #include <climits>
 
 #include "fkl_device.h"
@@ -47,6 +50,79 @@ constexpr int kSelThreads = 256;
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kMaxK = 1024;
+constexpr int kCand = 2048;  // LDS candidates of the boundary bin
+
+struct SelectState {
+  uint64_t prefix;  // chosen digits, most significant first
+  int pbits;        // number of chosen bits
+  uint32_t need;    // keys still to take among those matching prefix
+};
+
+// One digit of the selection over n keys given by key_at(i): histogram of the
+// next digit among keys matching the prefix, then the digit holding the
+// need-th largest key. Returns the number of keys in that digit's bin.
+template <class KeyAt>
+__device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* above_of,
+                                 uint32_t* s_vals) {
+  const int tid = threadIdx.x;
+  const int w = 64 - st.pbits < kDigitBits ? 64 - st.pbits : kDigitBits;
+  const int nb = 1 << w;
+  const int shift = 64 - st.pbits - w;
+  for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kSelThreads) {
+    const uint64_t key = key_at(i);
+    if (st.pbits == 0 || (key >> (64 - st.pbits)) == st.prefix)
+      atomicAdd(&hist[static_cast<uint32_t>(key >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  const int per = (nb + kSelThreads - 1) / kSelThreads;
+  const int b0 = tid * per;
+  const int b1 = b0 + per < nb ? b0 + per : nb;
+  uint32_t mine = 0;
+  for (int b = b0; b < b1; ++b) mine += hist[b];
+  above_of[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    for (int t = kSelThreads - 1; t >= 0; --t) {
+      const uint32_t v = above_of[t];
+      above_of[t] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  uint32_t above = above_of[tid];
+  if (above < st.need && above + mine >= st.need) {
+    for (int b = b1 - 1; b >= b0; --b) {
+      const uint32_t c = hist[b];
+      if (above + c >= st.need) {
+        s_vals[0] = static_cast<uint32_t>(b);
+        s_vals[1] = above;
+        s_vals[2] = c;
+        break;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+  st.need -= s_vals[1];
+  st.prefix = (st.prefix << w) | s_vals[0];
+  st.pbits += w;
+  const uint32_t in_bin = s_vals[2];
+  __syncthreads();  // every thread has read s_vals
+  return in_bin;
+}
+
+// Digits until the bin at the K-th key is taken whole (at the latest when all
+// 64 bits are fixed: keys are distinct).
+template <class KeyAt>
+__device__ void select_rest(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* above_of,
+                            uint32_t* s_vals) {
+  while (st.pbits < 64) {
+    if (select_digit(key_at, n, st, hist, above_of, s_vals) == st.need) break;
+  }
+}
 
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __restrict__ logits, int64_t ld,
                                                              int V, int K, int Kp, int64_t r0,
@@ -54,79 +130,60 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
                                                              float* __restrict__ t_logit) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t keys[kMaxK];
+  __shared__ uint64_t cand[kCand];
   __shared__ uint32_t above_of[kSelThreads];
-  __shared__ uint32_t s_digit, s_above, s_count, s_fill;
+  __shared__ uint32_t s_vals[3];
+  __shared__ uint32_t s_fill, s_cand;
   const int tid = threadIdx.x;
   const float* row = logits + static_cast<int64_t>(blockIdx.x) * ld;
+  auto row_key = [row](int i) { return topk_key(row[i], i); };
 
-  // Digits of the key from the most significant end; `prefix` holds the
-  // chosen digits (pbits of them), `need` how many keys below the elements
-  // already known to be above still have to be taken.
-  uint64_t prefix = 0;
-  int pbits = 0;
-  uint32_t need = static_cast<uint32_t>(K);
-  while (true) {
-    const int w = 64 - pbits < kDigitBits ? 64 - pbits : kDigitBits;
-    const int nb = 1 << w;
-    const int shift = 64 - pbits - w;
-    for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
-    __syncthreads();
-    for (int i = tid; i < V; i += kSelThreads) {
-      const uint64_t key = topk_key(row[i], i);
-      if (pbits == 0 || (key >> (64 - pbits)) == prefix)
-        atomicAdd(&hist[static_cast<uint32_t>(key >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    // Counts of the bins above each thread's contiguous range of bins.
-    const int per = (nb + kSelThreads - 1) / kSelThreads;
-    const int b0 = tid * per;
-    const int b1 = b0 + per < nb ? b0 + per : nb;
-    uint32_t mine = 0;
-    for (int b = b0; b < b1; ++b) mine += hist[b];
-    above_of[tid] = mine;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t acc = 0;
-      for (int t = kSelThreads - 1; t >= 0; --t) {
-        const uint32_t v = above_of[t];
-        above_of[t] = acc;
-        acc += v;
-      }
-    }
-    __syncthreads();
-    uint32_t above = above_of[tid];
-    if (above < need && above + mine >= need) {
-      for (int b = b1 - 1; b >= b0; --b) {
-        const uint32_t c = hist[b];
-        if (above + c >= need) {
-          s_digit = static_cast<uint32_t>(b);
-          s_above = above;
-          s_count = c;
-          break;
-        }
-        above += c;
-      }
-    }
-    __syncthreads();
-    need -= s_above;
-    prefix = (prefix << w) | s_digit;
-    pbits += w;
-    const uint32_t in_bin = s_count;
-    __syncthreads();  // every thread has read s_*
-    // The whole bin is taken; keys are distinct, so this holds at the latest
-    // once all 64 bits are fixed.
-    if (in_bin == need || pbits >= 64) break;
-  }
-
-  // Exactly K keys have their top pbits >= prefix.
-  if (tid == 0) s_fill = 0;
   for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
-  __syncthreads();
+  if (tid == 0) {
+    s_fill = 0;
+    s_cand = 0;
+  }
+  SelectState st{0, 0, static_cast<uint32_t>(K)};
+  const uint32_t in_bin = select_digit(row_key, V, st, hist, above_of, s_vals);
+  // Pass 2 over the row: keys above the boundary bin are taken now; the
+  // boundary bin goes to LDS (or everything of the bin when it is taken whole).
+  const uint64_t d0 = st.prefix;
+  const bool whole = in_bin == st.need;
   for (int i = tid; i < V; i += kSelThreads) {
-    const uint64_t key = topk_key(row[i], i);
-    if ((key >> (64 - pbits)) >= prefix) {
+    const uint64_t key = row_key(i);
+    const uint64_t top = key >> (64 - kDigitBits);
+    if (top > d0 || (whole && top == d0)) {
       const uint32_t slot = atomicAdd(&s_fill, 1u);
       if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+    } else if (top == d0) {
+      const uint32_t c = atomicAdd(&s_cand, 1u);
+      if (c < static_cast<uint32_t>(kCand)) cand[c] = key;
+    }
+  }
+  __syncthreads();
+  if (!whole) {
+    const uint32_t nc = s_cand;
+    if (nc <= static_cast<uint32_t>(kCand)) {
+      const uint64_t* cp = cand;
+      auto cand_key = [cp](int i) { return cp[i]; };
+      select_rest(cand_key, static_cast<int>(nc), st, hist, above_of, s_vals);
+      for (uint32_t i = tid; i < nc; i += kSelThreads) {
+        const uint64_t key = cand[i];
+        if ((key >> (64 - st.pbits)) >= st.prefix) {
+          const uint32_t slot = atomicAdd(&s_fill, 1u);
+          if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+        }
+      }
+    } else {
+      // Boundary bin too large for LDS: finish over the row itself.
+      select_rest(row_key, V, st, hist, above_of, s_vals);
+      for (int i = tid; i < V; i += kSelThreads) {
+        const uint64_t key = row_key(i);
+        if ((key >> (64 - kDigitBits)) == d0 && (key >> (64 - st.pbits)) >= st.prefix) {
+          const uint32_t slot = atomicAdd(&s_fill, 1u);
+          if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+        }
+      }
     }
   }
   __syncthreads();
@@ -183,7 +240,7 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
       hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g);
     }
     {
-      TraceScope ts(st, "topk_select", 0.0, 3.0 * 4.0 * rows * p.V + 8.0 * rows * p.K);
+      TraceScope ts(st, "topk_select", 0.0, 2.0 * 4.0 * rows * p.V + 8.0 * rows * p.K);
       hipLaunchKernelGGL(k_topk_select, dim3(rows), dim3(kSelThreads), 0, st, z, p.ld, static_cast<int>(p.V),
                          p.K, Kp, c0, t_idx, t_logit);
     }

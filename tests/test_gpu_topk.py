@@ -94,15 +94,30 @@ def test_topk_integer_logits_exact_with_ties(K):
     _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
 
 
-def test_topk_all_equal_logits():
-    """W = 0: every logit is 0; the K lowest indices in order."""
+@pytest.mark.parametrize("V", [500, 5000])
+def test_topk_all_equal_logits(V):
+    """W = 0: every logit is 0; the K lowest indices in order (V = 5000 puts more
+    equal keys in one first-digit bin than the LDS candidate buffer holds)."""
     dev = _dev()
     h = torch.ones((9, 16), dtype=torch.bfloat16, device=dev)
-    W = torch.zeros((500, 16), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((V, 16), dtype=torch.bfloat16, device=dev)
     ti, tl = fkl.topk(h, W, 37)
     torch.cuda.synchronize()
     assert (ti.cpu().numpy() == np.arange(37)[None, :]).all()
     assert (tl.cpu().numpy() == 0).all()
+
+
+def test_topk_integer_logits_exact_large_boundary_bin():
+    """Few distinct integer logits over a wide vocabulary: the boundary bin holds
+    thousands of keys, so selection continues over the row; still exact."""
+    dev = _dev()
+    rng = np.random.default_rng(77)
+    N, d, V, K = 24, 16, 30000, 300
+    h, hf = _to_dev_bf16(rng.integers(-1, 2, size=(N, d)).astype(np.float32), dev)
+    W, Wf = _to_dev_bf16(rng.integers(-1, 2, size=(V, d)).astype(np.float32), dev)
+    ti, tl = fkl.topk(h, W, K)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
 
 
 def test_topk_feeds_the_loss():
