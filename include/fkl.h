@@ -71,7 +71,30 @@ typedef struct {
                     a pass's gradient block holds about 64 Mi elements.
                     Rounded up to a multiple of 256. Results do not depend
                     on it beyond fp32 summation order of grad_h. */
+  uint32_t flags; /* backward options, FKL_* below (0 = defaults); ignored by
+                     fkl_forward */
 } fkl_shape;
+
+/*
+ * Backward options, for use inside a training step (the loss is meant as a
+ * drop-in replacement for the KL term of a distillation loop: page "Making
+ * knowledge distillation cheap enough to run in production").
+ *   FKL_ACCUMULATE_GRAD_W  grad_W += this call's gradient (micro-batch
+ *                          accumulation) instead of grad_W = ...
+ *   FKL_ACCUMULATE_GRAD_H  grad_h += this call's gradient
+ *   FKL_SKIP_GRAD_W        grad_W is not computed (frozen head); may be NULL
+ *   FKL_SKIP_GRAD_H        grad_h is not computed; may be NULL
+ *   FKL_GRAD_H_BF16        grad_h is bf16 [N, d]: accumulated in fp32 in the
+ *                          workspace over the vocabulary and rounded once
+ *                          (round to nearest even); with FKL_ACCUMULATE_GRAD_H
+ *                          the old bf16 value is added in fp32 first
+ */
+#define FKL_ACCUMULATE_GRAD_W 0x1u
+#define FKL_ACCUMULATE_GRAD_H 0x2u
+#define FKL_SKIP_GRAD_W 0x4u
+#define FKL_SKIP_GRAD_H 0x8u
+#define FKL_GRAD_H_BF16 0x10u
+#define FKL_FLAGS_ALL 0x1fu
 
 /*
  * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
@@ -95,13 +118,15 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
 /*
  * Backward pass with recomputation of the logits. row_lse is the forward's
  * output for the same inputs. grad_loss is a device fp32 [1] holding g, or
- * NULL for g = 1. grad_h (fp32 [N, d]) and grad_W (fp32 [V, d]) are
- * overwritten. Masked rows get exactly zero grad_h rows.
+ * NULL for g = 1. grad_h (fp32 [N, d], or bf16 with FKL_GRAD_H_BF16) and
+ * grad_W (fp32 [V, d]) are overwritten, or accumulated into, as shape->flags
+ * says. Masked rows get exactly zero grad_h rows (unchanged rows when
+ * accumulating).
  */
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
                         const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
                         const float* row_lse, const float* grad_loss,
-                        float* grad_h, float* grad_W,
+                        void* grad_h, float* grad_W,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -27,6 +27,12 @@ __all__ = [
     "forward",
     "backward",
     "validate_teacher",
+    "FusedKLLoss",
+    "ACCUMULATE_GRAD_W",
+    "ACCUMULATE_GRAD_H",
+    "SKIP_GRAD_W",
+    "SKIP_GRAD_H",
+    "GRAD_H_BF16",
     "TopkShape",
     "topk_workspace_size",
     "topk",
@@ -85,6 +91,7 @@ class Shape(ctypes.Structure):
         ("T", ctypes.c_float),
         ("chunk", ctypes.c_int32),
         ("vslab", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -142,14 +149,22 @@ def _check(status: int) -> None:
         raise FklError(status, f"{L.fkl_status_string(status).decode()}: {L.fkl_last_error().decode()}")
 
 
-def make_shape(N, d, V, K, T=1.0, chunk=0, vslab=0) -> Shape:
-    return Shape(int(N), int(d), int(V), int(K), float(T), int(chunk), int(vslab))
+# Backward options (fkl_shape.flags; see include/fkl.h).
+ACCUMULATE_GRAD_W = 0x1
+ACCUMULATE_GRAD_H = 0x2
+SKIP_GRAD_W = 0x4
+SKIP_GRAD_H = 0x8
+GRAD_H_BF16 = 0x10
 
 
-def workspace_size(N, d, V, K, T=1.0, chunk=0, vslab=0):
+def make_shape(N, d, V, K, T=1.0, chunk=0, vslab=0, flags=0) -> Shape:
+    return Shape(int(N), int(d), int(V), int(K), float(T), int(chunk), int(vslab), int(flags))
+
+
+def workspace_size(N, d, V, K, T=1.0, chunk=0, vslab=0, flags=0):
     """(forward_bytes, backward_bytes) of workspace for this shape."""
     f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
-    s = make_shape(N, d, V, K, T, chunk, vslab)
+    s = make_shape(N, d, V, K, T, chunk, vslab, flags)
     _check(lib().fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)))
     return f.value, b.value
 
@@ -235,21 +250,39 @@ def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vsl
 
 
 def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss=None, chunk: int = 0,
-             vslab: int = 0, workspace=None, grad_h=None, grad_W=None):
-    """Fused backward with recomputation. Returns (grad_h fp32 [N, d], grad_W fp32 [V, d])."""
+             vslab: int = 0, workspace=None, grad_h=None, grad_W=None, need_grad_h: bool = True,
+             need_grad_W: bool = True, accumulate_grad_h: bool = False, accumulate_grad_W: bool = False,
+             grad_h_dtype=None):
+    """Fused backward with recomputation. Returns (grad_h [N, d], grad_W fp32 [V, d]); a
+    gradient that is not needed comes back as None. grad_h is fp32, or bf16 when
+    grad_h_dtype is torch.bfloat16 (or a bf16 grad_h is passed). With accumulate_*,
+    the passed tensor is added to instead of overwritten."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
     _need(row_lse, "row_lse", torch.float32, (N,))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, (1,))
-    s = make_shape(N, d, V, K, T, chunk, vslab)
-    _, bb = workspace_size(N, d, V, K, T, chunk, vslab)
+    if grad_h_dtype is None:
+        grad_h_dtype = grad_h.dtype if grad_h is not None else torch.float32
+    if grad_h_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("grad_h must be float32 or bfloat16")
+    flags = ((0 if need_grad_h else SKIP_GRAD_H) | (0 if need_grad_W else SKIP_GRAD_W) |
+             (ACCUMULATE_GRAD_H if accumulate_grad_h else 0) | (ACCUMULATE_GRAD_W if accumulate_grad_W else 0) |
+             (GRAD_H_BF16 if grad_h_dtype == torch.bfloat16 else 0))
+    if (accumulate_grad_h and need_grad_h and grad_h is None) or (accumulate_grad_W and need_grad_W and grad_W is None):
+        raise ValueError("accumulating needs the tensor to accumulate into")
+    s = make_shape(N, d, V, K, T, chunk, vslab, flags)
+    _, bb = workspace_size(N, d, V, K, T, chunk, vslab, flags)
     ws = _workspace(bb, h.device, workspace)
-    if grad_h is None:
-        grad_h = torch.empty((N, d), dtype=torch.float32, device=h.device)
+    if not need_grad_h:
+        grad_h = None
+    elif grad_h is None:
+        grad_h = torch.empty((N, d), dtype=grad_h_dtype, device=h.device)
     else:
-        _need(grad_h, "grad_h", torch.float32, (N, d))
-    if grad_W is None:
+        _need(grad_h, "grad_h", grad_h_dtype, (N, d))
+    if not need_grad_W:
+        grad_W = None
+    elif grad_W is None:
         grad_W = torch.empty((V, d), dtype=torch.float32, device=h.device)
     else:
         _need(grad_W, "grad_W", torch.float32, (V, d))
@@ -257,6 +290,44 @@ def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss
                               _ptr(row_lse), _ptr(grad_loss), _ptr(grad_h), _ptr(grad_W), _ptr(ws),
                               ctypes.c_size_t(ws.numel()), _stream()))
     return grad_h, grad_W
+
+
+class FusedKLLoss:
+    """Autograd entry: ``FusedKLLoss.apply(h, W, t_idx, t_logit, T=1.0, mask=None, chunk=0)``
+    returns the scalar loss; its backward runs fkl_backward, reading the upstream
+    gradient on the device (no host synchronisation), returns grad_h in h's dtype
+    and grad_W in fp32 (autograd casts it to W's dtype), and skips whichever of
+    the two is not required."""
+
+    _fn = None
+
+    @classmethod
+    def apply(cls, h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0):
+        if cls._fn is None:
+            torch = _torch()
+
+            class _Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, h, W, t_idx, t_logit, T, mask, chunk):
+                    loss, lse = forward(h, W, t_idx, t_logit, T=T, mask=mask, chunk=chunk)
+                    ctx.save_for_backward(h, W, t_idx, t_logit, lse, mask)
+                    ctx.T, ctx.chunk = T, chunk
+                    return loss.reshape(())
+
+                @staticmethod
+                def backward(ctx, g):
+                    h, W, t_idx, t_logit, lse, mask = ctx.saved_tensors
+                    need_h, need_W = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+                    if not (need_h or need_W):
+                        return (None,) * 7
+                    gl = g.detach().reshape(1).to(torch.float32).contiguous()
+                    gh, gW = backward(h, W, t_idx, t_logit, lse, T=ctx.T, mask=mask, grad_loss=gl,
+                                      chunk=ctx.chunk, need_grad_h=need_h, need_grad_W=need_W,
+                                      grad_h_dtype=h.dtype if h.dtype == torch.bfloat16 else torch.float32)
+                    return gh, gW, None, None, None, None, None
+
+            cls._fn = _Fn
+        return cls._fn.apply(h, W, t_idx, t_logit, T, mask, chunk)
 
 
 def validate_teacher(t_idx, t_logit, V: int) -> int:

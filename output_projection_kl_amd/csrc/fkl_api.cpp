@@ -39,6 +39,7 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   if (!(s->T > 0.0f) || !std::isfinite(s->T)) return fail(FKL_EINVAL, "T must be finite and > 0");
   if (s->chunk < 0) return fail(FKL_EINVAL, "chunk must be >= 0");
   if (s->vslab < 0) return fail(FKL_EINVAL, "vslab must be >= 0");
+  if (s->flags & ~FKL_FLAGS_ALL) return fail(FKL_EINVAL, "unknown bits in flags");
 
   p->N = s->N;
   p->d = s->d;
@@ -88,6 +89,10 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->ghp_rows = splits > 1 ? splits * p->chunk_alloc : 0;
   p->off_ghp = off;
   off = align256(off + static_cast<size_t>(p->ghp_rows) * s->d * 4);
+  p->flags = s->flags;
+  p->off_gh32 = off;
+  if ((s->flags & FKL_GRAD_H_BF16) && !(s->flags & FKL_SKIP_GRAD_H))
+    off = align256(off + static_cast<size_t>(p->chunk_alloc) * s->d * 4);
   p->bwd_bytes = off;
   return FKL_OK;
 }
@@ -164,25 +169,29 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
 
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
                         const float* t_logit, const uint8_t* row_mask, const float* row_lse,
-                        const float* grad_loss, float* grad_h, float* grad_W, void* workspace,
+                        const float* grad_loss, void* grad_h, float* grad_W, void* workspace,
                         size_t workspace_bytes, void* stream) {
   fkl::Plan p;
   fkl_status st = fkl::make_plan(shape, &p);
   if (st != FKL_OK) return st;
-  if (!grad_W) return fail(FKL_EINVAL, "grad_W is NULL");
-  if (!aligned(grad_W, 16)) return fail(FKL_EINVAL, "grad_W must be 16-byte aligned");
+  const bool want_w = !(p.flags & FKL_SKIP_GRAD_W);
+  const bool want_h = !(p.flags & FKL_SKIP_GRAD_H);
+  if (want_w && !grad_W) return fail(FKL_EINVAL, "grad_W is NULL");
+  if (want_w && !aligned(grad_W, 16)) return fail(FKL_EINVAL, "grad_W must be 16-byte aligned");
   if (grad_loss && !aligned(grad_loss, 4)) return fail(FKL_EINVAL, "grad_loss must be 4-byte aligned");
   if (p.N > 0) {
-    if (!h || !W || !t_idx || !t_logit || !row_lse || !grad_h)
-      return fail(FKL_EINVAL, "h, W, t_idx, t_logit, row_lse and grad_h must not be NULL");
+    if (!h || !W || !t_idx || !t_logit || !row_lse)
+      return fail(FKL_EINVAL, "h, W, t_idx, t_logit and row_lse must not be NULL");
+    if (want_h && !grad_h) return fail(FKL_EINVAL, "grad_h is NULL");
     if (!aligned(h, 16) || !aligned(W, 16)) return fail(FKL_EINVAL, "h and W must be 16-byte aligned");
-    if (!aligned(grad_h, 16)) return fail(FKL_EINVAL, "grad_h must be 16-byte aligned");
+    if (want_h && !aligned(grad_h, 16)) return fail(FKL_EINVAL, "grad_h must be 16-byte aligned");
     if (!aligned(t_idx, 4) || !aligned(t_logit, 4) || !aligned(row_lse, 4))
       return fail(FKL_EINVAL, "t_idx, t_logit and row_lse must be 4-byte aligned");
   }
   if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.bwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
+  if (!want_w && !want_h) return FKL_OK;  // nothing asked for
   fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_backward(p, a, static_cast<hipStream_t>(stream));

@@ -35,6 +35,8 @@ struct Plan {
   // (= splits x rows) rows of d fp32 each, reduced in a fixed order
   int64_t ghp_rows;
   size_t off_ghp;
+  uint32_t flags;  // FKL_* backward options
+  size_t off_gh32;  // fp32 [chunk_alloc][d] grad_h accumulator when grad_h is bf16
 };
 
 constexpr int kMaxGradHSplits = 8;
@@ -67,7 +69,7 @@ struct BwdArgs {
   const uint8_t* mask;
   const float* row_lse;
   const float* grad_loss;
-  float* grad_h;
+  void* grad_h;  // fp32, or bf16 with FKL_GRAD_H_BF16
   float* grad_W;
   char* ws;
 };

@@ -530,6 +530,25 @@ __global__ __launch_bounds__(256) void k_reduce_grad_h(const f32x4* __restrict__
   }
 }
 
+// bf16 grad_h rows from the fp32 accumulator (round to nearest even), adding
+// the old bf16 values in fp32 first when accumulating.
+__global__ __launch_bounds__(256) void k_grad_h_to_bf16(const f32x4* __restrict__ src, int64_t n4,
+                                                        uint16_t* __restrict__ dst, int accumulate) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
+    f32x4 v = src[i];
+    bf16x4* o = reinterpret_cast<bf16x4*>(dst) + i;
+    if (accumulate) {
+      const bf16x4 old = *o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += static_cast<float>(old[e]);
+    }
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(v[e]);
+    *o = r;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Teacher-cache validation: one wave per row
 // ---------------------------------------------------------------------------
@@ -639,9 +658,19 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   const float invT = 1.0f / p.T;
   const float k2 = kLog2e / p.T;
 
+  const bool want_w = !(p.flags & FKL_SKIP_GRAD_W);
+  const bool want_h = !(p.flags & FKL_SKIP_GRAD_H);
+  const bool acc_w = (p.flags & FKL_ACCUMULATE_GRAD_W) != 0;
+  const bool acc_h = (p.flags & FKL_ACCUMULATE_GRAD_H) != 0;
+  const bool h_bf16 = (p.flags & FKL_GRAD_H_BF16) != 0;
+  // fp32 destination of grad_h while the slabs of a chunk are summed: the
+  // caller's grad_h, or the workspace accumulator when grad_h is bf16
+  float* gh32 = reinterpret_cast<float*>(a.ws + p.off_gh32);
+
+  if (!want_w && !want_h) return hipGetLastError();
   hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
   if (p.N == 0) {
-    hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, a.grad_W, p.V * p.d);
+    if (want_w && !acc_w) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, a.grad_W, p.V * p.d);
     return hipGetLastError();
   }
   const int64_t n_slabs = ceil_div(p.V, p.vslab);
@@ -673,7 +702,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       GradParams gp2;
       GemmAccParams& hp = gp2.gh;
       const int64_t rows_written = static_cast<int64_t>(rbs) * kTile;  // G^T columns this chunk wrote
-      int hsplits = grad_h_splits(rows, slab_w, p.d);
+      int hsplits = want_h ? grad_h_splits(rows, slab_w, p.d) : 1;
       if (hsplits > 1 && hsplits * rows_written > p.ghp_rows)
         hsplits = static_cast<int>(p.ghp_rows / rows_written);
       if (hsplits < 1) hsplits = 1;
@@ -692,8 +721,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
         hp.beta = 0;
         hp.c_split = rows_written * p.d;
       } else {
-        hp.C = a.grad_h + c0 * p.d;
-        hp.beta = s > 0;
+        hp.C = h_bf16 ? gh32 : static_cast<float*>(a.grad_h) + c0 * p.d;
+        hp.beta = s > 0 || (acc_h && !h_bf16);
         hp.c_split = 0;
       }
       GemmAccParams& wp = gp2.gw;
@@ -704,18 +733,20 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.ldc = p.d;
       wp.m_lim = slab_w;
       wp.n_lim = p.d;
-      wp.beta = chunk_index > 0;
+      wp.beta = chunk_index > 0 || acc_w;
       wp.mblocks = nvt;
       wp.nblocks = static_cast<int32_t>(ceil_div(p.d, kTile));
       wp.splits = 1;
       wp.kper = wp.nk;
       wp.c_split = 0;
-      gp2.h_tiles = hp.mblocks * hp.nblocks * hsplits;
-      gp2.w_tiles = wp.mblocks * wp.nblocks;
+      gp2.h_tiles = want_h ? hp.mblocks * hp.nblocks * hsplits : 0;
+      gp2.w_tiles = want_w ? wp.mblocks * wp.nblocks : 0;
       {
-        TraceScope ts(st, "bwd_grads", 4.0 * rows * slab_w * dd,
-                      4.0 * rows * slab_w + 2.0 * slab_w * dd + 2.0 * rows * dd +
-                          (hp.beta ? 8.0 : 4.0) * rows * dd + (wp.beta ? 8.0 : 4.0) * slab_w * dd);
+        const double hw = (want_h ? 1.0 : 0.0) + (want_w ? 1.0 : 0.0);
+        TraceScope ts(st, "bwd_grads", 2.0 * hw * rows * slab_w * dd,
+                      2.0 * rows * slab_w + 2.0 * slab_w * dd + 2.0 * rows * dd +
+                          (want_h ? (hp.beta ? 8.0 : 4.0) * rows * dd : 0.0) +
+                          (want_w ? (wp.beta ? 8.0 : 4.0) * slab_w * dd : 0.0));
         hipLaunchKernelGGL(k_bwd_grads, dim3(gp2.h_tiles + gp2.w_tiles), dim3(kBlockThreads), 0, st, gp2);
       }
       if (hsplits > 1) {
@@ -724,9 +755,18 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
         TraceScope ts(st, "grad_h_reduce", 0.0, 4.0 * rows * p.d * (hsplits + (s > 0 ? 2 : 1)));
         hipLaunchKernelGGL(k_reduce_grad_h, dim3(static_cast<unsigned>(rgrid)),
                            dim3(256), 0, st, reinterpret_cast<const f32x4*>(a.ws + p.off_ghp), hsplits,
-                           rows_written * p.d / 4, n4, reinterpret_cast<f32x4*>(a.grad_h + c0 * p.d),
-                           static_cast<int>(s > 0));
+                           rows_written * p.d / 4, n4,
+                           reinterpret_cast<f32x4*>(h_bf16 ? gh32 : static_cast<float*>(a.grad_h) + c0 * p.d),
+                           static_cast<int>(s > 0 || (acc_h && !h_bf16)));
       }
+    }
+    if (want_h && h_bf16) {
+      const int64_t n4 = static_cast<int64_t>(rows) * p.d / 4;
+      const int64_t cgrid = ceil_div(n4, 256) < 2048 ? ceil_div(n4, 256) : 2048;
+      TraceScope ts(st, "grad_h_to_bf16", 0.0, (acc_h ? 8.0 : 6.0) * rows * p.d);
+      hipLaunchKernelGGL(k_grad_h_to_bf16, dim3(static_cast<unsigned>(cgrid)), dim3(256), 0, st,
+                         reinterpret_cast<const f32x4*>(gh32), n4,
+                         static_cast<uint16_t*>(a.grad_h) + c0 * p.d, static_cast<int>(acc_h));
     }
   }
   return hipGetLastError();

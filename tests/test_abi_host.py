@@ -153,3 +153,27 @@ def test_topk_workspace_is_one_logits_block():
     assert b <= 512 << 20 and b >= 256 * 128256 * 4
     assert fkl.topk_workspace_size(16384, 4096, 128256, 100, chunk=256) == 256 * 128256 * 4
     assert fkl.topk_workspace_size(1000, 64, 1000, 10, chunk=300) == 512 * 1024 * 4
+
+
+def test_backward_flags_checked_on_the_host():
+    L = fkl.lib()
+    vp = ctypes.c_void_p
+
+    def bwd(flags, grad_h=8192, grad_W=16384, ws_bytes=1 << 30):
+        s = fkl.make_shape(16, 64, 100, 5, flags=flags)
+        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(256),
+                              vp(0), vp(grad_h), vp(grad_W), vp(1 << 20), ctypes.c_size_t(ws_bytes), vp(0))
+    assert bwd(0x40) == 1                                   # unknown bit
+    assert bwd(0, grad_W=0) == 1                            # grad_W needed
+    assert bwd(fkl.SKIP_GRAD_W, grad_W=0, ws_bytes=16) == 2  # NULL grad_W accepted when skipped
+    assert bwd(fkl.SKIP_GRAD_H, grad_h=0, ws_bytes=16) == 2  # NULL grad_h accepted when skipped
+    assert bwd(fkl.SKIP_GRAD_H | fkl.SKIP_GRAD_W, grad_h=0, grad_W=0) == 0  # nothing to do, no device work
+
+
+def test_bf16_grad_h_adds_an_fp32_accumulator_to_the_workspace():
+    _, b0 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096)
+    _, b1 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096, flags=fkl.GRAD_H_BF16)
+    assert b1 - b0 == 4096 * 2880 * 4
+    _, b2 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096,
+                               flags=fkl.GRAD_H_BF16 | fkl.SKIP_GRAD_H)
+    assert b2 == b0
