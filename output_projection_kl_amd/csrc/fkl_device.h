@@ -59,12 +59,13 @@ constexpr int kARows = 256;                                    // A operand exte
 constexpr int kAStageBytes = kARows * kStageK * 2;             // 16 KiB
 constexpr uint32_t kOob = 0x80000000u;                         // offset past every buffer
 
-// Block tile 256 x (WN * NBW * 32): 2 x WN waves, each 128 x NBW*32 of the
-// output. The B operand's LDS extent is the tile width rounded up to 128 or
-// 256 (a 192-wide tile keeps the 256 layout and masks the last quarter).
-template <int NBW, int WN = 2>
+// Block tile 256 x (WN * NBW * 32): (8 / MB) x WN waves, each MB*32 x NBW*32
+// of the output. The B operand's LDS extent is the tile width rounded up to
+// 128 or 256 (a narrower tile keeps that layout and masks the rest).
+template <int NBW, int WN = 2, int MB = 4>
 struct TileCfg {
-  static constexpr int kWaves = 2 * WN;
+  static constexpr int kWM = kARows / (MB * 32);
+  static constexpr int kWaves = kWM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kTileN = WN * NBW * 32;
   static constexpr int kBExtent = kTileN <= 128 ? 128 : 256;
@@ -224,18 +225,21 @@ __device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Fragments of one 16-deep contraction step for a wave: 4 of A (128 rows),
-// NBW of B (NBW * 32 columns).
-template <bool TA, bool TB, int NBW, int RB>
+// Fragments of one 16-deep contraction step for a wave: MB of A (MB * 32
+// rows), NBW of B (NBW * 32 columns).
+template <bool TA, bool TB, int NBW, int RB, int MB = 4>
 struct Frags {
-  bf16x8 a[4], b[NBW];
-  u32x2 ta[4][2], tb[NBW][2];
+  static constexpr int kX = MB > NBW ? MB : NBW;
+  bf16x8 a[MB], b[NBW];
+  u32x2 ta[MB][2], tb[NBW][2];
 
   __device__ __forceinline__ void issue(const char* ra, const char* rb, int wm, int wn, int kb, int lane) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      if constexpr (TA) frag_trans_issue<kARows>(ra, wm * 128 + x * 32, kb, lane, ta[x][0], ta[x][1]);
-      else a[x] = frag_plain(ra, wm * 128 + x * 32, kb, lane);
+    for (int x = 0; x < kX; ++x) {
+      if (x < MB) {
+        if constexpr (TA) frag_trans_issue<kARows>(ra, wm * MB * 32 + x * 32, kb, lane, ta[x][0], ta[x][1]);
+        else a[x] = frag_plain(ra, wm * MB * 32 + x * 32, kb, lane);
+      }
       if (x < NBW) {
         if constexpr (TB) frag_trans_issue<RB>(rb, wn * NBW * 32 + x * 32, kb, lane, tb[x][0], tb[x][1]);
         else b[x] = frag_plain(rb, wn * NBW * 32 + x * 32, kb, lane);
@@ -247,9 +251,17 @@ struct Frags {
   // these registers depend on the wait.
   __device__ __forceinline__ void settle() {
     if constexpr (TA) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
-                     "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
+      if constexpr (MB == 4) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
+                       "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
+      } else if constexpr (MB == 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]));
+      } else {
+        static_assert(MB == 1, "MB must be 1, 2 or 4");
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ta[0][0]), "+v"(ta[0][1]));
+      }
     }
     if constexpr (TB) {
       if constexpr (NBW == 4) {
@@ -266,25 +278,25 @@ struct Frags {
       }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      if constexpr (TA) a[x] = join_halves(ta[x][0], ta[x][1]);
+    for (int x = 0; x < kX; ++x) {
+      if constexpr (TA) if (x < MB) a[x] = join_halves(ta[x][0], ta[x][1]);
       if constexpr (TB) if (x < NBW) b[x] = join_halves(tb[x][0], tb[x][1]);
     }
   }
 
-  __device__ __forceinline__ void mma(f32x16 (&acc)[4][NBW]) const {
+  __device__ __forceinline__ void mma(f32x16 (&acc)[MB][NBW]) const {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
   }
 };
 
-template <int NB>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
+template <int MB, int NB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -292,8 +304,9 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
 }
 
 // acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+kTileN, 0 : 32*nk]^T over a
-// ring of TileCfg<NBW, WN>::kStages LDS stages (2 x WN waves, each 128 x
-// NBW*32 of the output; wave w sits at row block w / WN, column block w % WN).
+// ring of TileCfg<NBW, WN, MB>::kStages LDS stages ((8 / MB) x WN waves, each
+// MB*32 x NBW*32 of the output; wave w sits at row block w / WN, column block
+// w % WN).
 //
 // Schedule per stage kt (two 16-deep steps f0, f1):
 //   issue f1 reads (stage kt) | f0 MFMAs | settle f1
@@ -306,10 +319,10 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NB]) {
 // range past the end), so the compiler's wait counts hold on every path.
 // Starts with a block barrier (the previous user of the LDS is done) and ends
 // with one; on return no load is in flight and the LDS may be reused.
-template <bool TA, bool TB, int NBW, int WN = 2>
+template <bool TA, bool TB, int NBW, int WN = 2, int MB = 4>
 __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0,
-                                              int nk, f32x16 (&acc)[4][NBW], char* lds) {
-  using C = TileCfg<NBW, WN>;
+                                              int nk, f32x16 (&acc)[MB][NBW], char* lds) {
+  using C = TileCfg<NBW, WN, MB>;
   constexpr int S = C::kStages;
   constexpr int RB = C::kBExtent;
   constexpr int LA = C::kDmaA;
@@ -335,7 +348,7 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B
   }
   wait_vmcnt<(S - 1) * C::kDmaStage>();  // stage 0 landed
   block_barrier();
-  Frags<TA, TB, NBW, RB> f0, f1;
+  Frags<TA, TB, NBW, RB, MB> f0, f1;
   f0.issue(lds, lds + kAStageBytes, wm, wn, 0, lane);
   f0.settle();
   for (int kt = 0; kt + 1 < nk; ++kt) {

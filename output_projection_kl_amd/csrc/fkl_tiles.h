@@ -76,6 +76,55 @@ __device__ __forceinline__ int xcd_contiguous_range(int w, int first, int count)
 
 // One 256 x 256 output tile of C (+)= A B^T; `local` is this workgroup's
 // index among the problem's tiles (XCD-renumbered).
+// 256 x 64 output tile of C (+)= A B^T: 8 waves of 32 x 64, fp32 epilogue
+// through a 256 x 64 LDS tile (stride kNarrowLd), old values loaded first.
+constexpr int kNarrowN = 64;
+constexpr int kNarrowLd = kNarrowN + 4;
+
+template <bool TA, bool TB>
+__device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Operand& A, const Operand& B,
+                                                int64_t m0, int64_t n0, int nk, float* C, char* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  f32x16 acc[1][2];
+  zero_acc(acc);
+  gemm_mainloop<TA, TB, 2, 1, 1>(A, B, m0, n0, nk, acc, lds);
+  const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
+  const int cmax = static_cast<int>(P.n_lim - n0);
+  float* ctile = C + m0 * P.ldc + n0;
+  constexpr int kPer = (kTile * kNarrowN / 4) / kBlockThreads;  // 16-byte pieces per thread
+  f32x4 old[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + i * kBlockThreads;
+    const int r = q >> 4;
+    const int c4 = (q & 15) * 4;
+    old[i] = (P.beta && r < rmax && c4 < cmax)
+                 ? *reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float* stage = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      stage[(wave * 32 + acc_row(0, i, lane)) * kNarrowLd + acc_col(nb, lane)] = acc[0][nb][i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + i * kBlockThreads;
+    const int r = q >> 4;
+    const int c4 = (q & 15) * 4;
+    if (r < rmax && c4 < cmax) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kNarrowLd + c4);
+      *reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4) =
+          f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]};
+    }
+  }
+  __syncthreads();
+}
+
 template <bool TA, bool TB>
 __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local, char* lds) {
   const int tid = threadIdx.x;
@@ -93,6 +142,13 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
   const int64_t klen = static_cast<int64_t>(P.kper) * kStageK;
   const int nk = min(P.kper, P.nk - split * P.kper);
   float* C = P.C + split * P.c_split;
+  if (P.n_lim - n0 <= kNarrowN) {
+    // A last column block of at most 64 columns (d = 2880 leaves one): the
+    // 8 waves stack along the rows (32 x 64 each) instead of computing a
+    // 256-wide tile that is three quarters zero padding.
+    narrow_acc_tile<TA, TB>(P, k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk, C, lds);
+    return;
+  }
   f32x16 acc[4][kNBW];
   zero_acc(acc);
   gemm_mainloop<TA, TB, kNBW, kWN>(k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk,

@@ -102,6 +102,15 @@ def test_ragged_shapes():
     _check_full(wl, T=0.7, chunk=128, vslab=768, grad_loss=2.5, label="ragged")
 
 
+@pytest.mark.parametrize("d", [320, 264])
+def test_hidden_size_with_a_narrow_last_column_block(d):
+    """d = 256 + 64 and 256 + 8: the gradient contractions' last column block
+    takes the 256 x 64 tile path (grad_h with transposed operands, grad_W with
+    a plain one), over several chunks, slabs and vocabulary splits."""
+    wl = make_workload("tiny", N=300, d=d, V=3000, K=9, mask="random25")
+    _check_full(wl, T=1.3, chunk=128, vslab=768, grad_loss=0.8, label=f"narrow-d{d}")
+
+
 def test_single_teacher_entry():
     wl = make_workload("tiny", N=96, d=64, V=1000, K=1)
     _check_full(wl, T=1.0, chunk=64, label="K=1")
