@@ -15,4 +15,6 @@ from .fkl_oracle import (  # noqa: F401
     grad_W_rows,
     dense_teacher_grid,
     topk_teacher,
+    forward_terms,
+    backward_terms,
 )

@@ -64,6 +64,8 @@ __all__ = [
     "grad_W_rows",
     "dense_teacher_grid",
     "topk_teacher",
+    "forward_terms",
+    "backward_terms",
 ]
 
 
@@ -294,3 +296,67 @@ def topk_teacher(h, W, K: int):
         idx[r] = order
         val[r] = z[order]
     return idx, val
+
+
+def _weights(mask, row_weight, N: int) -> np.ndarray:
+    """Per-row weight: row_weight (1 if absent) times the mask (1 if absent)."""
+    w = np.ones(N) if row_weight is None else _f64(row_weight).reshape(N)
+    return np.where(_valid_rows(mask, N), w, 0.0)
+
+
+def forward_terms(h, W, t_idx, t_logit, T: float = 1.0, mask=None, row_weight=None, label=None,
+                  label_weight: float = 0.0):
+    """Loss variants on the same fused structure (readings; the pages name a
+    "choice of loss function" [AIX] but define no variant):
+
+      l_r  = (1 - a) KL(p_r || q_r) + a CE(y_r, q_r)      q_r = softmax(z_r / T)
+      loss = T^2 sum_r w_r l_r / sum_r w_r                (0 if sum_r w_r = 0)
+
+    with w_r = row_weight[r] * mask[r] (per-token weights; the mask is the
+    0/1 case), y_r = label[r] a hard label, a = label_weight (a = 0 or no
+    label: plain KL). Both terms use the loss temperature. Dense per row,
+    written directly from the definition. Returns (loss, row_lse, row_l)
+    with row_l the unweighted per-row l_r (0 where w_r = 0).
+    """
+    h = _f64(h)
+    W = _f64(W)
+    t_idx = np.asarray(t_idx, dtype=np.int64)
+    N = h.shape[0]
+    _check_teacher(t_idx, W.shape[0])
+    w = _weights(mask, row_weight, N)
+    a = float(label_weight) if label is not None else 0.0
+    s = _chunk_logits(h, W, T)
+    lse = _row_logsumexp(s)
+    log_q = s - lse[:, None]
+    p, log_p = teacher_distribution(t_logit, T)
+    kl = (p * (log_p - np.take_along_axis(log_q, t_idx, axis=1))).sum(axis=1)
+    ce = np.zeros(N) if label is None else -log_q[np.arange(N), np.asarray(label, dtype=np.int64)]
+    row_l = np.where(w > 0, (1.0 - a) * kl + a * ce, 0.0)
+    sw = w.sum()
+    loss = (T * T) * float((w * row_l).sum()) / sw if sw > 0 else 0.0
+    return loss, lse, row_l
+
+
+def backward_terms(h, W, t_idx, t_logit, T: float = 1.0, mask=None, row_weight=None, label=None,
+                   label_weight: float = 0.0, grad_loss: float = 1.0):
+    """Gradients of forward_terms: with c_r = g T w_r / sum w,
+    G[r, v] = c_r ((1 - a)(q - p~) + a (q - onehot(y_r)))[r, v],
+    grad_h = G W, grad_W = G^T h (dl/ds = q - target, ds/dz = 1/T, times T^2)."""
+    h = _f64(h)
+    W = _f64(W)
+    t_idx = np.asarray(t_idx, dtype=np.int64)
+    N = h.shape[0]
+    w = _weights(mask, row_weight, N)
+    sw = w.sum()
+    if sw <= 0:
+        return np.zeros_like(h), np.zeros_like(W)
+    a = float(label_weight) if label is not None else 0.0
+    s = _chunk_logits(h, W, T)
+    q = np.exp(s - _row_logsumexp(s)[:, None])
+    p, _ = teacher_distribution(t_logit, T)
+    target = np.zeros_like(q)
+    np.put_along_axis(target, t_idx, (1.0 - a) * p, axis=1)
+    if label is not None:
+        target[np.arange(N), np.asarray(label, dtype=np.int64)] += a
+    G = (float(grad_loss) * T * w / sw)[:, None] * (q - target)
+    return G @ W, G.T @ h

@@ -388,6 +388,70 @@ def test_topk_teacher_brute_force_with_ties():
         oracle.topk_teacher(h, W, 41)
 
 
+# ---------------------------------------------------------------------------
+# Loss variants: per-token weights and a hard-label cross-entropy term
+# ---------------------------------------------------------------------------
+
+def _torch_terms(h, W, t_idx, t_logit, T, w, label, a):
+    """Dense torch reference: kl_div and cross_entropy per row, weighted mean."""
+    ht = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    N, V = h.shape[0], W.shape[0]
+    p = torch.softmax(torch.tensor(np.asarray(t_logit, dtype=np.float64)) / T, dim=1)
+    grid = torch.zeros(N, V, dtype=torch.float64)
+    grid.scatter_(1, torch.tensor(np.asarray(t_idx, dtype=np.int64)), p)
+    s = (ht @ Wt.T) / T
+    kl = torch.nn.functional.kl_div(torch.log_softmax(s, dim=1), grid, reduction="none").sum(dim=1)
+    ce = torch.nn.functional.cross_entropy(s, torch.tensor(label, dtype=torch.int64), reduction="none")
+    wt = torch.tensor(w, dtype=torch.float64)
+    loss = (T * T) * (wt * ((1 - a) * kl + a * ce)).sum() / wt.sum()
+    loss.backward()
+    return loss.item(), ht.grad.numpy(), Wt.grad.numpy()
+
+
+@pytest.mark.parametrize("T,a", [(1.0, 0.3), (2.0, 0.5), (0.8, 1.0)])
+def test_loss_terms_match_torch_dense(T, a):
+    h, W, t_idx, t_logit, mask = _rand_problem(151, N=9, d=8, V=40, K=6, mask_frac=0.3)
+    rng = np.random.default_rng(152)
+    w = rng.random(9) * 2.0
+    label = rng.integers(0, 40, size=9)
+    label[0] = t_idx[0, 2]            # a label that is also a teacher index
+    w_eff = w * mask
+    loss_t, gh_t, gW_t = _torch_terms(h, W, t_idx, t_logit, T, w_eff, label, a)
+    loss, lse, row_l = oracle.forward_terms(h, W, t_idx, t_logit, T, mask, w, label, a)
+    gh, gW = oracle.backward_terms(h, W, t_idx, t_logit, T, mask, w, label, a)
+    assert loss == pytest.approx(loss_t, rel=1e-12)
+    np.testing.assert_allclose(gh, gh_t, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(gW, gW_t, rtol=1e-10, atol=1e-14)
+
+
+def test_loss_terms_reduce_to_the_plain_loss():
+    """No label (or a = 0) with 0/1 weights is the plain masked KL; scaling all
+    weights changes nothing."""
+    h, W, t_idx, t_logit, mask = _rand_problem(153, N=10, d=8, V=30, K=5, mask_frac=0.4)
+    T = 1.4
+    loss0, lse0, kl0 = oracle.forward(h, W, t_idx, t_logit, T, mask)
+    gh0, gW0 = oracle.backward(h, W, t_idx, t_logit, T, mask, grad_loss=0.6)
+    label = np.arange(10) % 30
+    for rw, lab, a in ((None, None, 0.0), (np.full(10, 3.5), label, 0.0), (None, None, 0.7)):
+        loss, lse, row_l = oracle.forward_terms(h, W, t_idx, t_logit, T, mask, rw, lab, a)
+        gh, gW = oracle.backward_terms(h, W, t_idx, t_logit, T, mask, rw, lab, a, grad_loss=0.6)
+        assert loss == pytest.approx(loss0, rel=1e-12)
+        np.testing.assert_allclose(row_l, kl0, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(gh, gh0, rtol=1e-11, atol=1e-16)
+        np.testing.assert_allclose(gW, gW0, rtol=1e-11, atol=1e-16)
+
+
+def test_loss_terms_label_only_is_cross_entropy():
+    h, W, t_idx, t_logit, _ = _rand_problem(154, N=7, d=8, V=25, K=4)
+    label = np.array([3, 0, 24, 7, 7, 11, 1])
+    T = 1.0
+    loss, _, row_l = oracle.forward_terms(h, W, t_idx, t_logit, T, None, None, label, 1.0)
+    ce = torch.nn.functional.cross_entropy(torch.tensor(h @ W.T), torch.tensor(label), reduction="none")
+    np.testing.assert_allclose(row_l, ce.numpy(), rtol=1e-13)
+    assert loss == pytest.approx(ce.mean().item(), rel=1e-13)
+
+
 def test_oracle_rejects_bad_teacher():
     h, W, t_idx, t_logit, _ = _rand_problem(121)
     bad = t_idx.copy()
