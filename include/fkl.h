@@ -97,6 +97,26 @@ typedef struct {
 #define FKL_FLAGS_ALL 0x1fu
 
 /*
+ * Optional loss terms (pass NULL for the plain loss). The pages name a
+ * "choice of loss function" for the distillation loss without defining
+ * variants; these are the ones the fused structure carries at no extra
+ * contraction work:
+ *   row_weight   fp32 [N] per-token weights w_r >= 0 (finite), multiplied by
+ *                the row mask; NULL means 1. The loss is the weighted mean
+ *                T^2 sum_r w_r l_r / sum_r w_r (0 when the sum is 0).
+ *   label        int32 [N] hard labels y_r in [0, V) (precondition, not
+ *                checked); NULL means no label term.
+ *   label_weight a in [0, 1]: per row l_r = (1 - a) KL(p_r || q_r) +
+ *                a CE(y_r, q_r), both at the loss temperature (q = softmax(z/T)).
+ * row_kl then reports l_r (0 where w_r = 0).
+ */
+typedef struct {
+  const float* row_weight;
+  const int32_t* label;
+  float label_weight;
+} fkl_terms;
+
+/*
  * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
  * Pure host code. The sizes grow with chunk, vslab and K only (never with
  * N or with V beyond one slab): forward O(chunk * (K + 64)), backward
@@ -112,7 +132,7 @@ fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t*
  */
 fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
                        const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
-                       float* loss, float* row_lse, float* row_kl,
+                       const fkl_terms* terms, float* loss, float* row_lse, float* row_kl,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -125,7 +145,7 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
  */
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
                         const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
-                        const float* row_lse, const float* grad_loss,
+                        const fkl_terms* terms, const float* row_lse, const float* grad_loss,
                         void* grad_h, float* grad_W,
                         void* workspace, size_t workspace_bytes, void* stream);
 

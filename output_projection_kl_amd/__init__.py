@@ -28,6 +28,7 @@ __all__ = [
     "backward",
     "validate_teacher",
     "FusedKLLoss",
+    "Terms",
     "ACCUMULATE_GRAD_W",
     "ACCUMULATE_GRAD_H",
     "SKIP_GRAD_W",
@@ -95,6 +96,16 @@ class Shape(ctypes.Structure):
     ]
 
 
+class Terms(ctypes.Structure):
+    """Mirror of ``fkl_terms``."""
+
+    _fields_ = [
+        ("row_weight", ctypes.c_void_p),
+        ("label", ctypes.c_void_p),
+        ("label_weight", ctypes.c_float),
+    ]
+
+
 class TopkShape(ctypes.Structure):
     """Mirror of ``fkl_topk_shape``."""
 
@@ -123,8 +134,8 @@ def lib() -> ctypes.CDLL:
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     shp = ctypes.POINTER(Shape)
     L.fkl_workspace_size.argtypes = [shp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
-    L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
     tshp = ctypes.POINTER(TopkShape)
     L.fkl_topk_workspace_size.argtypes = [tshp, ctypes.POINTER(sz)]
@@ -213,6 +224,18 @@ def _inputs(h, W, t_idx, t_logit, mask):
     return N, d, V, K
 
 
+def _terms(N, V, row_weight, label, label_weight):
+    """ctypes fkl_terms for the optional loss terms, or None for the plain loss."""
+    torch = _torch()
+    if row_weight is None and label is None:
+        return None
+    if row_weight is not None:
+        _need(row_weight, "row_weight", torch.float32, (N,))
+    if label is not None:
+        _need(label, "label", torch.int32, (N,))
+    return Terms(_ptr(row_weight), _ptr(label), float(label_weight))
+
+
 def _workspace(nbytes, device, workspace):
     torch = _torch()
     if workspace is not None:
@@ -223,12 +246,16 @@ def _workspace(nbytes, device, workspace):
 
 
 def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vslab: int = 0,
-            workspace=None, return_row_kl: bool = False, loss=None, row_lse=None, row_kl=None):
+            workspace=None, return_row_kl: bool = False, loss=None, row_lse=None, row_kl=None,
+            row_weight=None, label=None, label_weight: float = 0.0):
     """Fused forward. Returns (loss [1], row_lse [N]) or (loss, row_lse, row_kl).
 
-    Output tensors may be passed in to be overwritten (no allocation)."""
+    Output tensors may be passed in to be overwritten (no allocation).
+    row_weight (fp32 [N]), label (int32 [N]) and label_weight select the loss
+    variants of include/fkl.h (weighted mean; KL mixed with hard-label CE)."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
+    terms = _terms(N, V, row_weight, label, label_weight)
     s = make_shape(N, d, V, K, T, chunk, vslab)
     fb, _ = workspace_size(N, d, V, K, T, chunk, vslab)
     ws = _workspace(fb, h.device, workspace)
@@ -244,7 +271,7 @@ def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vsl
         _need(row_kl, "row_kl", torch.float32, (N,))
         return_row_kl = True
     _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
-                             _ptr(loss), _ptr(row_lse), _ptr(row_kl), _ptr(ws),
+                             None if terms is None else ctypes.byref(terms), _ptr(loss), _ptr(row_lse), _ptr(row_kl), _ptr(ws),
                              ctypes.c_size_t(ws.numel()), _stream()))
     return (loss, row_lse, row_kl) if return_row_kl else (loss, row_lse)
 
@@ -252,7 +279,7 @@ def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vsl
 def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss=None, chunk: int = 0,
              vslab: int = 0, workspace=None, grad_h=None, grad_W=None, need_grad_h: bool = True,
              need_grad_W: bool = True, accumulate_grad_h: bool = False, accumulate_grad_W: bool = False,
-             grad_h_dtype=None):
+             grad_h_dtype=None, row_weight=None, label=None, label_weight: float = 0.0):
     """Fused backward with recomputation. Returns (grad_h [N, d], grad_W fp32 [V, d]); a
     gradient that is not needed comes back as None. grad_h is fp32, or bf16 when
     grad_h_dtype is torch.bfloat16 (or a bf16 grad_h is passed). With accumulate_*,
@@ -262,6 +289,7 @@ def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss
     _need(row_lse, "row_lse", torch.float32, (N,))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, (1,))
+    terms = _terms(N, V, row_weight, label, label_weight)
     if grad_h_dtype is None:
         grad_h_dtype = grad_h.dtype if grad_h is not None else torch.float32
     if grad_h_dtype not in (torch.float32, torch.bfloat16):
@@ -287,7 +315,7 @@ def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss
     else:
         _need(grad_W, "grad_W", torch.float32, (V, d))
     _check(lib().fkl_backward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
-                              _ptr(row_lse), _ptr(grad_loss), _ptr(grad_h), _ptr(grad_W), _ptr(ws),
+                              None if terms is None else ctypes.byref(terms), _ptr(row_lse), _ptr(grad_loss), _ptr(grad_h), _ptr(grad_W), _ptr(ws),
                               ctypes.c_size_t(ws.numel()), _stream()))
     return grad_h, grad_W
 
@@ -302,32 +330,35 @@ class FusedKLLoss:
     _fn = None
 
     @classmethod
-    def apply(cls, h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0):
+    def apply(cls, h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, row_weight=None,
+              label=None, label_weight: float = 0.0):
         if cls._fn is None:
             torch = _torch()
 
             class _Fn(torch.autograd.Function):
                 @staticmethod
-                def forward(ctx, h, W, t_idx, t_logit, T, mask, chunk):
-                    loss, lse = forward(h, W, t_idx, t_logit, T=T, mask=mask, chunk=chunk)
-                    ctx.save_for_backward(h, W, t_idx, t_logit, lse, mask)
-                    ctx.T, ctx.chunk = T, chunk
+                def forward(ctx, h, W, t_idx, t_logit, T, mask, chunk, row_weight, label, label_weight):
+                    loss, lse = forward(h, W, t_idx, t_logit, T=T, mask=mask, chunk=chunk, row_weight=row_weight,
+                                        label=label, label_weight=label_weight)
+                    ctx.save_for_backward(h, W, t_idx, t_logit, lse, mask, row_weight, label)
+                    ctx.T, ctx.chunk, ctx.label_weight = T, chunk, label_weight
                     return loss.reshape(())
 
                 @staticmethod
                 def backward(ctx, g):
-                    h, W, t_idx, t_logit, lse, mask = ctx.saved_tensors
+                    h, W, t_idx, t_logit, lse, mask, row_weight, label = ctx.saved_tensors
                     need_h, need_W = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
                     if not (need_h or need_W):
-                        return (None,) * 7
+                        return (None,) * 10
                     gl = g.detach().reshape(1).to(torch.float32).contiguous()
                     gh, gW = backward(h, W, t_idx, t_logit, lse, T=ctx.T, mask=mask, grad_loss=gl,
                                       chunk=ctx.chunk, need_grad_h=need_h, need_grad_W=need_W,
-                                      grad_h_dtype=h.dtype if h.dtype == torch.bfloat16 else torch.float32)
-                    return gh, gW, None, None, None, None, None
+                                      grad_h_dtype=h.dtype if h.dtype == torch.bfloat16 else torch.float32,
+                                      row_weight=row_weight, label=label, label_weight=ctx.label_weight)
+                    return gh, gW, None, None, None, None, None, None, None, None
 
             cls._fn = _Fn
-        return cls._fn.apply(h, W, t_idx, t_logit, T, mask, chunk)
+        return cls._fn.apply(h, W, t_idx, t_logit, T, mask, chunk, row_weight, label, label_weight)
 
 
 def validate_teacher(t_idx, t_logit, V: int) -> int:

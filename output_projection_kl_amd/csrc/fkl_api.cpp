@@ -19,6 +19,18 @@ fkl_status fail(fkl_status st, const char* msg) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Optional loss terms: NULL means none; checks what the host can check.
+fkl_status read_terms(const fkl_terms* t, const float** weight, const int32_t** label, float* label_w) {
+  *weight = t ? t->row_weight : nullptr;
+  *label = t ? t->label : nullptr;
+  *label_w = (t && t->label) ? t->label_weight : 0.0f;
+  if (t && !(t->label_weight >= 0.0f && t->label_weight <= 1.0f))
+    return fail(FKL_EINVAL, "label_weight must be in [0, 1]");
+  if ((*weight && !aligned(*weight, 4)) || (*label && !aligned(*label, 4)))
+    return fail(FKL_EINVAL, "row_weight and label must be 4-byte aligned");
+  return FKL_OK;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
@@ -65,9 +77,10 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_negent = off;
   off = align256(off + static_cast<size_t>(p->chunk_alloc) * 4);
   p->off_tidx = off;
-  off = align256(off + static_cast<size_t>(p->chunk_alloc) * p->K * 4);
+  // teacher lists hold K entries, or K + 1 with hard labels
+  off = align256(off + static_cast<size_t>(p->chunk_alloc) * (p->K + 1) * 4);
   p->off_tp = off;
-  off = align256(off + static_cast<size_t>(p->chunk_alloc) * p->K * 4);
+  off = align256(off + static_cast<size_t>(p->chunk_alloc) * (p->K + 1) * 4);
   const size_t shared_end = off;
   // forward: split partials (two per row per workgroup) for up to (256 + rbs)
   // workgroups' rows, then block sums
@@ -139,12 +152,18 @@ fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t*
 }
 
 fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
-                       const float* t_logit, const uint8_t* row_mask, float* loss, float* row_lse,
+                       const float* t_logit, const uint8_t* row_mask, const fkl_terms* terms, float* loss,
+                       float* row_lse,
                        float* row_kl, void* workspace, size_t workspace_bytes, void* stream) {
   fkl::Plan p;
   fkl_status st = fkl::make_plan(shape, &p);
   if (st != FKL_OK) return st;
   if (!loss) return fail(FKL_EINVAL, "loss is NULL");
+  const float* weight;
+  const int32_t* label;
+  float label_w;
+  st = read_terms(terms, &weight, &label, &label_w);
+  if (st != FKL_OK) return st;
   if (!aligned(loss, 4)) return fail(FKL_EINVAL, "loss must be 4-byte aligned");
   if (p.N > 0) {
     if (!h || !W || !t_idx || !t_logit || !row_lse)
@@ -158,7 +177,7 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
   fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
-                 loss, row_lse, row_kl, static_cast<char*>(workspace)};
+                 weight, label, label_w, loss, row_lse, row_kl, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_forward(p, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("forward launch failed: ") + hipGetErrorString(e);
@@ -168,7 +187,8 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
 }
 
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
-                        const float* t_logit, const uint8_t* row_mask, const float* row_lse,
+                        const float* t_logit, const uint8_t* row_mask, const fkl_terms* terms,
+                        const float* row_lse,
                         const float* grad_loss, void* grad_h, float* grad_W, void* workspace,
                         size_t workspace_bytes, void* stream) {
   fkl::Plan p;
@@ -176,6 +196,11 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   if (st != FKL_OK) return st;
   const bool want_w = !(p.flags & FKL_SKIP_GRAD_W);
   const bool want_h = !(p.flags & FKL_SKIP_GRAD_H);
+  const float* weight;
+  const int32_t* label;
+  float label_w;
+  st = read_terms(terms, &weight, &label, &label_w);
+  if (st != FKL_OK) return st;
   if (want_w && !grad_W) return fail(FKL_EINVAL, "grad_W is NULL");
   if (want_w && !aligned(grad_W, 16)) return fail(FKL_EINVAL, "grad_W must be 16-byte aligned");
   if (grad_loss && !aligned(grad_loss, 4)) return fail(FKL_EINVAL, "grad_loss must be 4-byte aligned");
@@ -193,7 +218,7 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   if (workspace_bytes < p.bwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
   if (!want_w && !want_h) return FKL_OK;  // nothing asked for
   fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
-                 row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
+                 weight, label, label_w, row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_backward(p, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("backward launch failed: ") + hipGetErrorString(e);

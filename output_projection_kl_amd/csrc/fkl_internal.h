@@ -55,6 +55,9 @@ struct FwdArgs {
   const int32_t* t_idx;
   const float* t_logit;
   const uint8_t* mask;
+  const float* weight;   // per-row weights or NULL
+  const int32_t* label;  // hard labels or NULL
+  float label_weight;
   float* loss;
   float* row_lse;
   float* row_kl;
@@ -67,6 +70,9 @@ struct BwdArgs {
   const int32_t* t_idx;
   const float* t_logit;
   const uint8_t* mask;
+  const float* weight;
+  const int32_t* label;
+  float label_weight;
   const float* row_lse;
   const float* grad_loss;
   void* grad_h;  // fp32, or bf16 with FKL_GRAD_H_BF16

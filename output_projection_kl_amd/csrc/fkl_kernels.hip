@@ -34,41 +34,54 @@ namespace fkl {
 struct Scalars {
   double acc;       // running sum of valid-row KL (fp64, fixed order)
   int64_t n_valid;  // number of valid rows
+  double wsum;      // sum over rows of mask x row weight (= n_valid without weights)
 };
 
 // ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__ mask, int64_t N,
+__global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__ mask,
+                                                     const float* __restrict__ weight, int64_t N,
                                                      Scalars* sc) {
   __shared__ int64_t part[256];
+  __shared__ double wpart[256];
   int64_t cnt = 0;
-  if (mask) {
-    for (int64_t r = threadIdx.x; r < N; r += 256) cnt += (mask[r] != 0);
-  } else if (threadIdx.x == 0) {
-    cnt = N;
+  double ws = 0.0;
+  for (int64_t r = threadIdx.x; r < N; r += 256) {
+    const bool valid = !mask || mask[r] != 0;
+    cnt += valid;
+    ws += valid ? (weight ? static_cast<double>(weight[r]) : 1.0) : 0.0;
   }
   part[threadIdx.x] = cnt;
+  wpart[threadIdx.x] = ws;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    if (threadIdx.x < s) {
+      part[threadIdx.x] += part[threadIdx.x + s];
+      wpart[threadIdx.x] += wpart[threadIdx.x + s];
+    }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
     sc->n_valid = part[0];
+    sc->wsum = wpart[0];
     sc->acc = 0.0;
   }
 }
 
-// One wave per row, four rows per workgroup. p = softmax(t_logit / T) over
-// the K cached entries; negent = sum_k p log p; the (index, p) pairs are
-// written in ascending index order (stable rank, so even repeated indices
-// fill every slot).
+// One wave per row, four rows per workgroup: p = softmax(t_logit / T) over
+// the K cached entries, the row's list of (index, weight) sorted by vocabulary index, and the weighted
+// negative entropy (stable ranks, so even repeated indices fill every slot).
+// With a hard label y (weight a), the list holds the target
+// (1 - a) p~ + a onehot(y): teacher weights are scaled by 1 - a and y is
+// inserted with a, or a is added to the teacher entry at y (the list then ends
+// with an empty entry at INT_MAX). Lists have L = K (+ 1 with labels) entries.
 __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict__ t_idx,
-                                                      const float* __restrict__ t_logit, int64_t r0,
-                                                      int32_t rows, int32_t K, float invT,
-                                                      int32_t* __restrict__ tsort_idx,
+                                                      const float* __restrict__ t_logit,
+                                                      const int32_t* __restrict__ label, float label_w,
+                                                      int64_t r0, int32_t rows, int32_t K, int32_t L,
+                                                      float invT, int32_t* __restrict__ tsort_idx,
                                                       float* __restrict__ tsort_p,
                                                       float* __restrict__ negent) {
   __shared__ int32_t sidx[4][1024];
@@ -92,9 +105,23 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
   for (int k = lane; k < K; k += 64) se += expf(tl[k] * invT - mx);
   se = wave_sum(se);
   const float lnorm = mx + logf(se);
+  const bool has_label = label != nullptr;
+  const int32_t y = has_label ? label[r0 + r] : 0;
+  const float keep = has_label ? 1.0f - label_w : 1.0f;
+  // where y goes: the number of teacher indices below it, and whether it is one
+  int below = 0, dup = 0;
+  if (has_label) {
+    for (int k = lane; k < K; k += 64) {
+      below += sidx[wave][k] < y;
+      dup += sidx[wave][k] == y;
+    }
+    below = static_cast<int>(wave_sum(static_cast<float>(below)));
+    dup = static_cast<int>(wave_sum(static_cast<float>(dup)));
+  }
+  const bool insert = has_label && dup == 0;
   float ne = 0.f;
-  int32_t* oi = tsort_idx + static_cast<int64_t>(r) * K;
-  float* op = tsort_p + static_cast<int64_t>(r) * K;
+  int32_t* oi = tsort_idx + static_cast<int64_t>(r) * L;
+  float* op = tsort_p + static_cast<int64_t>(r) * L;
   for (int k = lane; k < K; k += 64) {
     const float lp = tl[k] * invT - lnorm;
     const float p = expf(lp);
@@ -105,11 +132,21 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
       const int32_t o = sidx[wave][j];
       rank += (o < key) | ((o == key) & (j < k));
     }
+    if (insert && key > y) ++rank;
     oi[rank] = key;
-    op[rank] = p;
+    op[rank] = keep * p + ((has_label && key == y) ? label_w : 0.0f);
   }
   ne = wave_sum(ne);
-  if (lane == 0) negent[r] = ne;
+  if (lane == 0) {
+    negent[r] = keep * ne;
+    if (insert) {
+      oi[below] = y;
+      op[below] = label_w;
+    } else if (has_label) {
+      oi[K] = INT_MAX;
+      op[K] = 0.0f;
+    }
+  }
 }
 
 __global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, Scalars* sc) {
@@ -122,9 +159,8 @@ __global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, 
 
 __global__ void k_finalize(const Scalars* sc, float T, float* loss) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const int64_t n = sc->n_valid;
-    loss[0] = n > 0 ? static_cast<float>(static_cast<double>(T) * T * sc->acc / static_cast<double>(n))
-                    : 0.0f;
+    const double w = sc->wsum;
+    loss[0] = w > 0.0 ? static_cast<float>(static_cast<double>(T) * T * sc->acc / w) : 0.0f;
   }
 }
 
@@ -324,7 +360,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
 __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int parts,
                                                      int rows, int64_t r0,
                                                      const float* __restrict__ negent,
-                                                     const uint8_t* __restrict__ mask, float invT,
+                                                     const uint8_t* __restrict__ mask,
+                                                     const float* __restrict__ weight, float invT,
                                                      float* __restrict__ row_lse,
                                                      float* __restrict__ row_kl,
                                                      double* __restrict__ block_sum) {
@@ -344,9 +381,10 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
     const float lse = (M + log2f(sum)) * kLn2;
     const float kl = negent[r] - gz * invT + lse;
     const bool valid = !mask || mask[r0 + r] != 0;
+    const float w = valid ? (weight ? weight[r0 + r] : 1.0f) : 0.0f;
     row_lse[r0 + r] = lse;
-    if (row_kl) row_kl[r0 + r] = valid ? kl : 0.f;
-    kl_d = valid ? static_cast<double>(kl) : 0.0;
+    if (row_kl) row_kl[r0 + r] = w > 0.f ? kl : 0.f;
+    kl_d = w > 0.f ? static_cast<double>(w) * kl : 0.0;
   }
   red[threadIdx.x] = kl_d;
   __syncthreads();
@@ -372,6 +410,7 @@ struct BwdGParams {
   const float* tsort_p;
   const float* row_lse;
   const uint8_t* mask;
+  const float* weight;
   const float* grad_loss;
   const Scalars* sc;
   int64_t slab0;
@@ -414,10 +453,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
 
   float c = 0.f, lse2 = 0.f;
   if (row < P.rows) {
-    const int64_t n = P.sc->n_valid;
+    const double wsum = P.sc->wsum;
     const float g = P.grad_loss ? P.grad_loss[0] : 1.0f;
     const bool valid = !P.mask || P.mask[grow] != 0;
-    c = (valid && n > 0) ? static_cast<float>(static_cast<double>(g) * P.T / static_cast<double>(n)) : 0.f;
+    const float w = valid ? (P.weight ? P.weight[grow] : 1.0f) : 0.0f;
+    c = (w > 0.f && wsum > 0.0) ? static_cast<float>(static_cast<double>(g) * P.T * w / wsum) : 0.f;
     lse2 = P.row_lse[grow] * kLog2e;
   }
   float* row_lse2 = reinterpret_cast<float*>(lds + kBwdGConstOff);
@@ -619,18 +659,19 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
   double* bsum = reinterpret_cast<double*>(a.ws + p.off_blocksum);
   const float invT = 1.0f / p.T;
   const float k2 = kLog2e / p.T;
+  const int32_t L = p.K + (a.label ? 1 : 0);  // teacher list entries per row
 
-  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
+  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, a.weight, p.N, sc);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
     const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
       hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                         c0, rows, p.K, invT, tidx, tp, negent);
+                         a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent);
     }
     const int splits = splits_for(rbs, p.n_vt);
-    FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, tidx, tp,
+    FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, L, k2, tidx, tp,
                       static_cast<int32_t>(p.n_vt), rbs, splits, partial};
     {
       const double dd = static_cast<double>(p.d);
@@ -641,7 +682,7 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
     {
       TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
       hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, 2 * splits, rows, c0, negent,
-                         a.mask, invT, a.row_lse, a.row_kl, bsum);
+                         a.mask, a.weight, invT, a.row_lse, a.row_kl, bsum);
     }
     hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, rbs, sc);
   }
@@ -657,6 +698,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   uint16_t* G = reinterpret_cast<uint16_t*>(a.ws + p.off_G);
   const float invT = 1.0f / p.T;
   const float k2 = kLog2e / p.T;
+  const int32_t L = p.K + (a.label ? 1 : 0);  // teacher list entries per row
 
   const bool want_w = !(p.flags & FKL_SKIP_GRAD_W);
   const bool want_h = !(p.flags & FKL_SKIP_GRAD_H);
@@ -668,7 +710,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   float* gh32 = reinterpret_cast<float*>(a.ws + p.off_gh32);
 
   if (!want_w && !want_h) return hipGetLastError();
-  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, p.N, sc);
+  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, a.weight, p.N, sc);
   if (p.N == 0) {
     if (want_w && !acc_w) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, a.grad_W, p.V * p.d);
     return hipGetLastError();
@@ -681,7 +723,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
       hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                         c0, rows, p.K, invT, tidx, tp, negent);
+                         a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent);
     }
     const double dd = static_cast<double>(p.d);
     for (int64_t s = 0; s < n_slabs; ++s) {
@@ -689,7 +731,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
       const int splits = splits_for(rbs, nvt);
-      BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, p.K, k2, p.T, tidx, tp, a.row_lse, a.mask,
+      BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, L, k2, p.T, tidx, tp, a.row_lse, a.mask, a.weight,
                     a.grad_loss, sc, slab0, slab_w, p.chunk_alloc, G, nvt, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,

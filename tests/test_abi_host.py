@@ -79,7 +79,7 @@ def test_k_larger_than_v_rejected():
 
 def _fwd(s, h=8192, W=16384, ti=4096, tl=4096, loss=256, lse=256, ws=1 << 20, ws_bytes=1 << 30):
     vp = ctypes.c_void_p
-    return fkl.lib().fkl_forward(ctypes.byref(s), vp(h), vp(W), vp(ti), vp(tl), vp(0), vp(loss), vp(lse),
+    return fkl.lib().fkl_forward(ctypes.byref(s), vp(h), vp(W), vp(ti), vp(tl), vp(0), vp(0), vp(loss), vp(lse),
                                  vp(0), vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
 
 
@@ -101,7 +101,7 @@ def test_backward_argument_errors_before_any_device_work():
     vp = ctypes.c_void_p
 
     def bwd(grad_h=8192, grad_W=16384, ws_bytes=1 << 30, grad_loss=0):
-        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(256),
+        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(0), vp(256),
                               vp(grad_loss), vp(grad_h), vp(grad_W), vp(1 << 20), ctypes.c_size_t(ws_bytes),
                               vp(0))
     assert bwd(grad_h=0) == 1
@@ -161,7 +161,7 @@ def test_backward_flags_checked_on_the_host():
 
     def bwd(flags, grad_h=8192, grad_W=16384, ws_bytes=1 << 30):
         s = fkl.make_shape(16, 64, 100, 5, flags=flags)
-        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(256),
+        return L.fkl_backward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), vp(0), vp(256),
                               vp(0), vp(grad_h), vp(grad_W), vp(1 << 20), ctypes.c_size_t(ws_bytes), vp(0))
     assert bwd(0x40) == 1                                   # unknown bit
     assert bwd(0, grad_W=0) == 1                            # grad_W needed
@@ -177,3 +177,18 @@ def test_bf16_grad_h_adds_an_fp32_accumulator_to_the_workspace():
     _, b2 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096,
                                flags=fkl.GRAD_H_BF16 | fkl.SKIP_GRAD_H)
     assert b2 == b0
+
+
+def test_loss_terms_checked_on_the_host():
+    vp = ctypes.c_void_p
+    s = fkl.make_shape(16, 64, 100, 5)
+    for a in (-0.1, 1.5, float("nan")):
+        t = fkl.Terms(None, 4096, a)
+        rc = fkl.lib().fkl_forward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0),
+                                   ctypes.byref(t), vp(256), vp(256), vp(0), vp(1 << 20), ctypes.c_size_t(1 << 30),
+                                   vp(0))
+        assert rc == 1
+    t = fkl.Terms(4098, None, 0.0)   # misaligned weights
+    rc = fkl.lib().fkl_forward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), ctypes.byref(t),
+                               vp(256), vp(256), vp(0), vp(1 << 20), ctypes.c_size_t(1 << 30), vp(0))
+    assert rc == 1

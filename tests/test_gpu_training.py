@@ -101,7 +101,7 @@ def test_skipped_gradients_are_untouched():
     gh3 = torch.empty((wl.N, wl.d), dtype=torch.float32, device=dev)
     import ctypes
     rc = fkl.lib().fkl_backward(ctypes.byref(s), h.data_ptr(), W.data_ptr(), ti.data_ptr(), tl.data_ptr(),
-                                m.data_ptr(), lse.data_ptr(), None, gh3.data_ptr(), poison.data_ptr(),
+                                m.data_ptr(), None, lse.data_ptr(), None, gh3.data_ptr(), poison.data_ptr(),
                                 ws.data_ptr(), ctypes.c_size_t(bb), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0
