@@ -136,6 +136,30 @@ def summarize_stats(stats_csv: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarize_mfma(counter_csv: str, command: str) -> str:
+    """Markdown table of MFMA utilisation per kernel from a rocprofv3 --pmc run
+    of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs, and MFMA busy cycles over the 1024 SIMDs."""
+    import collections
+    import csv
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"Command: `{command}`", "",
+             "| kernel | dispatches | MFMA busy SIMD-cycles | active cycles per XCD | MFMA utilisation |",
+             "|---|---|---|---|---|"]
+    for name, c in per.items():
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        act = c.get("GRBM_GUI_ACTIVE")
+        if not busy or not act or sum(busy) == 0:
+            continue
+        b = sum(busy) / len(busy)
+        a = sum(act) / len(act) / 8.0
+        lines.append(f"| {name} | {len(busy)} | {b:.4g} | {a:.4g} | {b / (1024.0 * a):.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(wl, rows: int):
     """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
     import numpy as np
@@ -237,12 +261,17 @@ def main() -> int:
                     help="time the teacher-cache builder (fkl_topk) on the large-head shape instead")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit (no GPU)")
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="print MFMA utilisation per kernel from a rocprofv3 counter run and exit (no GPU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE counter runs (no GPU)")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.command), end="")
+        return 0
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma, args.command), end="")
         return 0
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib or 1024, args.command)
