@@ -118,9 +118,13 @@ typedef struct {
 
 /*
  * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
- * Pure host code. The sizes grow with chunk, vslab and K only (never with
- * N or with V beyond one slab): forward O(chunk * (K + 64)), backward
- * O(chunk * (vslab + K)).
+ * Pure host code. The sizes depend on chunk, vslab, K, d and flags, never on
+ * N or on V beyond one slab: forward O(chunk * (K + 64)), backward
+ * O(chunk * (vslab + K)), plus O(chunk * d) fp32 when a chunk's grad_h is
+ * split along the vocabulary (few rows per chunk) or returned in bf16.
+ * Shapes whose h chunk (chunk x d bf16), W slab (vslab x d bf16) or
+ * gradient block (chunk x vslab bf16) would exceed 2 GiB return
+ * FKL_EUNSUPPORTED; the default vslab is capped to stay below.
  */
 fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t* bwd_bytes);
 

@@ -1,5 +1,6 @@
 // C ABI of libfkl: argument checks (pure host code, no HIP call), workspace
 // planning, and dispatch of the kernel sequences in fkl_kernels.hip.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -62,10 +63,18 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   if (s->N > 0 && chunk > s->N) chunk = s->N;
   p->chunk = chunk;
   p->chunk_alloc = round_up(chunk, kTile);
-  int64_t vslab = s->vslab ? s->vslab : kDefaultSlabElems / p->chunk_alloc;
+  // The kernels address each operand view (an h chunk, a W slab, the
+  // gradient block) through a buffer descriptor with a 32-bit byte size.
+  const int64_t kMaxView = (int64_t(1) << 31) - 1;
+  if (p->chunk_alloc * s->d * 2 > kMaxView)
+    return fail(FKL_EUNSUPPORTED, "chunk x d too large: a chunk of h must stay under 2 GiB");
+  const int64_t slab_cap = std::min(kMaxView / (2 * s->d), kMaxView / (2 * p->chunk_alloc)) / kTile * kTile;
+  int64_t vslab = s->vslab ? s->vslab : std::min<int64_t>(kDefaultSlabElems / p->chunk_alloc, slab_cap);
   vslab = round_up(vslab < kTile ? kTile : vslab, kTile);
   const int64_t v_all = round_up(s->V, kTile);
   if (vslab > v_all) vslab = v_all;
+  if (vslab > slab_cap)
+    return fail(FKL_EUNSUPPORTED, "vslab too large: a W slab and the gradient block must stay under 2 GiB");
   p->vslab = vslab;
   p->n_vt = ceil_div(s->V, kTile);
   const int64_t rbs = p->chunk_alloc / kTile;

@@ -192,3 +192,18 @@ def test_loss_terms_checked_on_the_host():
     rc = fkl.lib().fkl_forward(ctypes.byref(s), vp(8192), vp(16384), vp(4096), vp(4096), vp(0), ctypes.byref(t),
                                vp(256), vp(256), vp(0), vp(1 << 20), ctypes.c_size_t(1 << 30), vp(0))
     assert rc == 1
+
+
+def test_operand_views_stay_under_2_gib():
+    """Each operand view is addressed with a 32-bit byte size: shapes that would
+    need a larger h chunk, W slab or gradient block are refused; the default
+    slab is capped instead."""
+    L = fkl.lib()
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    s = fkl.make_shape(1 << 20, 65536, 50000, 10, chunk=32768)      # h chunk 4 GiB
+    assert L.fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)) == 5
+    s = fkl.make_shape(4096, 2880, 1 << 22, 10, chunk=4096, vslab=1 << 20)  # W slab 5.6 GiB
+    assert L.fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)) == 5
+    s = fkl.make_shape(4096, 65536, 1 << 22, 10, chunk=256)         # default slab capped
+    assert L.fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)) == 0
+    assert b.value < (2 << 30)
