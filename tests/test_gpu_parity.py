@@ -111,6 +111,18 @@ def test_hidden_size_with_a_narrow_last_column_block(d):
     _check_full(wl, T=1.3, chunk=128, vslab=768, grad_loss=0.8, label=f"narrow-d{d}")
 
 
+def test_largest_teacher_list():
+    """K = 1024, the largest supported teacher list, over a ragged vocabulary."""
+    wl = make_workload("tiny", N=300, d=64, V=3000, K=1024)
+    _check_full(wl, T=1.0, chunk=128, vslab=768, label="K=1024")
+
+
+def test_smallest_hidden_size_and_single_row():
+    """d = 8 (one 16-byte chunk per row) and N = 1."""
+    _check_full(make_workload("tiny", N=77, d=8, V=1000, K=5), T=1.0, label="d=8")
+    _check_full(make_workload("tiny", N=1, d=64, V=700, K=3), T=0.9, label="N=1")
+
+
 def test_single_teacher_entry():
     wl = make_workload("tiny", N=96, d=64, V=1000, K=1)
     _check_full(wl, T=1.0, chunk=64, label="K=1")
