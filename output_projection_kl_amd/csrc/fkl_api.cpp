@@ -78,7 +78,6 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->vslab = vslab;
   p->n_vt = ceil_div(s->V, kTile);
   const int64_t rbs = p->chunk_alloc / kTile;
-  p->fwd_splits = static_cast<int32_t>(ceil_div(kTargetBlocks, rbs));
 
   size_t off = 0;
   p->off_scalars = off;

@@ -27,7 +27,6 @@ struct Plan {
   int64_t chunk_alloc;  // chunk rounded up to 256
   int64_t vslab;        // vocabulary columns per backward pass, multiple of 256
   int64_t n_vt;         // ceil(V / 256): logits tiles along the vocabulary
-  int32_t fwd_splits;   // vocabulary splits of the forward sweep
   // workspace offsets (bytes)
   size_t off_scalars, off_negent, off_tidx, off_tp, off_partial, off_blocksum, fwd_bytes;
   size_t off_G, bwd_bytes;
