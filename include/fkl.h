@@ -66,7 +66,11 @@ typedef struct {
   int64_t V;     /* vocabulary size; V >= 1 */
   int32_t K;     /* cached teacher entries per row */
   float T;       /* temperature */
-  int32_t chunk; /* rows per pass; 0 = 4096. Results do not depend on it. */
+  int32_t chunk; /* rows per forward pass (and per backward pass when vslab
+                    is given); 0 = 4096. With vslab = 0 the backward takes
+                    passes of max(chunk, min(N, 4096)) rows: its memory is
+                    the gradient block, whose size vslab fixes. Results do
+                    not depend on it. */
   int32_t vslab; /* vocabulary columns per backward pass; 0 = chosen so that
                     a pass's gradient block holds about 64 Mi elements.
                     Rounded up to a multiple of 256. Results do not depend
@@ -118,12 +122,13 @@ typedef struct {
 
 /*
  * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
- * Pure host code. The sizes depend on chunk, vslab, K, d and flags, never on
- * N or on V beyond one slab: forward O(chunk * (K + 64)), backward
- * O(chunk * (vslab + K)), plus O(chunk * d) fp32 when a chunk's grad_h is
- * split along the vocabulary (few rows per chunk) or returned in bf16.
- * Shapes whose h chunk (chunk x d bf16), W slab (vslab x d bf16) or
- * gradient block (chunk x vslab bf16) would exceed 2 GiB return
+ * Pure host code. The sizes depend on the pass sizes, vslab, K, d and
+ * flags, on N only where N is below a pass, and on V only through one slab:
+ * with R the backward pass rows (chunk member), forward O(R * (K + 64)),
+ * backward O(R * (vslab + K)), plus O(R * d) fp32 when a pass's grad_h is
+ * split along the vocabulary (few rows per pass) or returned in bf16.
+ * Shapes whose h pass (R x d bf16), W slab (vslab x d bf16) or
+ * gradient block (R x vslab bf16) would exceed 2 GiB return
  * FKL_EUNSUPPORTED; the default vslab is capped to stay below.
  */
 fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t* bwd_bytes);

@@ -63,13 +63,24 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   if (s->N > 0 && chunk > s->N) chunk = s->N;
   p->chunk = chunk;
   p->chunk_alloc = round_up(chunk, kTile);
+  // Backward passes: the backward's memory is its gradient block (rows x
+  // vslab), so with the default slab it takes passes of at least
+  // min(N, kDefaultChunk) rows (a narrower slab keeps the block's size); an
+  // explicit vslab keeps the caller's chunk.
+  int64_t bchunk = chunk;
+  if (s->vslab == 0 && s->N > 0) {
+    const int64_t floor_rows = s->N < kDefaultChunk ? s->N : kDefaultChunk;
+    if (bchunk < floor_rows) bchunk = floor_rows;
+  }
+  p->bchunk = bchunk;
+  p->bchunk_alloc = round_up(bchunk, kTile);
   // The kernels address each operand view (an h chunk, a W slab, the
   // gradient block) through a buffer descriptor with a 32-bit byte size.
   const int64_t kMaxView = (int64_t(1) << 31) - 1;
-  if (p->chunk_alloc * s->d * 2 > kMaxView)
+  if (p->bchunk_alloc * s->d * 2 > kMaxView)
     return fail(FKL_EUNSUPPORTED, "chunk x d too large: a chunk of h must stay under 2 GiB");
-  const int64_t slab_cap = std::min(kMaxView / (2 * s->d), kMaxView / (2 * p->chunk_alloc)) / kTile * kTile;
-  int64_t vslab = s->vslab ? s->vslab : std::min<int64_t>(kDefaultSlabElems / p->chunk_alloc, slab_cap);
+  const int64_t slab_cap = std::min(kMaxView / (2 * s->d), kMaxView / (2 * p->bchunk_alloc)) / kTile * kTile;
+  int64_t vslab = s->vslab ? s->vslab : std::min<int64_t>(kDefaultSlabElems / p->bchunk_alloc, slab_cap);
   vslab = round_up(vslab < kTile ? kTile : vslab, kTile);
   const int64_t v_all = round_up(s->V, kTile);
   if (vslab > v_all) vslab = v_all;
@@ -83,12 +94,13 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_scalars = off;
   off += 256;
   p->off_negent = off;
-  off = align256(off + static_cast<size_t>(p->chunk_alloc) * 4);
+  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * 4);
   p->off_tidx = off;
-  // teacher lists hold K entries, or K + 1 with hard labels
-  off = align256(off + static_cast<size_t>(p->chunk_alloc) * (p->K + 1) * 4);
+  // teacher lists hold K entries, or K + 1 with hard labels (rows of the
+  // larger of the forward and backward passes)
+  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * (p->K + 1) * 4);
   p->off_tp = off;
-  off = align256(off + static_cast<size_t>(p->chunk_alloc) * (p->K + 1) * 4);
+  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * (p->K + 1) * 4);
   const size_t shared_end = off;
   // forward: split partials (two per row per workgroup) for up to (256 + rbs)
   // workgroups' rows, then block sums
@@ -97,23 +109,25 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_blocksum = off;
   off = align256(off + static_cast<size_t>(rbs) * 8);
   p->fwd_bytes = off;
-  // backward: the bf16 gradient block of chunk_alloc x vslab, then grad_h
-  // partial sums when a full chunk needs a vocabulary split (sized for a full
-  // chunk; a shorter last chunk takes at most as many partial rows)
+  // backward: the bf16 gradient block of bchunk_alloc x vslab, then grad_h
+  // partial sums when a full pass needs a vocabulary split (sized for a full
+  // pass; a shorter last pass takes at most as many partial rows)
   p->off_G = shared_end;
-  off = align256(shared_end + static_cast<size_t>(p->chunk_alloc) * p->vslab * 2);
+  off = align256(shared_end + static_cast<size_t>(p->bchunk_alloc) * p->vslab * 2);
   int splits = 1;
-  for (int64_t slab_w : {p->vslab, s->V - (ceil_div(s->V, p->vslab) - 1) * p->vslab}) {
-    const int sp = grad_h_splits(chunk, slab_w, s->d);
-    if (sp > splits) splits = sp;
+  if (!(s->flags & FKL_SKIP_GRAD_H)) {
+    for (int64_t slab_w : {p->vslab, s->V - (ceil_div(s->V, p->vslab) - 1) * p->vslab}) {
+      const int sp = grad_h_splits(bchunk, slab_w, s->d);
+      if (sp > splits) splits = sp;
+    }
   }
-  p->ghp_rows = splits > 1 ? splits * p->chunk_alloc : 0;
+  p->ghp_rows = splits > 1 ? splits * p->bchunk_alloc : 0;
   p->off_ghp = off;
   off = align256(off + static_cast<size_t>(p->ghp_rows) * s->d * 4);
   p->flags = s->flags;
   p->off_gh32 = off;
   if ((s->flags & FKL_GRAD_H_BF16) && !(s->flags & FKL_SKIP_GRAD_H))
-    off = align256(off + static_cast<size_t>(p->chunk_alloc) * s->d * 4);
+    off = align256(off + static_cast<size_t>(p->bchunk_alloc) * s->d * 4);
   p->bwd_bytes = off;
   return FKL_OK;
 }

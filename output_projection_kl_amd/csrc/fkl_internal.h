@@ -25,6 +25,8 @@ struct Plan {
   float T;
   int64_t chunk;        // rows per pass (<= N rounded up to 256 when N is small)
   int64_t chunk_alloc;  // chunk rounded up to 256
+  int64_t bchunk;       // rows per backward pass (>= chunk)
+  int64_t bchunk_alloc; // bchunk rounded up to 256
   int64_t vslab;        // vocabulary columns per backward pass, multiple of 256
   int64_t n_vt;         // ceil(V / 256): logits tiles along the vocabulary
   // workspace offsets (bytes)

@@ -717,8 +717,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   }
   const int64_t n_slabs = ceil_div(p.V, p.vslab);
   int64_t chunk_index = 0;
-  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk, ++chunk_index) {
-    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.bchunk, ++chunk_index) {
+    const int rows = static_cast<int>(p.N - c0 < p.bchunk ? p.N - c0 : p.bchunk);
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
@@ -732,7 +732,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
       const int splits = splits_for(rbs, nvt);
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, L, k2, p.T, tidx, tp, a.row_lse, a.mask, a.weight,
-                    a.grad_loss, sc, slab0, slab_w, p.chunk_alloc, G, nvt, rbs, splits};
+                    a.grad_loss, sc, slab0, slab_w, p.bchunk_alloc, G, nvt, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
@@ -748,7 +748,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       if (hsplits > 1 && hsplits * rows_written > p.ghp_rows)
         hsplits = static_cast<int>(p.ghp_rows / rows_written);
       if (hsplits < 1) hsplits = 1;
-      hp.A = Operand{G, p.chunk_alloc, rows_written, slab_w};
+      hp.A = Operand{G, p.bchunk_alloc, rows_written, slab_w};
       hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
       hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
       hp.ldc = p.d;
@@ -768,7 +768,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
         hp.c_split = 0;
       }
       GemmAccParams& wp = gp2.gw;
-      wp.A = Operand{G, p.chunk_alloc, slab_w, rows_written};
+      wp.A = Operand{G, p.bchunk_alloc, slab_w, rows_written};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
       wp.nk = static_cast<int32_t>(ceil_div(rows, kStageK));
       wp.C = a.grad_W + slab0 * p.d;

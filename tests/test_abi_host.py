@@ -207,3 +207,23 @@ def test_operand_views_stay_under_2_gib():
     s = fkl.make_shape(4096, 65536, 1 << 22, 10, chunk=256)         # default slab capped
     assert L.fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)) == 0
     assert b.value < (2 << 30)
+
+
+def test_backward_pass_rows_follow_gradient_block():
+    """With the default slab the backward takes passes of max(chunk, min(N, 4096))
+    rows, so a small forward chunk does not shrink the backward's passes or grow
+    its workspace; an explicit slab keeps chunk-row passes."""
+    _, b1024 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024)
+    _, b4096 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=4096)
+    assert b1024 == b4096
+    # gradient block rows x vslab bf16 follows chunk when vslab is given
+    # (grad_h skipped so that no vocabulary-split partial sums enter)
+    _, b_small = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024, vslab=4096,
+                                    flags=fkl.SKIP_GRAD_H)
+    _, b_big = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=4096, vslab=4096,
+                                  flags=fkl.SKIP_GRAD_H)
+    assert b_big - b_small >= (4096 - 1024) * 4096 * 2
+    # N below the pass floor: one pass of N rows
+    _, bn = fkl.workspace_size(300, 64, 1000, 5, 1.0, chunk=64)
+    _, bn2 = fkl.workspace_size(300, 64, 1000, 5, 1.0, chunk=300)
+    assert bn == bn2
