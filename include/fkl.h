@@ -68,7 +68,7 @@ typedef struct {
   float T;       /* temperature */
   int32_t chunk; /* rows per forward pass (and per backward pass when vslab
                     is given); 0 = 4096. With vslab = 0 the backward takes
-                    passes of max(chunk, min(N, 4096)) rows: its memory is
+                    passes of max(chunk, min(N, 8192)) rows: its memory is
                     the gradient block, whose size vslab fixes. Results do
                     not depend on it. */
   int32_t vslab; /* vocabulary columns per backward pass; 0 = chosen so that

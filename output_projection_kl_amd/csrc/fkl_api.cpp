@@ -65,11 +65,11 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->chunk_alloc = round_up(chunk, kTile);
   // Backward passes: the backward's memory is its gradient block (rows x
   // vslab), so with the default slab it takes passes of at least
-  // min(N, kDefaultChunk) rows (a narrower slab keeps the block's size); an
+  // min(N, kBwdPassRows) rows (a narrower slab keeps the block's size); an
   // explicit vslab keeps the caller's chunk.
   int64_t bchunk = chunk;
   if (s->vslab == 0 && s->N > 0) {
-    const int64_t floor_rows = s->N < kDefaultChunk ? s->N : kDefaultChunk;
+    const int64_t floor_rows = s->N < kBwdPassRows ? s->N : kBwdPassRows;
     if (bchunk < floor_rows) bchunk = floor_rows;
   }
   p->bchunk = bchunk;

@@ -173,7 +173,7 @@ def test_backward_flags_checked_on_the_host():
 def test_bf16_grad_h_adds_an_fp32_accumulator_to_the_workspace():
     _, b0 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096)
     _, b1 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096, flags=fkl.GRAD_H_BF16)
-    assert b1 - b0 == 4096 * 2880 * 4
+    assert b1 - b0 == 8192 * 2880 * 4      # one backward pass of 8192 rows
     _, b2 = fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096,
                                flags=fkl.GRAD_H_BF16 | fkl.SKIP_GRAD_H)
     assert b2 == b0
@@ -210,7 +210,7 @@ def test_operand_views_stay_under_2_gib():
 
 
 def test_backward_pass_rows_follow_gradient_block():
-    """With the default slab the backward takes passes of max(chunk, min(N, 4096))
+    """With the default slab the backward takes passes of max(chunk, min(N, 8192))
     rows, so a small forward chunk does not shrink the backward's passes or grow
     its workspace; an explicit slab keeps chunk-row passes."""
     _, b1024 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024)

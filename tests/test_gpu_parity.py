@@ -196,7 +196,7 @@ def test_chunk_invariance():
     dev = _dev()
     wl = make_workload("tiny", seed_offset=5, mask="random25")
     h, W, ti, tl, m = _upload(wl, dev)
-    # with vslab = 0 the backward takes passes of max(chunk, min(N, 4096))
+    # with vslab = 0 the backward takes passes of max(chunk, min(N, 8192))
     # rows; an explicit vslab keeps chunk-row backward passes
     outs = [_run_gpu(h, W, ti, tl, m, 1.0, chunk=c) for c in (64, 100, 256)]
     outs += [_run_gpu(h, W, ti, tl, m, 1.0, chunk=c, vslab=1024) for c in (64, 100)]
