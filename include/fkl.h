@@ -185,15 +185,24 @@ fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx,
  * Rows are processed `chunk` at a time (0: enough rows for a 512 MiB fp32
  * logits block, at least 256): the logits of a chunk are formed in the
  * workspace, chunk (rounded up to 256) x V (rounded up to 256) fp32, and the
- * top-K of each row is selected exactly. Constraints: d a multiple of 8
- * (<= 65536), 1 <= K <= min(V, 1024); h and W 16-byte aligned; the
- * workspace 256-byte aligned. Argument errors return before any HIP call.
+ * top-K of each row is selected exactly. Each row is normally read once: a
+ * threshold taken from a sample of the row keeps a few times K of its logits
+ * (at most about 2048 expected) in on-chip memory, where the selection runs.
+ * A threshold that keeps fewer than K or too many logits is moved and the row
+ * read again; after three tries the row is selected over the whole row
+ * (FKL_TOPK_DIRECT asks for that route on every row). Both routes return the
+ * same result. Constraints: d a multiple of 8 (<= 65536),
+ * 1 <= K <= min(V, 1024); h and W 16-byte aligned; the workspace 256-byte
+ * aligned. Argument errors return before any HIP call.
  */
 typedef struct {
   int64_t N, d, V;
   int32_t K;
-  int32_t chunk;  /* rows per pass; 0 = default */
+  int32_t chunk;   /* rows per pass; 0 = default */
+  uint32_t flags;  /* FKL_TOPK_* below; 0 = default */
 } fkl_topk_shape;
+
+#define FKL_TOPK_DIRECT 0x1u /* select over the whole row, no sampled threshold */
 
 /* Workspace bytes of fkl_topk for this shape (host only). */
 fkl_status fkl_topk_workspace_size(const fkl_topk_shape* shape, size_t* bytes);

@@ -115,7 +115,11 @@ class TopkShape(ctypes.Structure):
         ("V", ctypes.c_int64),
         ("K", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+TOPK_DIRECT = 0x1
 
 
 def library_path() -> str:
@@ -373,18 +377,19 @@ def validate_teacher(t_idx, t_logit, V: int) -> int:
     return int(bad.item())
 
 
-def topk_workspace_size(N, d, V, K, chunk=0) -> int:
+def topk_workspace_size(N, d, V, K, chunk=0, flags=0) -> int:
     """Workspace bytes of topk() for this shape."""
-    s = TopkShape(N, d, V, K, chunk)
+    s = TopkShape(N, d, V, K, chunk, flags)
     b = ctypes.c_size_t(0)
     _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
     return b.value
 
 
-def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None):
+def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None, direct: bool = False):
     """Offline teacher cache: per row of h (bf16 [N,d]), the K largest logits of
-    h W^T (W bf16 [V,d]), descending, ties by the lower index.
-    Returns (t_idx int32 [N,K], t_logit fp32 [N,K])."""
+    h W^T (W bf16 [V,d]), descending, ties by the lower index. direct=True
+    selects over every whole row instead of from a sampled threshold (same
+    result). Returns (t_idx int32 [N,K], t_logit fp32 [N,K])."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -392,7 +397,7 @@ def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None)
     V = W.shape[0]
     _need(h, "h", torch.bfloat16, (N, d))
     _need(W, "W", torch.bfloat16, (V, d))
-    s = TopkShape(N, d, V, K, chunk)
+    s = TopkShape(N, d, V, K, chunk, TOPK_DIRECT if direct else 0)
     b = ctypes.c_size_t(0)
     _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
     ws = _workspace(b.value, h.device, workspace)

@@ -144,10 +144,12 @@ fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
   if (s->K > 1024) return fail(FKL_EUNSUPPORTED, "K must be <= 1024");
   if (s->K > s->V) return fail(FKL_EINVAL, "K must be <= V");
   if (s->chunk < 0) return fail(FKL_EINVAL, "chunk must be >= 0");
+  if (s->flags & ~static_cast<uint32_t>(FKL_TOPK_DIRECT)) return fail(FKL_EINVAL, "unknown fkl_topk_shape flag");
   p->N = s->N;
   p->d = s->d;
   p->V = s->V;
   p->K = s->K;
+  p->flags = s->flags;
   p->ld = round_up(s->V, kTile);
   int64_t chunk = s->chunk;
   if (chunk == 0) {

@@ -103,6 +103,7 @@ struct TopkPlan {
   int64_t chunk;  // rows per pass
   int64_t ld;     // row stride of the logits block (V rounded up to 256)
   size_t bytes;   // workspace: chunk rounded up to 256 rows x ld fp32
+  uint32_t flags; // FKL_TOPK_* options
 };
 
 constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logits block (512 MiB)

@@ -132,14 +132,17 @@ def test_topk_argument_errors_before_any_device_work():
     L = fkl.lib()
     vp = ctypes.c_void_p
 
-    def call(N=16, d=64, V=100, K=5, chunk=0, h=8192, W=16384, ti=4096, tl=4096, ws=1 << 20, ws_bytes=1 << 30):
-        s = fkl.TopkShape(N, d, V, K, chunk)
+    def call(N=16, d=64, V=100, K=5, chunk=0, h=8192, W=16384, ti=4096, tl=4096, ws=1 << 20, ws_bytes=1 << 30,
+             flags=0):
+        s = fkl.TopkShape(N, d, V, K, chunk, flags)
         return L.fkl_topk(ctypes.byref(s), vp(h), vp(W), vp(ti), vp(tl), vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
     assert call(d=12) == 1
     assert call(K=0) == 1
     assert call(K=101) == 1       # K > V
     assert call(K=2000, V=5000) == 5
     assert call(chunk=-1) == 1
+    assert call(flags=0x2) == 1   # unknown flag
+    assert call(flags=fkl.TOPK_DIRECT, ws_bytes=16) == 2  # the whole-row route is a known flag
     assert call(h=0) == 1
     assert call(W=8) == 1         # misaligned
     assert call(ti=2) == 1

@@ -94,30 +94,78 @@ def test_topk_integer_logits_exact_with_ties(K):
     _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
 
 
-@pytest.mark.parametrize("V", [500, 5000])
-def test_topk_all_equal_logits(V):
-    """W = 0: every logit is 0; the K lowest indices in order (V = 5000 puts more
-    equal keys in one first-digit bin than the LDS candidate buffer holds)."""
+@pytest.mark.parametrize("direct", [False, True])
+@pytest.mark.parametrize("V", [500, 5000, 20000])
+def test_topk_all_equal_logits(V, direct):
+    """W = 0: every logit is 0; the K lowest indices in order (V = 5000 and 20000
+    put more equal keys in one first-digit bin than the LDS candidate buffer
+    holds when the whole row is selected)."""
     dev = _dev()
     h = torch.ones((9, 16), dtype=torch.bfloat16, device=dev)
     W = torch.zeros((V, 16), dtype=torch.bfloat16, device=dev)
-    ti, tl = fkl.topk(h, W, 37)
+    ti, tl = fkl.topk(h, W, 37, direct=direct)
     torch.cuda.synchronize()
     assert (ti.cpu().numpy() == np.arange(37)[None, :]).all()
     assert (tl.cpu().numpy() == 0).all()
 
 
-def test_topk_integer_logits_exact_large_boundary_bin():
+@pytest.mark.parametrize("direct", [False, True])
+def test_topk_integer_logits_exact_large_boundary_bin(direct):
     """Few distinct integer logits over a wide vocabulary: the boundary bin holds
-    thousands of keys, so selection continues over the row; still exact."""
+    thousands of keys (over the whole row, selection continues over the row);
+    still exact."""
     dev = _dev()
     rng = np.random.default_rng(77)
     N, d, V, K = 24, 16, 30000, 300
     h, hf = _to_dev_bf16(rng.integers(-1, 2, size=(N, d)).astype(np.float32), dev)
     W, Wf = _to_dev_bf16(rng.integers(-1, 2, size=(V, d)).astype(np.float32), dev)
+    ti, tl = fkl.topk(h, W, K, direct=direct)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
+
+
+@pytest.mark.parametrize("N,d,V,K", [
+    (200, 64, 5000, 7),         # just above the candidate buffer: sampled threshold
+    (130, 64, 4096, 100),       # fits the buffer: every key is a candidate
+    (64, 128, 60000, 1024),     # largest K: the threshold keeps about 2048 keys
+    (96, 64, 128256, 100),      # the large-head vocabulary
+])
+def test_topk_sampled_threshold_matches_whole_row_selection(N, d, V, K):
+    """The default route (threshold from a sample, selection among the keys it
+    keeps) and the whole-row route return identical outputs."""
+    dev = _dev()
+    rng = np.random.default_rng(N + V + K)
+    h, _ = _to_dev_bf16(rng.standard_normal((N, d)), dev)
+    W, _ = _to_dev_bf16(rng.standard_normal((V, d)) / np.sqrt(d), dev)
+    print(f"[topk-routes] N={N} d={d} V={V} K={K}", flush=True)
+    a_i, a_l = fkl.topk(h, W, K)
+    b_i, b_l = fkl.topk(h, W, K, direct=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_i, b_i)
+    assert torch.equal(a_l, b_l)
+
+
+def test_topk_threshold_that_keeps_too_few_keys_is_retried():
+    """Logits that are large only at the positions the threshold sample reads:
+    the first sampled threshold then keeps fewer than K keys and a lower one is
+    taken. Positions whose logits are 1 must come first, by index."""
+    dev = _dev()
+    N, d, V, K = 8, 16, 30000, 1024
+    # every position of the form 468 * b + i (i < 32) is high: this covers the
+    # sample's runs for V = 30000 (runs of 32 starting at b * V / 64, rounded
+    # down to a multiple of 4)
+    starts = (np.arange(64) * V // 64) & ~3
+    hi = np.unique((starts[:, None] + np.arange(32)[None, :]).ravel())
+    Wf = np.zeros((V, d), dtype=np.float32)
+    Wf[hi, 0] = 1.0
+    hf = np.zeros((N, d), dtype=np.float32)
+    hf[:, 0] = 1.0
+    h, hf = _to_dev_bf16(hf, dev)
+    W, Wf = _to_dev_bf16(Wf, dev)
     ti, tl = fkl.topk(h, W, K)
     torch.cuda.synchronize()
     _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
+    assert (ti.cpu().numpy() == hi[:K][None, :]).all()
 
 
 def test_topk_feeds_the_loss():
