@@ -157,10 +157,14 @@ def test_fullsize_3b_full_forward_and_grad_W_rows():
     e_loss = abs(loss - r_loss) / abs(r_loss)
     e_lse = float(np.abs(lse.cpu().numpy() - r_lse).max())
     e_kl = float(np.abs(kl.cpu().numpy() - r_kl).max())
-    # default vocabulary slab: 64 Mi gradient elements per chunk (65536 columns at chunk 1024)
-    slab = (64 << 20) // ((wl.chunk + 255) // 256 * 256)
+    # default backward shape: passes of max(chunk, min(N, 8192)) rows and vocabulary
+    # slabs of 64 Mi / rows columns (8192 here)
+    pass_rows = (max(wl.chunk, min(wl.N, 8192)) + 255) // 256 * 256
+    slab = (64 << 20) // pass_rows
+    edges = [slab, 2 * slab]
     hits, counts = np.unique(wl.t_idx_np, return_counts=True)
-    vrows = {0, 1, wl.V - 1, wl.V - 2, slab - 1, slab, 2 * slab - 1, int(hits[np.argmax(counts)])}
+    vrows = {0, 1, wl.V - 1, wl.V - 2, int(hits[np.argmax(counts)])}
+    vrows |= {e + o for e in edges for o in (-1, 0)}
     rng = np.random.default_rng(wl.seed)
     vrows |= set(int(v) for v in rng.choice(hits, 8, replace=False))
     vrows |= set(int(v) for v in rng.choice(wl.V, 8, replace=False))
