@@ -138,6 +138,30 @@ def test_zipf_teacher_reduced_vocab():
     _check_full(wl, chunk=256, vslab=2048, label="zipf")
 
 
+def test_largest_hidden_size():
+    """d = 65536, the largest supported hidden size (2048 contraction stages per tile)."""
+    wl = make_workload("tiny", N=70, d=65536, V=300, K=8)
+    _check_full(wl, T=1.0, label="d=65536")
+
+
+def test_single_word_vocabulary():
+    """V = K = 1: student and teacher are both certain of the only token, so the
+    loss and both gradients vanish. The gradient block holds bf16(c q) - c p with
+    c = T / n, so each of its entries is within c 2^-8 of zero, which bounds the
+    gradients: |grad_h| <= c 2^-8 max|W| and |grad_W| <= T 2^-8 max|h|."""
+    dev = _dev()
+    wl = make_workload("tiny", N=33, d=64, V=1, K=1)
+    h, W, ti, tl, m = _upload(wl, dev)
+    T = 1.0
+    loss, lse, kl, gh, gW = _run_gpu(h, W, ti, tl, m, T)
+    r_lse = oracle.forward(wl.h(), wl.W(), wl.t_idx, wl.t_logit, T)[1]
+    assert abs(loss) <= 1e-6 and np.abs(kl).max() <= 1e-6
+    assert np.abs(lse - r_lse).max() <= LSE_ATOL
+    c = T / wl.N
+    assert np.abs(gh).max() <= 1.01 * c * 2.0**-8 * np.abs(wl.W()).max()
+    assert np.abs(gW).max() <= 1.01 * T * 2.0**-8 * np.abs(wl.h()).max()
+
+
 def test_empty_rows():
     dev = _dev()
     d, V, K = 64, 300, 5
