@@ -15,9 +15,10 @@
 //   k_accumulate    fixed-order fp64 running loss
 // Backward, per chunk and vocabulary slab (same section: each chunk's logits
 // are recomputed rather than stored):
-//   k_bwd_g         logits tile again -> G = c (exp(s - lse) - p~) in
-//                   registers -> bf16 transposed gradient block G^T in the
-//                   workspace (the teacher entries subtracted in LDS)
+//   k_bwd_g         logits tile again -> fp32 through LDS -> G = c (exp(s - lse)
+//                   - p~) formed in fp32 by the row owners (teacher entries
+//                   subtracted before rounding) -> bf16 row-major gradient
+//                   block G in the workspace
 //   k_bwd_grads     grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk
 //                   in one launch (grad_h tiles optionally split along the
 //                   vocabulary into partial sums)
@@ -415,27 +416,21 @@ struct BwdGParams {
   const Scalars* sc;
   int64_t slab0;
   int32_t slab_w;
-  int64_t ld_g;  // row stride of G^T (chunk_alloc)
-  uint16_t* G;   // G^T [vslab][chunk_alloc]
+  int64_t ld_g;  // row stride of G (vslab)
+  uint16_t* G;   // G [pass rows][vslab], row-major
   int32_t n_vt;
   int32_t rbs, splits;  // splits <= n_vt
 };
 
-// LDS of the gradient-block kernel: the operand ring during the contraction,
-// then the tile's G values as bf16 stored column-major (kGtLd rows per
-// column, padded), plus the per-row constants of the block's 256 rows.
-constexpr int kGtLd = kTile + 8;
-constexpr int kGtStageBytes = kTile * kGtLd * 2;
-constexpr int kBwdGConstOff = kGtStageBytes > MainCfg::kLdsBytes ? kGtStageBytes : MainCfg::kLdsBytes;
-constexpr int kBwdGLdsBytes = kBwdGConstOff + 2 * kTile * 4;
-
-// One 256 x 256 tile of G = c_r (softmax(z/T) - p~) per step: each wave turns
-// its accumulators into c_r * exp2(z log2(e)/T - lse_r log2(e)) in registers,
-// stores them as bf16 into a column-major LDS tile, the row owners subtract
-// c_r p_k at the teacher entries inside the tile, and the tile is written to
-// the transposed gradient block G^T [vslab][chunk_alloc] with 16-byte stores.
+// One 256 x 256 tile of G = c_r (softmax(z/T) - p~) per step. The logits tile
+// is staged in fp32 through LDS one 128-column half at a time (as in the
+// forward); the thread that owns a row's 64-column quarter forms
+// c_r (exp2(z log2(e)/T - lse_r log2(e)) - p_k) in fp32, subtracting p_k at the
+// teacher entries it meets on the row's sorted list, and rounds once to bf16;
+// the half tile then goes to the row-major gradient block G [pass rows][vslab]
+// with coalesced 16-byte stores.
 __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
-  __shared__ __align__(16) char lds[kBwdGLdsBytes];
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -460,75 +455,67 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
     c = (w > 0.f && wsum > 0.0) ? static_cast<float>(static_cast<double>(g) * P.T * w / wsum) : 0.f;
     lse2 = P.row_lse[grow] * kLog2e;
   }
-  float* row_lse2 = reinterpret_cast<float*>(lds + kBwdGConstOff);
-  float* row_c = row_lse2 + kTile;
-  if (sub == 0) {
-    row_lse2[rloc] = lse2;
-    row_c[rloc] = c;
-  }
   Cursor cur;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
-           P.K, static_cast<int>(P.slab0) + vt0 * kTile + sub * 128, c != 0.f && vt0 < vt1);
+           P.K, static_cast<int>(P.slab0) + vt0 * kTile, c != 0.f && vt0 < vt1);
 
   const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
   const int nk = static_cast<int>((P.d + kStageK - 1) / kStageK);
-  uint16_t* gt = reinterpret_cast<uint16_t*>(lds);
-  const int64_t slab_end = P.slab0 + P.slab_w;
+  float* stage = reinterpret_cast<float*>(lds);
+  const int slab_end = static_cast<int>(P.slab0 + P.slab_w);
 
   for (int vt = vt0; vt < vt1; ++vt) {
     f32x16 acc[4][kNBW];
     zero_acc(acc);
-    const int64_t vbase = P.slab0 + static_cast<int64_t>(vt) * kTile;
-    // (the mainloop's opening barrier also publishes row_lse2 / row_c)
-    gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc,
-                                           lds);
-    // Registers -> G values -> bf16 column-major LDS tile. Elements i = 4j..4j+3
-    // of a block are 4 consecutive rows of one column: one 8-byte store.
+    const int vbase = static_cast<int>(P.slab0) + vt * kTile;
+    gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc, lds);
+    for (int half = 0; half < 2; ++half) {
+      if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
+      __syncthreads();
+      const int c0 = vbase + half * 128;
+      const int c1 = c0 + sub * 64;
+      // This thread's 64 fp32 logits; its 64 bf16 results go back over the
+      // first half of the same 256 bytes.
+      float* sr = stage + rloc * kStageLd + sub * 64;
+      bf16x8* so = reinterpret_cast<bf16x8*>(sr);
+      while (cur.cur() < c1) cur.next();  // entries of the other quarter before this one
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+      for (int c8 = 0; c8 < 64; c8 += 8) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(sr + c8);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sr + c8 + 4);
+        float q[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r4 = wm * 128 + acc_row(mb, 4 * j, lane);
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r4);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(row_c + r4);
+        for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(e < 4 ? x0[e] : x1[e - 4], P.k2, -lse2));
+        if (cur.cur() < c1 + c8 + 8) {  // teacher entries among these 8 columns
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb) {
-          const int col = wn * (kNBW * 32) + acc_col(nb, lane);
-          const bool col_ok = vbase + col < slab_end;
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = acc[mb][nb][4 * j + e];
-            const float gv = c4[e] * __builtin_amdgcn_exp2f(fmaf(x, P.k2, -l4[e]));
-            o[e] = static_cast<__bf16>((col_ok && c4[e] != 0.f) ? gv : 0.f);
+          for (int e = 0; e < 8; ++e) {
+            if (cur.cur() == c1 + c8 + e) {
+              q[e] -= cur.cp();
+              cur.next();
+            }
           }
-          *reinterpret_cast<bf16x4*>(gt + col * kGtLd + r4) = o;
         }
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(c1 + c8 + e < slab_end ? c * q[e] : 0.f);
+        so[c8 / 8] = o;
       }
-    }
-    __syncthreads();
-    // Row owners: subtract c * p at the teacher entries of their half of the tile.
-    {
-      const int c_lo = static_cast<int>(vbase) + sub * 128;
-      while (cur.cur() < c_lo + 128) {
-        const int e = cur.cur();
-        __bf16* q = reinterpret_cast<__bf16*>(gt + (e - static_cast<int>(vbase)) * kGtLd + rloc);
-        *q = static_cast<__bf16>(static_cast<float>(*q) - c * cur.cp());
-        cur.next();
+      while (cur.cur() < c0 + 128) cur.next();  // the rest of this half tile
+      __syncthreads();
+      // Coalesced copy of the 256 x 128 bf16 half tile: 16 lanes per row, each
+      // 16 bytes (the row's two quarters sit 256 bytes apart in LDS).
+      const char* sb = reinterpret_cast<const char*>(stage);
+      uint16_t* gdst = P.G + static_cast<int64_t>(rb) * kTile * P.ld_g + vt * kTile + half * 128;
+#pragma unroll
+      for (int i = 0; i < (kTile * 16) / kBlockThreads; ++i) {
+        const int q = tid + i * kBlockThreads;
+        const int r = q >> 4;
+        const int j = q & 15;
+        *reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(r) * P.ld_g + j * 8) =
+            *reinterpret_cast<const u32x4*>(sb + r * (kStageLd * 4) + (j < 8 ? j * 16 : 256 + (j - 8) * 16));
       }
-      // skip the other half's entries up to the next tile's range
-      while (cur.cur() < c_lo + 256) cur.next();
-    }
-    __syncthreads();
-    uint16_t* gdst = P.G + (static_cast<int64_t>(vt) * kTile) * P.ld_g + static_cast<int64_t>(rb) * kTile;
-#pragma unroll 4
-    for (int i = 0; i < (kTile * kTile / 8) / kBlockThreads; ++i) {
-      const int q = tid + i * kBlockThreads;
-      const int cc = q >> 5;
-      const int r8 = (q & 31) * 8;
-      *reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(cc) * P.ld_g + r8) =
-          *reinterpret_cast<const u32x4*>(gt + cc * kGtLd + r8);
+      __syncthreads();
     }
   }
 }
@@ -550,9 +537,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int w = blockIdx.x;
   if (w < P.h_tiles) {
-    gemm_acc_tile<true, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
+    gemm_acc_tile<false, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
   } else {
-    gemm_acc_tile<false, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
+    gemm_acc_tile<true, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
   }
 }
 
@@ -732,7 +719,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
       const int splits = splits_for(rbs, nvt);
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, L, k2, p.T, tidx, tp, a.row_lse, a.mask, a.weight,
-                    a.grad_loss, sc, slab0, slab_w, p.bchunk_alloc, G, nvt, rbs, splits};
+                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, rbs, splits};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
@@ -743,12 +730,12 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       // grad_W[slab0 : slab0 + slab_w] (+)= G[:rows, :slab_w]^T @ h[c0 : c0 + rows], one launch.
       GradParams gp2;
       GemmAccParams& hp = gp2.gh;
-      const int64_t rows_written = static_cast<int64_t>(rbs) * kTile;  // G^T columns this chunk wrote
+      const int64_t rows_written = static_cast<int64_t>(rbs) * kTile;  // G rows this pass wrote
       int hsplits = want_h ? grad_h_splits(rows, slab_w, p.d) : 1;
       if (hsplits > 1 && hsplits * rows_written > p.ghp_rows)
         hsplits = static_cast<int>(p.ghp_rows / rows_written);
       if (hsplits < 1) hsplits = 1;
-      hp.A = Operand{G, p.bchunk_alloc, rows_written, slab_w};
+      hp.A = Operand{G, p.vslab, rows_written, slab_w};
       hp.B = Operand{a.W + slab0 * p.d, p.d, p.d, slab_w};
       hp.nk = static_cast<int32_t>(ceil_div(slab_w, kStageK));
       hp.ldc = p.d;
@@ -768,7 +755,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
         hp.c_split = 0;
       }
       GemmAccParams& wp = gp2.gw;
-      wp.A = Operand{G, p.bchunk_alloc, slab_w, rows_written};
+      wp.A = Operand{G, p.vslab, slab_w, rows_written};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
       wp.nk = static_cast<int32_t>(ceil_div(rows, kStageK));
       wp.C = a.grad_W + slab0 * p.d;
