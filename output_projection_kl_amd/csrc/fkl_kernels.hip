@@ -314,15 +314,20 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
         float s = 0.f;
         const float off = m2 == -INFINITY ? 0.f : m2;
         if (nvalid == 64) {
-#pragma unroll 8
+          // four independent chains (columns c mod 4), summed in a fixed order
+          f32x4 mx4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
           for (int c = 0; c < 64; c += 4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(sr + c);
-            mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            s += __builtin_amdgcn_exp2f(fmaf(x[0], P.k2, -off));
-            s += __builtin_amdgcn_exp2f(fmaf(x[1], P.k2, -off));
-            s += __builtin_amdgcn_exp2f(fmaf(x[2], P.k2, -off));
-            s += __builtin_amdgcn_exp2f(fmaf(x[3], P.k2, -off));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              mx4[e] = fmaxf(mx4[e], x[e]);
+              s4[e] += __builtin_amdgcn_exp2f(fmaf(x[e], P.k2, -off));
+            }
           }
+          mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+          s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         } else {
           for (int c = 0; c < nvalid; ++c) {
             mx = fmaxf(mx, sr[c]);
