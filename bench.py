@@ -336,13 +336,24 @@ def main() -> int:
         fkl.trace_enable(True)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    # per-step events: before the forward, between forward and backward, after
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        marks[i][0].record()
+        fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, mask=wl.mask, chunk=wl.chunk, workspace=ws,
+                    loss=loss, row_lse=row_lse)
+        marks[i][1].record()
+        fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, row_lse, T=wl.T, mask=wl.mask, chunk=wl.chunk,
+                     workspace=ws, grad_h=grad_h, grad_W=grad_W)
+        marks[i][2].record()
     stop.record()
     torch.cuda.synchronize()
+    fwd_ms = sorted(m[0].elapsed_time(m[1]) for m in marks)
+    bwd_ms = sorted(m[1].elapsed_time(m[2]) for m in marks)
+    step_ms = sorted(m[0].elapsed_time(m[2]) for m in marks)
     wall = time.perf_counter() - t_wall
     if trace:
         fkl.trace_enable(False)
@@ -398,6 +409,12 @@ def main() -> int:
                    "mask": "packed: last token of each of 8 documents" if wl.mask is not None else "none"},
         "tflops": round(tflops, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 3),
+        "step_ms_min": round(step_ms[0], 3),
+        "forward": {"ms_median": round(fwd_ms[len(fwd_ms) // 2], 3),
+                    "tflops": round(2.0 * wl.N * wl.d * wl.V / (fwd_ms[len(fwd_ms) // 2] / 1e3) / 1e12, 1)},
+        "backward": {"ms_median": round(bwd_ms[len(bwd_ms) // 2], 3),
+                     "tflops": round(6.0 * wl.N * wl.d * wl.V / (bwd_ms[len(bwd_ms) // 2] / 1e3) / 1e12, 1)},
         "peak_gib": round(peak / 2**30, 3),
         "extra_gib": round((peak - in_out_bytes) / 2**30, 3),
         "inputs_outputs_gib": round(in_out_bytes / 2**30, 3),
