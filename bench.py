@@ -189,6 +189,29 @@ def cpu_baseline(wl, rows: int):
     }
 
 
+def vendor_gemm_context(torch, wl, dev) -> dict:
+    """Attainable-peak context: the vendor library's bf16 GEMM (torch.mm, which
+    runs hipBLASLt) on one forward chunk's logits shape, chunk x d times d x V.
+    Not part of the loss; reported beside it."""
+    rows = min(wl.chunk, wl.N)
+    a = wl.h[:rows]
+    out = torch.empty((rows, wl.V), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.mm(a, wl.W.t(), out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, wl.W.t(), out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del out
+    return {"op": f"torch.mm bf16 [{rows} x {wl.d}] x [{wl.d} x {wl.V}] -> bf16", "ms": round(ms, 3),
+            "tflops": round(2.0 * rows * wl.d * wl.V / (ms / 1e3) / 1e12, 1)}
+
+
 def bench_builder(args, torch, fkl, make_device_workload, dev) -> int:
     """fkl_topk on the large-head shape: N=16384 rows, d=4096, V=128256, K=100,
     teacher head W_t = W + 0.1 N(0, 1/d). One step = one full cache build."""
@@ -254,6 +277,8 @@ def main() -> int:
                     help="synthetic workload (default: the GPT-OSS-20B-like head)")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-context", action="store_true",
+                    help="skip the vendor bf16 GEMM timing reported as context")
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM counters)")
@@ -423,6 +448,8 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_gemm_context:
+        out["vendor_gemm_context"] = vendor_gemm_context(torch, wl, dev)
     if not args.no_cpu_baseline:
         print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
