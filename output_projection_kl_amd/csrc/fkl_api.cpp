@@ -103,11 +103,11 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   off = align256(off + static_cast<size_t>(p->bchunk_alloc) * (p->K + 1) * 4);
   const size_t shared_end = off;
   // forward: split partials (two per row per workgroup) for up to (256 + rbs)
-  // workgroups' rows, then block sums
+  // workgroups' rows, then one fp64 KL sum per kCombineRows rows
   p->off_partial = off;
   off = align256(off + static_cast<size_t>(kTargetBlocks + rbs) * 2 * kTile * 16);
   p->off_blocksum = off;
-  off = align256(off + static_cast<size_t>(rbs) * 8);
+  off = align256(off + static_cast<size_t>(p->chunk_alloc / kCombineRows) * 8);
   p->fwd_bytes = off;
   // backward: the bf16 gradient block of bchunk_alloc x vslab, then grad_h
   // partial sums when a full pass needs a vocabulary split (sized for a full

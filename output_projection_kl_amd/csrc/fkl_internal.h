@@ -41,6 +41,8 @@ struct Plan {
   size_t off_gh32;  // fp32 [chunk_alloc][d] grad_h accumulator when grad_h is bf16
 };
 
+constexpr int kCombineRows = 16;  // rows per workgroup of the forward's split merge
+
 constexpr int kMaxGradHSplits = 8;
 
 // Vocabulary splits for the grad_h tiles of one backward launch (rows of the

@@ -362,8 +362,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
   P.partial[static_cast<int64_t>(split * 2 + sub) * ld + row] = f32x4{m2, se, gz, 0.f};
 }
 
-// One thread per row of the chunk: merge the split statistics.
-__global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int parts,
+// Sixteen lanes per row of the chunk merge the split statistics (each lane a
+// strided subset of the parts, then a fixed-order reduction across the 16):
+// row_lse, row_kl, and one fp64 KL sum per workgroup of kCombineRows rows.
+
+__global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ partial, int parts, int64_t ld,
                                                      int rows, int64_t r0,
                                                      const float* __restrict__ negent,
                                                      const uint8_t* __restrict__ mask,
@@ -371,19 +374,31 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
                                                      float* __restrict__ row_lse,
                                                      float* __restrict__ row_kl,
                                                      double* __restrict__ block_sum) {
-  __shared__ double red[256];
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  const int ld = gridDim.x * 256;
-  double kl_d = 0.0;
-  if (r < rows) {
-    float M = -INFINITY;
-    for (int s = 0; s < parts; ++s) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
-    float sum = 0.f, gz = 0.f;
-    for (int s = 0; s < parts; ++s) {
+  __shared__ double red[kCombineRows];
+  const int l16 = threadIdx.x & 15;
+  const int rl = threadIdx.x >> 4;
+  const int r = blockIdx.x * kCombineRows + rl;
+  const bool ok = r < rows;
+  float M = -INFINITY;
+  if (ok)
+    for (int s = l16; s < parts; s += 16) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+  float sum = 0.f, gz = 0.f;
+  if (ok) {
+    for (int s = l16; s < parts; s += 16) {
       const f32x4 pr = partial[static_cast<int64_t>(s) * ld + r];
       if (pr[1] > 0.f) sum += pr[1] * exp2f(pr[0] - M);
       gz += pr[2];
     }
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o, 16);
+    gz += __shfl_xor(gz, o, 16);
+  }
+  double kl_d = 0.0;
+  if (ok && l16 == 0) {
     const float lse = (M + log2f(sum)) * kLn2;
     const float kl = negent[r] - gz * invT + lse;
     const bool valid = !mask || mask[r0 + r] != 0;
@@ -392,13 +407,13 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
     if (row_kl) row_kl[r0 + r] = w > 0.f ? kl : 0.f;
     kl_d = w > 0.f ? static_cast<double>(w) * kl : 0.0;
   }
-  red[threadIdx.x] = kl_d;
+  if (l16 == 0) red[rl] = kl_d;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kCombineRows; ++i) t += red[i];
+    block_sum[blockIdx.x] = t;
   }
-  if (threadIdx.x == 0) block_sum[blockIdx.x] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -671,12 +686,14 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
                     2.0 * rows * dd + 2.0 * p.V * dd + 8.0 * rows * p.K + 16.0 * splits * rows);
       hipLaunchKernelGGL(k_fwd_sweep, dim3(rbs * splits), dim3(kBlockThreads), 0, st, fp);
     }
+    const int cblocks = static_cast<int>(ceil_div(rows, kCombineRows));
     {
       TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
-      hipLaunchKernelGGL(k_fwd_combine, dim3(rbs), dim3(256), 0, st, partial, 2 * splits, rows, c0, negent,
-                         a.mask, a.weight, invT, a.row_lse, a.row_kl, bsum);
+      hipLaunchKernelGGL(k_fwd_combine, dim3(cblocks), dim3(256), 0, st, partial, 2 * splits,
+                         static_cast<int64_t>(rbs) * kTile, rows, c0, negent, a.mask, a.weight, invT, a.row_lse,
+                         a.row_kl, bsum);
     }
-    hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, rbs, sc);
+    hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, cblocks, sc);
   }
   hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, sc, p.T, a.loss);
   return hipGetLastError();
