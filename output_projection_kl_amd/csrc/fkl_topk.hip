@@ -74,7 +74,7 @@ struct SelectState {
 // next digit among keys matching the prefix, then the digit holding the
 // need-th largest key. Returns the number of keys in that digit's bin.
 template <class KeyAt>
-__device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* above_of,
+__device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* wave_tot,
                                  uint32_t* s_vals) {
   const int tid = threadIdx.x;
   const int w = 64 - st.pbits < kDigitBits ? 64 - st.pbits : kDigitBits;
@@ -103,10 +103,10 @@ __device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t*
     const uint32_t y = static_cast<uint32_t>(__shfl_down(static_cast<int>(incl), o, 64));
     if (lane + o < 64) incl += y;
   }
-  if (lane == 0) above_of[wv] = incl;
+  if (lane == 0) wave_tot[wv] = incl;
   __syncthreads();
   uint32_t above = incl - mine;
-  for (int w2 = wv + 1; w2 < kSelThreads / 64; ++w2) above += above_of[w2];
+  for (int w2 = wv + 1; w2 < kSelThreads / 64; ++w2) above += wave_tot[w2];
   if (above < st.need && above + mine >= st.need) {
     for (int b = b1 - 1; b >= b0; --b) {
       const uint32_t c = hist[b];
@@ -131,10 +131,10 @@ __device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t*
 // Digits until the bin at the K-th key is taken whole (at the latest when all
 // 64 bits are fixed: keys are distinct).
 template <class KeyAt>
-__device__ void select_rest(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* above_of,
+__device__ void select_rest(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* wave_tot,
                             uint32_t* s_vals) {
   while (st.pbits < 64) {
-    if (select_digit(key_at, n, st, hist, above_of, s_vals) == st.need) break;
+    if (select_digit(key_at, n, st, hist, wave_tot, s_vals) == st.need) break;
   }
 }
 
@@ -143,11 +143,11 @@ __device__ void select_rest(KeyAt key_at, int n, SelectState& st, uint32_t* hist
 // the remaining digits in LDS, or over the row when the bin does not fit.
 // The K keys go to keys[] in no particular order. *s_fill and *s_cand are 0.
 __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint64_t* cand, uint32_t* hist,
-                           uint32_t* above_of, uint32_t* s_vals, uint32_t* s_fill, uint32_t* s_cand) {
+                           uint32_t* wave_tot, uint32_t* s_vals, uint32_t* s_fill, uint32_t* s_cand) {
   const int tid = threadIdx.x;
   auto row_key = [row](int i) { return topk_key(row[i], i); };
   SelectState st{0, 0, static_cast<uint32_t>(K)};
-  const uint32_t in_bin = select_digit(row_key, V, st, hist, above_of, s_vals);
+  const uint32_t in_bin = select_digit(row_key, V, st, hist, wave_tot, s_vals);
   // Pass 2 over the row: keys above the boundary bin are taken now; the
   // boundary bin goes to LDS (or everything of the bin when it is taken whole).
   const uint64_t d0 = st.prefix;
@@ -169,7 +169,7 @@ __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint6
     if (nc <= static_cast<uint32_t>(kCand)) {
       const uint64_t* cp = cand;
       auto cand_key = [cp](int i) { return cp[i]; };
-      select_rest(cand_key, static_cast<int>(nc), st, hist, above_of, s_vals);
+      select_rest(cand_key, static_cast<int>(nc), st, hist, wave_tot, s_vals);
       for (uint32_t i = tid; i < nc; i += kSelThreads) {
         const uint64_t key = cand[i];
         if ((key >> (64 - st.pbits)) >= st.prefix) {
@@ -179,7 +179,7 @@ __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint6
       }
     } else {
       // Boundary bin too large for LDS: finish over the row itself.
-      select_rest(row_key, V, st, hist, above_of, s_vals);
+      select_rest(row_key, V, st, hist, wave_tot, s_vals);
       for (int i = tid; i < V; i += kSelThreads) {
         const uint64_t key = row_key(i);
         if ((key >> (64 - kDigitBits)) == d0 && (key >> (64 - st.pbits)) >= st.prefix) {
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t keys[kMaxK];
   __shared__ uint64_t cand[kCand];
-  __shared__ uint32_t above_of[kSelThreads / 64];
+  __shared__ uint32_t wave_tot[kSelThreads / 64];
   __shared__ uint32_t s_vals[3];
   __shared__ uint32_t s_fill, s_cand;
   const int tid = threadIdx.x;
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
         }
         __syncthreads();
         SelectState ss{0, 0, static_cast<uint32_t>(j)};
-        select_rest(cand_key, kSample, ss, hist, above_of, s_vals);
+        select_rest(cand_key, kSample, ss, hist, wave_tot, s_vals);
         thr = ss.pbits >= 64 ? ss.prefix : ss.prefix << (64 - ss.pbits);
       }
       if (tid == 0) s_cand = 0;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
       __syncthreads();  // every thread has read s_cand
       if (n_cand >= static_cast<uint32_t>(K) && n_cand <= static_cast<uint32_t>(kCand)) {
         SelectState st{0, 0, static_cast<uint32_t>(K)};
-        select_rest(cand_key, static_cast<int>(n_cand), st, hist, above_of, s_vals);
+        select_rest(cand_key, static_cast<int>(n_cand), st, hist, wave_tot, s_vals);
         for (uint32_t i = tid; i < n_cand; i += kSelThreads) {
           const uint64_t key = cand[i];
           if ((key >> (64 - st.pbits)) >= st.prefix) {
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
   }
   if (!done) {
     if (tid == 0) s_cand = 0;
-    select_row(row, V, K, keys, cand, hist, above_of, s_vals, &s_fill, &s_cand);
+    select_row(row, V, K, keys, cand, hist, wave_tot, s_vals, &s_fill, &s_cand);
   }
   __syncthreads();
   // Bitonic sort of Kp keys, descending.
