@@ -225,20 +225,23 @@ def bench_builder(args, torch, fkl, make_device_workload, dev) -> int:
     for _ in range(args.warmup):
         fkl.topk(wl.h, Wt, K, workspace=ws, t_idx=ti, t_logit=tl)
     torch.cuda.synchronize()
-    fkl.trace_read()
-    fkl.trace_enable(True)
+    trace = not args.no_trace
+    if trace:
+        fkl.trace_read()
+        fkl.trace_enable(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
         fkl.topk(wl.h, Wt, K, workspace=ws, t_idx=ti, t_logit=tl)
     stop.record()
     torch.cuda.synchronize()
-    fkl.trace_enable(False)
+    if trace:
+        fkl.trace_enable(False)
     ms = start.elapsed_time(stop) / args.steps
     kernels = {k["name"]: {"launches_per_step": k["launches"] / args.steps,
                            "avg_ms": k["total_ms"] / k["launches"],
                            "tflops": (k["flops"] / k["launches"]) / (k["total_ms"] / k["launches"] / 1e3) / 1e12
-                           if k["flops"] else None} for k in fkl.trace_read()}
+                           if k["flops"] else None} for k in (fkl.trace_read() if trace else [])}
     # context: torch fp32 GEMM (no TF32) + torch.topk over the same rows, in 1024-row passes
     prev = torch.backends.cuda.matmul.allow_tf32
     torch.backends.cuda.matmul.allow_tf32 = False
