@@ -61,6 +61,14 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->T = s->T;
   int64_t chunk = s->chunk ? s->chunk : kDefaultChunk;
   if (s->N > 0 && chunk > s->N) chunk = s->N;
+  // Forward passes: no [rows x V] block is ever formed, so a pass costs only
+  // its teacher lists and split statistics (a few MiB at 4096 rows). With the
+  // default slab the forward takes passes of at least min(N, kDefaultChunk)
+  // rows; an explicit vslab keeps the caller's chunk in both directions.
+  if (s->vslab == 0 && s->N > 0) {
+    const int64_t floor_rows = s->N < kDefaultChunk ? s->N : kDefaultChunk;
+    if (chunk < floor_rows) chunk = floor_rows;
+  }
   p->chunk = chunk;
   p->chunk_alloc = round_up(chunk, kTile);
   // Backward passes: the backward's memory is its gradient block (rows x
