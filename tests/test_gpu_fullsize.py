@@ -183,3 +183,55 @@ def test_fullsize_3b_full_forward_and_grad_W_rows():
     assert e_kl <= 1e-3 * max(1.0, np.abs(r_kl).max())
     assert e_gh <= GRAD_TOL
     assert e_gW <= GRAD_TOL
+
+
+def test_fullsize_terms_weighted_subset():
+    """Loss variants at the headline shape: per-token weights that are zero
+    outside a spread subset of rows, and hard labels mixed in with weight 0.3
+    (half of them one of the row's teacher indices, half elsewhere). The
+    oracle computes the loss, those rows' grad_h and all of grad_W exactly."""
+    dev = _dev()
+    wl = make_device_workload("gptoss20b", dev, mask="none")
+    rows = _sample_rows(wl.N, wl.chunk, wl.seed + 11, n_random=30)
+    rng = np.random.default_rng(wl.seed + 12)
+    w_np = np.zeros(wl.N, np.float32)
+    w_np[rows] = rng.uniform(0.25, 2.0, len(rows)).astype(np.float32)
+    y_np = rng.integers(0, wl.V, wl.N).astype(np.int32)
+    half = rows[::2]
+    y_np[half] = wl.t_idx_np[half, 0]
+    a = 0.3
+    w = torch.from_numpy(w_np).to(dev)
+    y = torch.from_numpy(y_np).to(dev)
+    print(f"[fullsize-terms] {wl.describe()} weighted rows {len(rows)} a={a}", flush=True)
+    loss, lse, kl = fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, chunk=wl.chunk, return_row_kl=True,
+                                row_weight=w, label=y, label_weight=a)
+    gh, gW = fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, lse, T=wl.T, chunk=wl.chunk,
+                          row_weight=w, label=y, label_weight=a)
+    torch.cuda.synchronize()
+    loss = loss.item()
+    Wd = _W64(wl)
+    hs = wl.h[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    ti, tl = wl.t_idx_np[rows], wl.t_logit_np[rows]
+    kw = dict(row_weight=w_np[rows].astype(np.float64), label=y_np[rows], label_weight=a)
+    r_loss, r_lse, r_l = oracle.forward_terms(hs, Wd, ti, tl, wl.T, **kw)
+    r_gh, r_gW = oracle.backward_terms(hs, Wd, ti, tl, wl.T, **kw)
+    del Wd
+    e_loss = abs(loss - r_loss) / abs(r_loss)
+    e_lse = float(np.abs(lse.cpu().numpy()[rows] - r_lse).max())
+    e_l = float(np.abs(kl.cpu().numpy()[rows] - r_l).max() / np.abs(r_l).max())
+    sel = torch.from_numpy(rows).to(dev)
+    e_gh = _rel_max(gh[sel].cpu().numpy(), r_gh)
+    gh[sel] = 0.0
+    others_zero = bool((gh == 0).all().item())
+    del gh
+    ref = torch.from_numpy(r_gW.astype(np.float32)).to(dev)
+    del r_gW
+    e_gW = float((gW - ref).abs().max().item() / ref.abs().max().item())
+    print(f"   loss {loss:.7g} ref {r_loss:.7g} rel {e_loss:.2e} | lse {e_lse:.2e} | row l {e_l:.2e} | "
+          f"grad_h {e_gh:.2e} | grad_W (all {wl.V} rows) {e_gW:.2e}", flush=True)
+    assert e_loss <= LOSS_RTOL
+    assert e_lse <= LSE_ATOL
+    assert e_l <= 1e-3
+    assert e_gh <= GRAD_TOL
+    assert e_gW <= GRAD_TOL
+    assert others_zero
