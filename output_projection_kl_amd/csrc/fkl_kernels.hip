@@ -24,6 +24,7 @@
 //                   vocabulary into partial sums)
 //   k_reduce_grad_h grad_h[chunk] (+)= the partial sums, in split order
 #include <climits>
+#include <type_traits>
 #include <cmath>
 
 #include "fkl_device.h"
@@ -78,6 +79,12 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__
 // (1 - a) p~ + a onehot(y): teacher weights are scaled by 1 - a and y is
 // inserted with a, or a is added to the teacher entry at y (the list then ends
 // with an empty entry at INT_MAX). Lists have L = K (+ 1 with labels) entries.
+constexpr int kPrepRankMaxK = 128;  // longer teacher lists are sorted bitonically
+
+// LONG = false: each entry's rank by counting (ties by position), for K up to
+// kPrepRankMaxK. LONG = true: a bitonic sort of (index, position) pairs in the
+// wave's LDS rows, which gives the same order, for K up to 1024.
+template <bool LONG>
 __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict__ t_idx,
                                                       const float* __restrict__ t_logit,
                                                       const int32_t* __restrict__ label, float label_w,
@@ -85,27 +92,40 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
                                                       float invT, int32_t* __restrict__ tsort_idx,
                                                       float* __restrict__ tsort_p,
                                                       float* __restrict__ negent) {
-  __shared__ int32_t sidx[4][1024];
+  using Key = typename std::conditional<LONG, uint64_t, int32_t>::type;
+  __shared__ Key skey[4][1024];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
-  const bool active = r < rows;
+  if (r >= rows) return;  // no block-wide synchronisation below
+  Key* sk = &skey[wave][0];
   const int32_t* ti = t_idx + (r0 + r) * static_cast<int64_t>(K);
   const float* tl = t_logit + (r0 + r) * static_cast<int64_t>(K);
-  float mx = -INFINITY;
-  if (active) {
-    for (int k = lane; k < K; k += 64) {
-      mx = fmaxf(mx, tl[k] * invT);
-      sidx[wave][k] = ti[k];
-    }
+  int Kp = K;
+  if constexpr (LONG) {
+    Kp = 1;
+    while (Kp < K) Kp <<= 1;
   }
-  __syncthreads();
-  if (!active) return;
+  float mx = -INFINITY;
+  for (int k = lane; k < Kp; k += 64) {
+    if constexpr (LONG) {
+      sk[k] = k < K ? (static_cast<uint64_t>(static_cast<uint32_t>(ti[k])) << 32) | static_cast<uint32_t>(k)
+                    : ~uint64_t(0);
+    } else {
+      sk[k] = ti[k];
+    }
+    if (k < K) mx = fmaxf(mx, tl[k] * invT);
+  }
+  __builtin_amdgcn_wave_barrier();
   mx = wave_max(mx);
   float se = 0.f;
   for (int k = lane; k < K; k += 64) se += expf(tl[k] * invT - mx);
   se = wave_sum(se);
   const float lnorm = mx + logf(se);
+  auto index_at = [sk](int k) -> int32_t {
+    if constexpr (LONG) return static_cast<int32_t>(sk[k] >> 32);
+    else return sk[k];
+  };
   const bool has_label = label != nullptr;
   const int32_t y = has_label ? label[r0 + r] : 0;
   const float keep = has_label ? 1.0f - label_w : 1.0f;
@@ -113,29 +133,56 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
   int below = 0, dup = 0;
   if (has_label) {
     for (int k = lane; k < K; k += 64) {
-      below += sidx[wave][k] < y;
-      dup += sidx[wave][k] == y;
+      below += index_at(k) < y;
+      dup += index_at(k) == y;
     }
     below = static_cast<int>(wave_sum(static_cast<float>(below)));
     dup = static_cast<int>(wave_sum(static_cast<float>(dup)));
   }
   const bool insert = has_label && dup == 0;
   float ne = 0.f;
-  int32_t* oi = tsort_idx + static_cast<int64_t>(r) * L;
-  float* op = tsort_p + static_cast<int64_t>(r) * L;
   for (int k = lane; k < K; k += 64) {
     const float lp = tl[k] * invT - lnorm;
-    const float p = expf(lp);
-    ne += p * lp;
-    const int32_t key = sidx[wave][k];
-    int rank = 0;
-    for (int j = 0; j < K; ++j) {
-      const int32_t o = sidx[wave][j];
-      rank += (o < key) | ((o == key) & (j < k));
+    ne += expf(lp) * lp;
+  }
+  int32_t* oi = tsort_idx + static_cast<int64_t>(r) * L;
+  float* op = tsort_p + static_cast<int64_t>(r) * L;
+  if constexpr (!LONG) {
+    for (int k = lane; k < K; k += 64) {
+      const int32_t key = sk[k];
+      int rank = 0;
+      for (int j = 0; j < K; ++j) {
+        const int32_t o = sk[j];
+        rank += (o < key) | ((o == key) & (j < k));
+      }
+      if (insert && key > y) ++rank;
+      oi[rank] = key;
+      op[rank] = keep * expf(tl[k] * invT - lnorm) + ((has_label && key == y) ? label_w : 0.0f);
     }
-    if (insert && key > y) ++rank;
-    oi[rank] = key;
-    op[rank] = keep * p + ((has_label && key == y) ? label_w : 0.0f);
+  } else {
+    for (int size = 2; size <= Kp; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = lane; t < Kp / 2; t += 64) {
+          const int i = 2 * t - (t & (stride - 1));
+          const int j = i + stride;
+          const uint64_t a = sk[i];
+          const uint64_t b = sk[j];
+          if (((i & size) == 0) == (a > b)) {
+            sk[i] = b;
+            sk[j] = a;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    for (int i = lane; i < K; i += 64) {
+      const uint64_t v = sk[i];
+      const int32_t key = static_cast<int32_t>(v >> 32);
+      const int k = static_cast<int>(v & 0xFFFFFFFFu);
+      const int rank = i + ((insert && key > y) ? 1 : 0);
+      oi[rank] = key;
+      op[rank] = keep * expf(tl[k] * invT - lnorm) + ((has_label && key == y) ? label_w : 0.0f);
+    }
   }
   ne = wave_sum(ne);
   if (lane == 0) {
@@ -148,6 +195,18 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
       op[K] = 0.0f;
     }
   }
+}
+
+hipError_t launch_teacher_prep(const int32_t* t_idx, const float* t_logit, const int32_t* label, float label_w,
+                               int64_t r0, int rows, int K, int L, float invT, int32_t* tsort_idx, float* tsort_p,
+                               float* negent, hipStream_t st) {
+  if (K <= kPrepRankMaxK)
+    hipLaunchKernelGGL(k_teacher_prep<false>, dim3(ceil_div(rows, 4)), dim3(256), 0, st, t_idx, t_logit, label,
+                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent);
+  else
+    hipLaunchKernelGGL(k_teacher_prep<true>, dim3(ceil_div(rows, 4)), dim3(256), 0, st, t_idx, t_logit, label,
+                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent);
+  return hipGetLastError();
 }
 
 __global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, Scalars* sc) {
@@ -674,8 +733,8 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
-      hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                         a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent);
+      launch_teacher_prep(a.t_idx, a.t_logit, a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent,
+                          st);
     }
     const int splits = splits_for(rbs, p.n_vt);
     FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, L, k2, tidx, tp,
@@ -731,8 +790,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
     const int rbs = static_cast<int>(ceil_div(rows, kTile));
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
-      hipLaunchKernelGGL(k_teacher_prep, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a.t_idx, a.t_logit,
-                         a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent);
+      launch_teacher_prep(a.t_idx, a.t_logit, a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent,
+                          st);
     }
     const double dd = static_cast<double>(p.d);
     for (int64_t s = 0; s < n_slabs; ++s) {

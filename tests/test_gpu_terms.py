@@ -85,6 +85,15 @@ def test_weights_and_labels_ragged():
     _case(wl, 0.7, rng.random(wl.N) * 3.0, _labels(wl, rng), 0.4, chunk=128, vslab=768, g=2.5)
 
 
+@pytest.mark.parametrize("K", [129, 700])
+def test_labels_with_long_teacher_lists(K):
+    """Teacher lists longer than 128 entries take the sorted (bitonic) path of
+    the list preparation; hard labels land inside and outside the lists."""
+    wl = make_workload("tiny", 3, N=200, d=64, V=3000, K=K, mask="random25")
+    rng = np.random.default_rng(14)
+    _case(wl, 1.3, rng.random(wl.N) + 0.5, _labels(wl, rng), 0.35, chunk=64, vslab=768, g=0.9)
+
+
 def test_zero_total_weight():
     wl = make_workload("tiny", 2)
     loss, gh, gW = _case(wl, 1.0, np.zeros(wl.N), None, 0.0, chunk=64, vslab=1024)
