@@ -100,7 +100,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, command: st
     kernels = {}
     for tag, d, scale in (("fetch", fetch, rscale), ("write", write, wscale)):
         for name, v in d.values():
-            short = name.split("(")[0].split("::")[-1].replace("void ", "").strip()
+            short = name.split("(")[0].split("<")[0].split("::")[-1].replace("void ", "").strip()
             if not short.startswith("k_"):
                 continue
             k = kernels.setdefault(short[2:], {"launches_fetch": 0, "launches_write": 0,
