@@ -41,14 +41,40 @@ TEACHER_RECIPES = {
 }
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string
+    literals kept), so that comment edits leave the hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's code (kernels and launch plans), comments excluded."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "output_projection_kl_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
                 h.update(f.encode())
-                h.update(fh.read())
+                h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()
 
 

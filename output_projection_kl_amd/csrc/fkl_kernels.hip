@@ -1,6 +1,6 @@
 // HIP kernels of libfkl for gfx950, and their launch sequences.
 //
-// Forward, per chunk of rows (blog post on the page "Efficient Offline Top-K
+// Forward, per pass of rows (blog post on the page "Efficient Offline Top-K
 // Logits and Fused Chunked KL Loss Enable Scalable LLM Distillation",
 // section "Two systems changes": logits are formed one chunk at a time,
 // folded into the running loss and dropped):
@@ -11,10 +11,10 @@
 //                   MFMA logits tile -> LDS -> per-row online max / sum of
 //                   exp2, and the logits at the teacher indices picked up by a
 //                   per-row cursor while the tile is resident
-//   k_fwd_combine   merge the vocabulary splits -> row_lse, row KL, block sums
+//   k_fwd_combine   merge the vocabulary splits -> row_lse, row KL, fp64 sums
 //   k_accumulate    fixed-order fp64 running loss
-// Backward, per chunk and vocabulary slab (same section: each chunk's logits
-// are recomputed rather than stored):
+// Backward, per pass of rows and vocabulary slab (same section: each pass's
+// logits are recomputed rather than stored):
 //   k_bwd_g         logits tile again -> fp32 through LDS -> G = c (exp(s - lse)
 //                   - p~) formed in fp32 by the row owners (teacher entries
 //                   subtracted before rounding) -> bf16 row-major gradient
@@ -73,17 +73,18 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__
 }
 
 // One wave per row, four rows per workgroup: p = softmax(t_logit / T) over
-// the K cached entries, the row's list of (index, weight) sorted by vocabulary index, and the weighted
-// negative entropy (stable ranks, so even repeated indices fill every slot).
-// With a hard label y (weight a), the list holds the target
-// (1 - a) p~ + a onehot(y): teacher weights are scaled by 1 - a and y is
-// inserted with a, or a is added to the teacher entry at y (the list then ends
-// with an empty entry at INT_MAX). Lists have L = K (+ 1 with labels) entries.
-constexpr int kPrepRankMaxK = 128;  // longer teacher lists are sorted bitonically
-
-// LONG = false: each entry's rank by counting (ties by position), for K up to
-// kPrepRankMaxK. LONG = true: a bitonic sort of (index, position) pairs in the
-// wave's LDS rows, which gives the same order, for K up to 1024.
+// the K cached entries, the row's list of (index, weight) sorted by vocabulary
+// index (ties by position, so even repeated indices fill every slot), and the
+// weighted negative entropy. With a hard label y (weight a), the list holds
+// the target (1 - a) p~ + a onehot(y): teacher weights are scaled by 1 - a and
+// y is inserted with a, or a is added to the teacher entry at y (the list then
+// ends with an empty entry at INT_MAX). Lists have L = K (+ 1 with labels)
+// entries.
+//
+// LONG = false: each entry's rank by counting, for K up to kPrepRankMaxK.
+// LONG = true: a bitonic sort of (index, position) pairs in the wave's LDS
+// row, which gives the same order, for K up to 1024.
+constexpr int kPrepRankMaxK = 128;
 template <bool LONG>
 __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict__ t_idx,
                                                       const float* __restrict__ t_logit,
