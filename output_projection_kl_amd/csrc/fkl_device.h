@@ -3,9 +3,10 @@
 // ("plain") or contraction-strided ("transposed").
 //
 // Block tile: 256 (M) x (WN * NBW * 32) (N), contraction in LDS stages of 32,
-// 2 x WN waves; each wave owns 128 x NBW*32 of the output as 4 x NBW
-// accumulators of v_mfma_f32_32x32x16_bf16 (32 x 32, fp32). The path's
-// kernels use WN = 4, NBW = 2: a 256 x 256 tile on 8 waves (2 per SIMD).
+// (8 / MB) x WN waves; each wave owns MB*32 x NBW*32 of the output as
+// 2MB x 2NBW accumulators of v_mfma_f32_16x16x32_bf16 (16 x 16, fp32), one
+// MFMA step of 32 per stage. The path's kernels use WN = 4, NBW = 2, MB = 4:
+// a 256 x 256 tile on 8 waves (2 per SIMD), 128 x 64 per wave.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,10 +49,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 //    c of row r is stored at physical chunk c ^ swz_plain(r).
 //  * transposed operand: 32 k-rows x 256 mn = 512 B per k-row (32 chunks of
 //    8 mn); chunk c of k-row r is stored at physical chunk c ^ swz_trans(r).
-// The XOR swizzles keep the fragment reads (16 lanes per LDS cycle) on
-// distinct banks. MFMA fragments (32 mn x 16 k per lane group) are read with
-// ds_read_b128 from a plain stage and with two ds_read_b64_tr_b16 (4 x 16
-// transposes within each 16-lane group) from a transposed stage.
+// The XOR swizzles keep the fragment reads on distinct banks (16 lanes per
+// LDS cycle for ds_read_b128, 32 for ds_read_b64_tr_b16). MFMA fragments
+// (16 mn x 32 k) are read with ds_read_b128 from a plain stage and with two
+// ds_read_b64_tr_b16 (4 x 16 transposes within each 16-lane group) from a
+// transposed stage.
 // ---------------------------------------------------------------------------
 
 constexpr int kStageK = 32;
@@ -79,7 +81,7 @@ struct TileCfg {
 };
 
 __device__ __forceinline__ int swz_plain(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
-__device__ __forceinline__ int swz_trans(int r) { return (r & 3) << 2; }
+__device__ __forceinline__ int swz_trans(int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 1); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -183,11 +185,11 @@ __device__ __forceinline__ void issue_stage(const StageSrc<LW>& s, int kt, bool 
   }
 }
 
-// Fragment of 32 (mn) x 16 (k) for this lane from a plain stage region: lane
-// l receives mn = mn_base + (l & 31), k = kb + 8 * (l >> 5) .. + 7.
-__device__ __forceinline__ bf16x8 frag_plain(const char* region, int mn_base, int kb, int lane) {
-  const int r = mn_base + (lane & 31);
-  const int c = (kb >> 3) + (lane >> 5);
+// Fragment of 16 (mn) x 32 (k) for this lane from a plain stage region: lane
+// l receives mn = mn_base + (l & 15), k = 8 * (l >> 4) .. + 7.
+__device__ __forceinline__ bf16x8 frag_plain(const char* region, int mn_base, int lane) {
+  const int r = mn_base + (lane & 15);
+  const int c = lane >> 4;
   return *reinterpret_cast<const bf16x8*>(region + r * (kStageK * 2) + ((c ^ swz_plain(r)) << 4));
 }
 
@@ -204,16 +206,16 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const char* p) {
   return v;
 }
 
-// Lane l receives mn = mn_base + (l & 31) and k = kb + 8 * (l >> 5) .. + 7 as
-// two halves of 4 k each: lanes 4j..4j+3 of each 16-lane group point at k-row j
-// (4 consecutive mn each) and lane i gets column i.
+// Lane l receives mn = mn_base + (l & 15) and k = 8 * (l >> 4) .. + 7 as two
+// halves of 4 k each: in 16-lane group g, lanes 4j..4j+3 point at k-row
+// 8g + j (then 8g + 4 + j), 4 consecutive mn each, and lane i gets column i.
 template <int R>
-__device__ __forceinline__ void frag_trans_issue(const char* region, int mn_base, int kb, int lane,
-                                                 u32x2& lo, u32x2& hi) {
+__device__ __forceinline__ void frag_trans_issue(const char* region, int mn_base, int lane, u32x2& lo,
+                                                 u32x2& hi) {
   const int g = lane >> 4;
   const int i = lane & 15;
-  const int r = kb + 8 * (g >> 1) + (i >> 2);
-  const int mn = mn_base + 16 * (g & 1) + 4 * (i & 3);
+  const int r = 8 * g + (i >> 2);
+  const int mn = mn_base + 4 * (i & 3);
   const int c = mn >> 3;
   const int half = (mn & 7) * 2;
   lo = ds_read_tr16(region + r * (2 * R) + ((c ^ swz_trans(r)) << 4) + half);
@@ -225,109 +227,92 @@ __device__ __forceinline__ bf16x8 join_halves(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Fragments of one 16-deep contraction step for a wave: MB of A (MB * 32
-// rows), NBW of B (NBW * 32 columns).
-template <bool TA, bool TB, int NBW, int RB, int MB = 4>
-struct Frags {
-  static constexpr int kX = MB > NBW ? MB : NBW;
-  bf16x8 a[MB], b[NBW];
-  u32x2 ta[MB][2], tb[NBW][2];
+// Settle outstanding ds_read_b64_tr_b16 results: the asm operands make every
+// later use of these registers depend on the wait.
+template <int X>
+__device__ __forceinline__ void settle_tr(u32x2 (&t)[X][2]) {
+  static_assert(X == 2 || X == 4 || X == 8, "fragment count");
+  if constexpr (X == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
+  } else if constexpr (X == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]), "+v"(t[2][1]),
+                   "+v"(t[3][0]), "+v"(t[3][1]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]), "+v"(t[2][1]),
+                   "+v"(t[3][0]), "+v"(t[3][1]), "+v"(t[4][0]), "+v"(t[4][1]), "+v"(t[5][0]), "+v"(t[5][1]),
+                   "+v"(t[6][0]), "+v"(t[6][1]), "+v"(t[7][0]), "+v"(t[7][1]));
+  }
+}
 
-  __device__ __forceinline__ void issue(const char* ra, const char* rb, int wm, int wn, int kb, int lane) {
+// Fragments of one 32-deep stage for a wave: XA of A (16 rows each), XB of B
+// (16 columns each).
+template <bool TA, bool TB, int XA, int XB, int RB>
+struct Frags {
+  bf16x8 a[XA], b[XB];
+  u32x2 ta[XA][2], tb[XB][2];
+
+  __device__ __forceinline__ void issue(const char* ra, const char* rb, int am, int bn, int lane) {
 #pragma unroll
-    for (int x = 0; x < kX; ++x) {
-      if (x < MB) {
-        if constexpr (TA) frag_trans_issue<kARows>(ra, wm * MB * 32 + x * 32, kb, lane, ta[x][0], ta[x][1]);
-        else a[x] = frag_plain(ra, wm * MB * 32 + x * 32, kb, lane);
-      }
-      if (x < NBW) {
-        if constexpr (TB) frag_trans_issue<RB>(rb, wn * NBW * 32 + x * 32, kb, lane, tb[x][0], tb[x][1]);
-        else b[x] = frag_plain(rb, wn * NBW * 32 + x * 32, kb, lane);
-      }
+    for (int x = 0; x < XA; ++x) {
+      if constexpr (TA) frag_trans_issue<kARows>(ra, am + x * 16, lane, ta[x][0], ta[x][1]);
+      else a[x] = frag_plain(ra, am + x * 16, lane);
+    }
+#pragma unroll
+    for (int y = 0; y < XB; ++y) {
+      if constexpr (TB) frag_trans_issue<RB>(rb, bn + y * 16, lane, tb[y][0], tb[y][1]);
+      else b[y] = frag_plain(rb, bn + y * 16, lane);
     }
   }
 
-  // Wait for the transposed reads; the asm operands make every later use of
-  // these registers depend on the wait.
   __device__ __forceinline__ void settle() {
     if constexpr (TA) {
-      if constexpr (MB == 4) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]), "+v"(ta[2][0]),
-                       "+v"(ta[2][1]), "+v"(ta[3][0]), "+v"(ta[3][1]));
-      } else if constexpr (MB == 2) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(ta[0][0]), "+v"(ta[0][1]), "+v"(ta[1][0]), "+v"(ta[1][1]));
-      } else {
-        static_assert(MB == 1, "MB must be 1, 2 or 4");
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ta[0][0]), "+v"(ta[0][1]));
-      }
+      settle_tr(ta);
+#pragma unroll
+      for (int x = 0; x < XA; ++x) a[x] = join_halves(ta[x][0], ta[x][1]);
     }
     if constexpr (TB) {
-      if constexpr (NBW == 4) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
-                       "+v"(tb[2][1]), "+v"(tb[3][0]), "+v"(tb[3][1]));
-      } else if constexpr (NBW == 3) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]), "+v"(tb[2][0]),
-                       "+v"(tb[2][1]));
-      } else {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(tb[0][0]), "+v"(tb[0][1]), "+v"(tb[1][0]), "+v"(tb[1][1]));
-      }
-    }
+      settle_tr(tb);
 #pragma unroll
-    for (int x = 0; x < kX; ++x) {
-      if constexpr (TA) if (x < MB) a[x] = join_halves(ta[x][0], ta[x][1]);
-      if constexpr (TB) if (x < NBW) b[x] = join_halves(tb[x][0], tb[x][1]);
+      for (int y = 0; y < XB; ++y) b[y] = join_halves(tb[y][0], tb[y][1]);
     }
   }
 
-  __device__ __forceinline__ void mma(f32x16 (&acc)[MB][NBW]) const {
+  __device__ __forceinline__ void mma(f32x4 (&acc)[XA][XB]) const {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int x = 0; x < XA; ++x)
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      for (int y = 0; y < XB; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
   }
 };
 
-template <int MB, int NB>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
+template <int X, int Y>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[X][Y]) {
 #pragma unroll
-  for (int a = 0; a < MB; ++a)
+  for (int a = 0; a < X; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+    for (int b = 0; b < Y; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // acc += A[m0 : m0+256, 0 : 32*nk] * B[n0 : n0+kTileN, 0 : 32*nk]^T over a
 // ring of TileCfg<NBW, WN, MB>::kStages LDS stages ((8 / MB) x WN waves, each
-// MB*32 x NBW*32 of the output; wave w sits at row block w / WN, column block
-// w % WN).
+// MB*32 x NBW*32 of the output as 2MB x 2NBW blocks of 16 x 16; wave w sits at
+// row block w / WN, column block w % WN).
 //
-// Schedule per stage kt (two 16-deep steps f0, f1):
-//   issue f1 reads (stage kt) | f0 MFMAs | settle f1
-//   wait for stage kt+1 + block barrier   (every wave has issued its reads
-//                                          of stage kt)
-//   issue f0 reads of stage kt+1 | DMA stage kt+S into stage kt's buffer
-//   f1 MFMAs | settle f0
-// so the barrier and the LDS latency of the next stage sit between two MFMA
-// bursts instead of in front of an idle pipe. Plain-layout reads of stage kt
-// may still be queued at the LDS when the barrier opens. The schedule relies
-// on the LDS serving them before the DMA writes into that buffer, which are
-// issued after the barrier and first make a round trip through the caches.
-// (Waiting for those reads before the barrier cost 1.3% of the loop's
-// throughput when measured.) The loop body has no branch
-// (the last stage is peeled and a stage is issued every iteration, out of
-// range past the end), so the compiler's wait counts hold on every path.
-// Starts with a block barrier (the previous user of the LDS is done) and ends
-// with one; on return no load is in flight and the LDS may be reused.
+// Schedule per stage kt: the stage's MFMAs, a wait for stage kt+1 and one
+// block barrier (every wave has read stage kt), then the fragment reads of
+// stage kt+1 and the DMA of stage kt+S into stage kt's buffer. The two waves
+// on a SIMD interleave, so one wave's MFMAs cover the other's LDS reads.
+// (Splitting the MFMAs around the barrier measured slower.) The loop body has
+// no branch (a stage is issued every iteration, out of range past the end),
+// so the compiler's wait counts hold on every path. Starts with a block
+// barrier (the previous user of the LDS is done) and ends with one; on return
+// no load is in flight and the LDS may be reused.
 template <bool TA, bool TB, int NBW, int WN = 2, int MB = 4>
 __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0,
-                                              int nk, f32x16 (&acc)[MB][NBW], char* lds) {
+                                              int nk, f32x4 (&acc)[2 * MB][2 * NBW], char* lds) {
   using C = TileCfg<NBW, WN, MB>;
   constexpr int S = C::kStages;
   constexpr int RB = C::kBExtent;
@@ -354,31 +339,24 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B
   }
   wait_vmcnt<(S - 1) * C::kDmaStage>();  // stage 0 landed
   block_barrier();
-  Frags<TA, TB, NBW, RB, MB> f0, f1;
-  f0.issue(lds, lds + kAStageBytes, wm, wn, 0, lane);
-  f0.settle();
+  const int am = wm * MB * 32;
+  const int bn = wn * NBW * 32;
+  Frags<TA, TB, 2 * MB, 2 * NBW, RB> f;
+  f.issue(lds, lds + kAStageBytes, am, bn, lane);
+  f.settle();
   for (int kt = 0; kt + 1 < nk; ++kt) {
     char* cur = lds + (kt % S) * C::kStageBytes;
     const char* nxt = lds + ((kt + 1) % S) * C::kStageBytes;
-    f1.issue(cur, cur + kAStageBytes, wm, wn, 16, lane);
-    f0.mma(acc);
-    f1.settle();
+    f.mma(acc);
     wait_vmcnt<(S - 2) * C::kDmaStage>();  // stage kt+1 landed
     block_barrier();
-    f0.issue(nxt, nxt + kAStageBytes, wm, wn, 0, lane);
+    f.issue(nxt, nxt + kAStageBytes, am, bn, lane);
     const bool live = kt + S < nk;
     issue_stage<LA>(sa, kt + S, live, cur, wave);
     issue_stage<LB>(sb, kt + S, live, cur + kAStageBytes, wave);
-    f1.mma(acc);
-    f0.settle();
+    f.settle();
   }
-  {
-    char* cur = lds + ((nk - 1) % S) * C::kStageBytes;
-    f1.issue(cur, cur + kAStageBytes, wm, wn, 16, lane);
-    f0.mma(acc);
-    f1.settle();
-    f1.mma(acc);
-  }
+  f.mma(acc);
   wait_vmcnt<0>();
   block_barrier();
 }
@@ -409,12 +387,11 @@ __device__ __forceinline__ void grouped_tile(int L, int R, int S, int group, int
   s = in / rows;
 }
 
-// Row / column of accumulator element i of block (mb, nb) for this lane,
-// relative to the wave's 128 x BN/2 sub-tile.
-__device__ __forceinline__ int acc_row(int mb, int i, int lane) {
-  return mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-__device__ __forceinline__ int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
+// Row / column of accumulator element i of block (x, y) for this lane,
+// relative to the wave's sub-tile (16 x 16 blocks: lane l holds column
+// l & 15 and rows 4 (l >> 4) .. + 3).
+__device__ __forceinline__ int acc_row(int x, int i, int lane) { return x * 16 + 4 * (lane >> 4) + i; }
+__device__ __forceinline__ int acc_col(int y, int lane) { return y * 16 + (lane & 15); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

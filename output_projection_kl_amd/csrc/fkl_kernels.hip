@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
   float m2 = -INFINITY, se = 0.f, gz = 0.f;
 
   for (int vt = vt0; vt < vt1; ++vt) {
-    f32x16 acc[4][kNBW];
+    MainAcc acc;
     zero_acc(acc);
     gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
                                            static_cast<int64_t>(vt) * kTile, nk, acc, lds);
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
   const int slab_end = static_cast<int>(P.slab0 + P.slab_w);
 
   for (int vt = vt0; vt < vt1; ++vt) {
-    f32x16 acc[4][kNBW];
+    MainAcc acc;
     zero_acc(acc);
     const int vbase = static_cast<int>(P.slab0) + vt * kTile;
     gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc, lds);

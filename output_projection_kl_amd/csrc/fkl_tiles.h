@@ -17,18 +17,20 @@ constexpr int kWN = 4;
 using MainCfg = TileCfg<kNBW, kWN>;
 constexpr int kBlockThreads = MainCfg::kThreads;  // 512
 
+// Accumulators of one wave of a main block tile: 8 x 4 blocks of 16 x 16.
+using MainAcc = f32x4[8][2 * kNBW];
+
 // Waves whose 64 columns fall in half `half` of the tile copy their 128 x 64
 // accumulators into a 256 x 128 fp32 LDS half tile (stride kStageLd floats).
-__device__ __forceinline__ void stage_half_tile(const f32x16 (&acc)[4][kNBW], float* stage, int wm, int wn,
-                                                int lane) {
+__device__ __forceinline__ void stage_half_tile(const MainAcc& acc, float* stage, int wm, int wn, int lane) {
   const int cbase = (wn & 1) * 64;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int x = 0; x < 8; ++x)
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
+    for (int y = 0; y < 2 * kNBW; ++y)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        stage[(wm * 128 + acc_row(mb, i, lane)) * kStageLd + cbase + acc_col(nb, lane)] = acc[mb][nb][i];
+      for (int i = 0; i < 4; ++i)
+        stage[(wm * 128 + acc_row(x, i, lane)) * kStageLd + cbase + acc_col(y, lane)] = acc[x][y][i];
 }
 
 constexpr int kStageFp32Bytes = kTile * kStageLd * 4;  // 256 x 128 fp32 half tile, padded
@@ -87,7 +89,7 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  f32x16 acc[1][2];
+  f32x4 acc[2][4];
   zero_acc(acc);
   gemm_mainloop<TA, TB, 2, 1, 1>(A, B, m0, n0, nk, acc, lds);
   const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
@@ -106,10 +108,12 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
   }
   float* stage = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      stage[(wave * 32 + acc_row(0, i, lane)) * kNarrowLd + acc_col(nb, lane)] = acc[0][nb][i];
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stage[(wave * 32 + acc_row(x, i, lane)) * kNarrowLd + acc_col(y, lane)] = acc[x][y][i];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -149,7 +153,7 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
     narrow_acc_tile<TA, TB>(P, k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk, C, lds);
     return;
   }
-  f32x16 acc[4][kNBW];
+  MainAcc acc;
   zero_acc(acc);
   gemm_mainloop<TA, TB, kNBW, kWN>(k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk,
                                    acc, lds);
