@@ -236,10 +236,13 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 // ---------------------------------------------------------------------------
 
 // Walk over one row's teacher entries sorted by vocabulary index. A window of
-// four entries sits in registers and every step loads the entry four ahead,
-// so a row that meets several entries in one half tile does not stall on
-// memory; the refill of the last slot has three steps (normally a whole
-// tile) to arrive.
+// four entries sits in registers. A step shifts the window and leaves its
+// last slot empty; refill(), called once per tile after the epilogue, loads
+// the empty slots, so those loads have the whole next mainloop to arrive and
+// the epilogue never waits for memory unless a row takes more than three
+// entries in one tile (then the current entry is loaded on the spot).
+constexpr int kUnloaded = INT_MAX - 1;  // slot not loaded yet (INT_MAX: past the row's end)
+
 struct Cursor {
   const int32_t* idx;
   const float* p;
@@ -301,8 +304,15 @@ struct Cursor {
     p1 = p2;
     e2 = e3;
     p2 = p3;
+    e3 = kUnloaded;
     ++pos;
-    load_at(pos + 3, e3, p3);
+    if (e0 == kUnloaded) load_at(pos, e0, p0);
+  }
+
+  __device__ __forceinline__ void refill() {
+    if (e1 == kUnloaded) load_at(pos + 1, e1, p1);
+    if (e2 == kUnloaded) load_at(pos + 2, e2, p2);
+    if (e3 == kUnloaded) load_at(pos + 3, e3, p3);
   }
 };
 
@@ -417,6 +427,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
       }
       __syncthreads();
     }
+    cur.refill();
   }
   const int ld = P.rbs * kTile;
   P.partial[static_cast<int64_t>(split * 2 + sub) * ld + row] = f32x4{m2, se, gz, 0.f};
@@ -597,6 +608,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
       }
       __syncthreads();
     }
+    cur.refill();
   }
 }
 
