@@ -61,25 +61,19 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->T = s->T;
   int64_t chunk = s->chunk ? s->chunk : kDefaultChunk;
   if (s->N > 0 && chunk > s->N) chunk = s->N;
-  // Forward passes: no [rows x V] block is ever formed, so a pass costs only
-  // its teacher lists and split statistics (a few MiB at 4096 rows). With the
-  // default slab the forward takes passes of at least min(N, kDefaultChunk)
-  // rows; an explicit vslab keeps the caller's chunk in both directions.
+  // Passes: no [rows x V] block is ever formed, so a forward pass costs only
+  // its teacher lists and split statistics (a few MiB at 8192 rows) and a
+  // backward pass its gradient block (rows x vslab). With the default slab
+  // both directions take passes of at least min(N, kPassRows) rows (the
+  // forward's W stream is then shared by more rows; a narrower slab keeps the
+  // gradient block's size); an explicit vslab keeps the caller's chunk.
   if (s->vslab == 0 && s->N > 0) {
-    const int64_t floor_rows = s->N < kDefaultChunk ? s->N : kDefaultChunk;
+    const int64_t floor_rows = s->N < kPassRows ? s->N : kPassRows;
     if (chunk < floor_rows) chunk = floor_rows;
   }
   p->chunk = chunk;
   p->chunk_alloc = round_up(chunk, kTile);
-  // Backward passes: the backward's memory is its gradient block (rows x
-  // vslab), so with the default slab it takes passes of at least
-  // min(N, kBwdPassRows) rows (a narrower slab keeps the block's size); an
-  // explicit vslab keeps the caller's chunk.
   int64_t bchunk = chunk;
-  if (s->vslab == 0 && s->N > 0) {
-    const int64_t floor_rows = s->N < kBwdPassRows ? s->N : kBwdPassRows;
-    if (bchunk < floor_rows) bchunk = floor_rows;
-  }
   p->bchunk = bchunk;
   p->bchunk_alloc = round_up(bchunk, kTile);
   // The kernels address each operand view (an h chunk, a W slab, the

@@ -13,7 +13,7 @@ namespace fkl {
 constexpr int kTile = 256;          // rows and vocabulary columns of one logits tile
 constexpr int kTargetBlocks = 256;  // workgroups a launch aims for (one per CU on MI355X)
 constexpr int kDefaultChunk = 4096;
-constexpr int kBwdPassRows = 8192;  // backward pass rows floor with the default slab
+constexpr int kPassRows = 8192;  // pass rows floor (forward and backward) with the default slab
 constexpr int64_t kDefaultSlabElems = int64_t(64) << 20;  // gradient block of ~64 Mi bf16 (128 MiB)
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

@@ -213,12 +213,14 @@ def test_operand_views_stay_under_2_gib():
 
 
 def test_backward_pass_rows_follow_gradient_block():
-    """With the default slab the backward takes passes of max(chunk, min(N, 8192))
-    rows, so a small forward chunk does not shrink the backward's passes or grow
-    its workspace; an explicit slab keeps chunk-row passes."""
-    _, b1024 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024)
-    _, b4096 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=4096)
-    assert b1024 == b4096
+    """With the default slab both directions take passes of max(chunk, min(N, 8192))
+    rows, so a small chunk does not shrink the passes or grow the workspace; an
+    explicit slab keeps chunk-row passes."""
+    f1024, b1024 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024)
+    f4096, b4096 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=4096)
+    f8192, b8192 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=8192)
+    assert b1024 == b4096 == b8192
+    assert f1024 == f4096 == f8192
     # gradient block rows x vslab bf16 follows chunk when vslab is given
     # (grad_h skipped so that no vocabulary-split partial sums enter)
     _, b_small = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024, vslab=4096,
