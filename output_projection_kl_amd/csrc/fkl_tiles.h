@@ -76,8 +76,6 @@ __device__ __forceinline__ int xcd_contiguous_range(int w, int first, int count)
   return before + (w - fx) / kXcds;
 }
 
-// One 256 x 256 output tile of C (+)= A B^T; `local` is this workgroup's
-// index among the problem's tiles (XCD-renumbered).
 // 256 x 64 output tile of C (+)= A B^T: 8 waves of 32 x 64, fp32 epilogue
 // through a 256 x 64 LDS tile (stride kNarrowLd), old values loaded first.
 constexpr int kNarrowN = 64;
@@ -129,6 +127,9 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
   __syncthreads();
 }
 
+// One output tile of C (+)= A B^T (256 x 256, or 256 x 64 for a last column
+// block of at most 64 columns); `local` is this workgroup's index among the
+// problem's tiles (XCD-renumbered).
 template <bool TA, bool TB>
 __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local, char* lds) {
   const int tid = threadIdx.x;
