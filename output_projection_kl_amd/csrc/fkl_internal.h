@@ -95,7 +95,7 @@ class TraceScope {
 
  private:
   hipStream_t stream_;
-  int slot_;
+  uint64_t id_;  // 0: not traced
 };
 
 // Teacher-cache builder (fkl_topk): rows per pass and the fp32 logits block.

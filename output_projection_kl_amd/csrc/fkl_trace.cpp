@@ -2,6 +2,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <iterator>
 #include <map>
 #include <mutex>
 #include <string>
@@ -18,11 +19,14 @@ struct Record {
   hipEvent_t stop = nullptr;
   double flops = 0.0;
   double bytes = 0.0;
+  uint64_t id = 0;
+  bool closed = false;  // stop event recorded
 };
 
 std::atomic<bool> g_enabled{false};
 std::mutex g_mu;
 std::vector<Record> g_records;
+uint64_t g_next_id = 1;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_pool;
 
 std::pair<hipEvent_t, hipEvent_t> take_events() {
@@ -45,7 +49,7 @@ std::pair<hipEvent_t, hipEvent_t> take_events() {
 namespace fkl {
 
 TraceScope::TraceScope(hipStream_t stream, const char* name, double flops, double bytes)
-    : stream_(stream), slot_(-1) {
+    : stream_(stream), id_(0) {
   if (!g_enabled.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
   auto ev = take_events();
@@ -60,14 +64,26 @@ TraceScope::TraceScope(hipStream_t stream, const char* name, double flops, doubl
   r.stop = ev.second;
   r.flops = flops;
   r.bytes = bytes;
+  r.id = g_next_id++;
+  id_ = r.id;
   g_records.push_back(r);
-  slot_ = static_cast<int>(g_records.size()) - 1;
 }
 
+// The scope closes its own record, found by id: a concurrent fkl_trace_read
+// takes only closed records, so an open one stays in g_records until here.
 TraceScope::~TraceScope() {
-  if (slot_ < 0) return;
+  if (id_ == 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (slot_ < static_cast<int>(g_records.size())) (void)hipEventRecord(g_records[slot_].stop, stream_);
+  for (auto it = g_records.rbegin(); it != g_records.rend(); ++it) {
+    if (it->id == id_) {
+      if (hipEventRecord(it->stop, stream_) == hipSuccess) it->closed = true;
+      else {
+        g_pool.emplace_back(it->start, it->stop);
+        g_records.erase(std::next(it).base());
+      }
+      return;
+    }
+  }
 }
 
 }  // namespace fkl
@@ -81,10 +97,13 @@ fkl_status fkl_trace_enable(int on) {
 
 fkl_status fkl_trace_read(fkl_kernel_stat* stats, int capacity, int* count) {
   if (capacity < 0 || (capacity > 0 && !stats)) return FKL_EINVAL;
+  // Closed records only; scopes still open on other threads keep theirs.
   std::vector<Record> recs;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    recs.swap(g_records);
+    std::vector<Record> open;
+    for (auto& r : g_records) (r.closed ? recs : open).push_back(std::move(r));
+    g_records.swap(open);
   }
   std::map<std::string, fkl_kernel_stat> agg;
   std::vector<std::string> order;
