@@ -193,17 +193,24 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream():
+def _stream(device=None):
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, shape):
+def _on(device):
+    """Makes `device` current for a library call (its kernels run on the current device)."""
+    return _torch().cuda.device(device)
+
+
+def _need(t, name, dtype, shape, device=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, like h; got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -220,33 +227,40 @@ def _inputs(h, W, t_idx, t_logit, mask):
     V = W.shape[0]
     K = t_idx.shape[1]
     _need(h, "h", torch.bfloat16, (N, d))
-    _need(W, "W", torch.bfloat16, (V, d))
-    _need(t_idx, "t_idx", torch.int32, (N, K))
-    _need(t_logit, "t_logit", torch.float32, (N, K))
+    dev = h.device
+    _need(W, "W", torch.bfloat16, (V, d), dev)
+    _need(t_idx, "t_idx", torch.int32, (N, K), dev)
+    _need(t_logit, "t_logit", torch.float32, (N, K), dev)
     if mask is not None:
-        _need(mask, "mask", torch.uint8, (N,))
+        _need(mask, "mask", torch.uint8, (N,), dev)
     return N, d, V, K
 
 
-def _terms(N, V, row_weight, label, label_weight):
+def _terms(N, V, row_weight, label, label_weight, device=None):
     """ctypes fkl_terms for the optional loss terms, or None for the plain loss."""
     torch = _torch()
     if row_weight is None and label is None:
         return None
     if row_weight is not None:
-        _need(row_weight, "row_weight", torch.float32, (N,))
+        _need(row_weight, "row_weight", torch.float32, (N,), device)
     if label is not None:
-        _need(label, "label", torch.int32, (N,))
+        _need(label, "label", torch.int32, (N,), device)
     return Terms(_ptr(row_weight), _ptr(label), float(label_weight))
 
 
 def _workspace(nbytes, device, workspace):
     torch = _torch()
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
+        if _nbytes(workspace) < nbytes:
             raise ValueError(f"workspace needs {nbytes} bytes")
         return workspace
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vslab: int = 0,
@@ -259,24 +273,25 @@ def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vsl
     variants of include/fkl.h (weighted mean; KL mixed with hard-label CE)."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
-    terms = _terms(N, V, row_weight, label, label_weight)
+    terms = _terms(N, V, row_weight, label, label_weight, h.device)
     s = make_shape(N, d, V, K, T, chunk, vslab)
     fb, _ = workspace_size(N, d, V, K, T, chunk, vslab)
     ws = _workspace(fb, h.device, workspace)
     if loss is None:
         loss = torch.empty(1, dtype=torch.float32, device=h.device)
-    _need(loss, "loss", torch.float32, (1,))
+    _need(loss, "loss", torch.float32, (1,), h.device)
     if row_lse is None:
         row_lse = torch.empty(N, dtype=torch.float32, device=h.device)
-    _need(row_lse, "row_lse", torch.float32, (N,))
+    _need(row_lse, "row_lse", torch.float32, (N,), h.device)
     if return_row_kl and row_kl is None:
         row_kl = torch.empty(N, dtype=torch.float32, device=h.device)
     if row_kl is not None:
-        _need(row_kl, "row_kl", torch.float32, (N,))
+        _need(row_kl, "row_kl", torch.float32, (N,), h.device)
         return_row_kl = True
-    _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
-                             None if terms is None else ctypes.byref(terms), _ptr(loss), _ptr(row_lse), _ptr(row_kl), _ptr(ws),
-                             ctypes.c_size_t(ws.numel()), _stream()))
+    with _on(h.device):
+        _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
+                                 None if terms is None else ctypes.byref(terms), _ptr(loss), _ptr(row_lse),
+                                 _ptr(row_kl), _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream(h.device)))
     return (loss, row_lse, row_kl) if return_row_kl else (loss, row_lse)
 
 
@@ -290,10 +305,10 @@ def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss
     the passed tensor is added to instead of overwritten."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
-    _need(row_lse, "row_lse", torch.float32, (N,))
+    _need(row_lse, "row_lse", torch.float32, (N,), h.device)
     if grad_loss is not None:
-        _need(grad_loss, "grad_loss", torch.float32, (1,))
-    terms = _terms(N, V, row_weight, label, label_weight)
+        _need(grad_loss, "grad_loss", torch.float32, (1,), h.device)
+    terms = _terms(N, V, row_weight, label, label_weight, h.device)
     if grad_h_dtype is None:
         grad_h_dtype = grad_h.dtype if grad_h is not None else torch.float32
     if grad_h_dtype not in (torch.float32, torch.bfloat16):
@@ -311,16 +326,18 @@ def backward(h, W, t_idx, t_logit, row_lse, T: float = 1.0, mask=None, grad_loss
     elif grad_h is None:
         grad_h = torch.empty((N, d), dtype=grad_h_dtype, device=h.device)
     else:
-        _need(grad_h, "grad_h", grad_h_dtype, (N, d))
+        _need(grad_h, "grad_h", grad_h_dtype, (N, d), h.device)
     if not need_grad_W:
         grad_W = None
     elif grad_W is None:
         grad_W = torch.empty((V, d), dtype=torch.float32, device=h.device)
     else:
-        _need(grad_W, "grad_W", torch.float32, (V, d))
-    _check(lib().fkl_backward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
-                              None if terms is None else ctypes.byref(terms), _ptr(row_lse), _ptr(grad_loss), _ptr(grad_h), _ptr(grad_W), _ptr(ws),
-                              ctypes.c_size_t(ws.numel()), _stream()))
+        _need(grad_W, "grad_W", torch.float32, (V, d), h.device)
+    with _on(h.device):
+        _check(lib().fkl_backward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
+                                  None if terms is None else ctypes.byref(terms), _ptr(row_lse), _ptr(grad_loss),
+                                  _ptr(grad_h), _ptr(grad_W), _ptr(ws), ctypes.c_size_t(_nbytes(ws)),
+                                  _stream(h.device)))
     return grad_h, grad_W
 
 
@@ -370,10 +387,12 @@ def validate_teacher(t_idx, t_logit, V: int) -> int:
     torch = _torch()
     N, K = t_idx.shape
     _need(t_idx, "t_idx", torch.int32, (N, K))
-    _need(t_logit, "t_logit", torch.float32, (N, K))
+    _need(t_logit, "t_logit", torch.float32, (N, K), t_idx.device)
     s = make_shape(N, 8, V, K, 1.0)
     bad = torch.empty(1, dtype=torch.int32, device=t_idx.device)
-    _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad), _stream()))
+    with _on(t_idx.device):
+        _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad),
+                                          _stream(t_idx.device)))
     return int(bad.item())
 
 
@@ -396,19 +415,20 @@ def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None,
     N, d = h.shape
     V = W.shape[0]
     _need(h, "h", torch.bfloat16, (N, d))
-    _need(W, "W", torch.bfloat16, (V, d))
+    _need(W, "W", torch.bfloat16, (V, d), h.device)
     s = TopkShape(N, d, V, K, chunk, TOPK_DIRECT if direct else 0)
     b = ctypes.c_size_t(0)
     _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
     ws = _workspace(b.value, h.device, workspace)
     if t_idx is None:
         t_idx = torch.empty((N, K), dtype=torch.int32, device=h.device)
-    _need(t_idx, "t_idx", torch.int32, (N, K))
+    _need(t_idx, "t_idx", torch.int32, (N, K), h.device)
     if t_logit is None:
         t_logit = torch.empty((N, K), dtype=torch.float32, device=h.device)
-    _need(t_logit, "t_logit", torch.float32, (N, K))
-    _check(lib().fkl_topk(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(ws),
-                          ctypes.c_size_t(ws.numel()), _stream()))
+    _need(t_logit, "t_logit", torch.float32, (N, K), h.device)
+    with _on(h.device):
+        _check(lib().fkl_topk(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(ws),
+                              ctypes.c_size_t(_nbytes(ws)), _stream(h.device)))
     return t_idx, t_logit
 
 

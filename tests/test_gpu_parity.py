@@ -306,6 +306,26 @@ def test_caller_workspace_reuse():
     assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
 
 
+def test_workspace_of_any_dtype_is_sized_in_bytes():
+    """A caller's workspace is measured in bytes whatever its dtype; one a byte short is refused."""
+    dev = _dev()
+    wl = make_workload("tiny", seed_offset=4)
+    h, W, ti, tl, m = _upload(wl, dev)
+    fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, 1.0, chunk=64)
+    nb = max(fb, bb)
+    ws = torch.empty((nb + 3) // 4, dtype=torch.float32, device=dev)
+    l1, lse1 = fkl.forward(h, W, ti, tl, chunk=64, workspace=ws)
+    g1 = fkl.backward(h, W, ti, tl, lse1, chunk=64, workspace=ws)
+    l2, lse2 = fkl.forward(h, W, ti, tl, chunk=64)
+    g2 = fkl.backward(h, W, ti, tl, lse2, chunk=64)
+    torch.cuda.synchronize()
+    assert l1.item() == l2.item()
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
+    short = torch.empty(fb - 1, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError):
+        fkl.forward(h, W, ti, tl, chunk=64, workspace=short)
+
+
 @pytest.mark.parametrize("T", [0.5, 1.0])
 def test_wide_logit_range(T):
     """Logit scale grows ~400x across the vocabulary (row maxima in the last
