@@ -236,7 +236,9 @@ fkl_status fkl_trace_enable(int on);
 /*
  * Waits for the recorded events, aggregates them per kernel name into
  * stats[0 .. min(capacity, kinds)), sets *count to the number of kernel
- * names seen, and clears the record. Host-synchronising.
+ * names seen, and clears the record. Host-synchronising. Thread-safe: a
+ * launch still being enqueued on another thread is left for a later read,
+ * so each launch is reported exactly once.
  */
 fkl_status fkl_trace_read(fkl_kernel_stat* stats, int capacity, int* count);
 
