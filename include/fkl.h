@@ -33,10 +33,15 @@
  *   - h, W, grad_h and grad_W must be 16-byte aligned; every other array
  *     4-byte aligned.
  *   - d must be a multiple of 8; 1 <= K <= min(V, 1024); T > 0 and finite.
- *   - Teacher indices must lie in [0, V) and be distinct within each row
- *     (checked only by fkl_validate_teacher); t_logit finite.
+ *   - Teacher indices must lie in [0, V) and be distinct within each row;
+ *     t_logit finite. Checked by fkl_validate_teacher, and by fkl_forward and
+ *     fkl_backward themselves when the environment sets FKL_VALIDATE=1: they
+ *     then return FKL_EINDEX for bad lists (a debugging aid that waits for
+ *     the stream on the host). Bad lists never make the kernels access memory
+ *     out of bounds; the loss and gradients are then undefined.
  *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream)
- *     and is complete when the stream is. No call synchronises the host.
+ *     and is complete when the stream is. No call synchronises the host
+ *     (except under FKL_VALIDATE=1).
  *   - Argument errors are reported before any device work is enqueued; such
  *     calls never touch the device, so they are safe without a GPU.
  *   - The same workspace must not be used by two calls in flight at once.
@@ -55,7 +60,7 @@ typedef enum {
   FKL_OK = 0,
   FKL_EINVAL = 1,       /* bad shape, NULL or misaligned pointer */
   FKL_EWORKSPACE = 2,   /* workspace NULL or smaller than fkl_workspace_size() */
-  FKL_EINDEX = 3,       /* reserved for teacher-data errors */
+  FKL_EINDEX = 3,       /* bad teacher lists (FKL_VALIDATE=1) */
   FKL_EDEVICE = 4,      /* a HIP call failed; see fkl_last_error() */
   FKL_EUNSUPPORTED = 5  /* shape outside what this build supports */
 } fkl_status;

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -33,6 +34,31 @@ fkl_status read_terms(const fkl_terms* t, const float** weight, const int32_t** 
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// With FKL_VALIDATE=1 in the environment, fkl_forward and fkl_backward first
+// check the teacher lists on the device (the checks of fkl_validate_teacher)
+// and refuse bad ones with FKL_EINDEX. This waits for `stream` on the host: a
+// debugging aid, not for graph capture.
+fkl_status validate_if_asked(const fkl::Plan& p, const int32_t* t_idx, const float* t_logit, char* ws,
+                             hipStream_t stream) {
+  const char* v = std::getenv("FKL_VALIDATE");
+  if (!v || std::strcmp(v, "1") != 0 || p.N == 0) return FKL_OK;
+  int32_t* bad = reinterpret_cast<int32_t*>(ws + p.off_scalars + fkl::kValidateCountOffset);
+  hipError_t e = fkl::launch_validate(p.N, p.V, p.K, t_idx, t_logit, bad, stream);
+  int32_t host_bad = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&host_bad, bad, sizeof(host_bad), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    g_last_error = std::string("teacher validation failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  if (host_bad > 0) {
+    g_last_error = std::to_string(host_bad) +
+                   " teacher rows have an index outside [0, V), a repeated index or a non-finite logit";
+    return FKL_EINDEX;
+  }
+  return FKL_OK;
+}
 
 }  // namespace
 
@@ -202,6 +228,8 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
   if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
+  st = validate_if_asked(p, t_idx, t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  if (st != FKL_OK) return st;
   fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, loss, row_lse, row_kl, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_forward(p, a, static_cast<hipStream_t>(stream));
@@ -243,6 +271,8 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.bwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
   if (!want_w && !want_h) return FKL_OK;  // nothing asked for
+  st = validate_if_asked(p, t_idx, t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  if (st != FKL_OK) return st;
   fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_backward(p, a, static_cast<hipStream_t>(stream));

@@ -43,6 +43,10 @@ struct Plan {
 
 constexpr int kCombineRows = 16;  // rows per workgroup of the forward's split merge
 
+// Byte offset, in the workspace's 256-byte scalars block, of the int32 bad-row
+// count that FKL_VALIDATE=1 uses (the block's loss accumulators sit below it).
+constexpr size_t kValidateCountOffset = 128;
+
 constexpr int kMaxGradHSplits = 8;
 
 // Vocabulary splits for the grad_h tiles of one backward launch (rows of the

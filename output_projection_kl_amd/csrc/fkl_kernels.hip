@@ -38,6 +38,7 @@ struct Scalars {
   int64_t n_valid;  // number of valid rows
   double wsum;      // sum over rows of mask x row weight (= n_valid without weights)
 };
+static_assert(sizeof(Scalars) <= kValidateCountOffset, "scalars overlap the validation count");
 
 // ---------------------------------------------------------------------------
 // Small kernels

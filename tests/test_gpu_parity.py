@@ -290,6 +290,30 @@ def test_validate_teacher():
     assert n_bad == 4
 
 
+def test_validate_environment_refuses_bad_teacher(monkeypatch):
+    """FKL_VALIDATE=1: forward and backward check the teacher lists first and
+    refuse a repeated index with FKL_EINDEX; good lists give the usual results."""
+    dev = _dev()
+    wl = make_workload("tiny", N=64, d=64, V=500, K=9)
+    h, W, ti, tl, m = _upload(wl, dev)
+    l0, lse0 = fkl.forward(h, W, ti, tl)
+    g0 = fkl.backward(h, W, ti, tl, lse0)
+    bad_i = wl.t_idx.copy()
+    bad_i[3, 2] = bad_i[3, 5]
+    bad = torch.from_numpy(bad_i).to(dev)
+    monkeypatch.setenv("FKL_VALIDATE", "1")
+    l1, lse1 = fkl.forward(h, W, ti, tl)
+    g1 = fkl.backward(h, W, ti, tl, lse1)
+    torch.cuda.synchronize()
+    assert l1.item() == l0.item() and torch.equal(g1[0], g0[0]) and torch.equal(g1[1], g0[1])
+    with pytest.raises(fkl.FklError) as e:
+        fkl.forward(h, W, bad, tl)
+    assert e.value.status == 3 and "1 teacher rows" in str(e.value)
+    with pytest.raises(fkl.FklError) as e:
+        fkl.backward(h, W, bad, tl, lse1)
+    assert e.value.status == 3
+
+
 def test_caller_workspace_reuse():
     """One workspace buffer serves repeated calls; results match fresh allocations."""
     dev = _dev()
