@@ -299,9 +299,12 @@ def topk_teacher(h, W, K: int):
 
 
 def _weights(mask, row_weight, N: int) -> np.ndarray:
-    """Per-row weight: row_weight (1 if absent) times the mask (1 if absent)."""
+    """Per-row weight: row_weight (1 if absent) on unmasked rows. A row whose
+    weight is not positive (zero, negative or NaN) takes no part in the loss,
+    like a masked row (reading R10: weights generalise the 0/1 mask)."""
     w = np.ones(N) if row_weight is None else _f64(row_weight).reshape(N)
-    return np.where(_valid_rows(mask, N), w, 0.0)
+    keep = _valid_rows(mask, N) & (w > 0)
+    return np.where(keep, w, 0.0)
 
 
 def forward_terms(h, W, t_idx, t_logit, T: float = 1.0, mask=None, row_weight=None, label=None,

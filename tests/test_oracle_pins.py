@@ -533,3 +533,28 @@ def test_pins_catch_planted_gradient_mistakes(kind):
     gW = G.T @ h if kind != "transposed" else (h.T @ G).T[::-1]
     bad = (not np.allclose(gh, gh_t, rtol=1e-8, atol=1e-12)) or (not np.allclose(gW, gW_t, rtol=1e-8, atol=1e-12))
     assert bad
+
+
+def test_loss_terms_nonpositive_weight_drops_the_row():
+    """A zero, negative or NaN weight leaves the row out entirely, exactly as
+    the sub-batch without it (the masking pin P11 for weights)."""
+    rng = np.random.default_rng(77)
+    N, d, V, K, T = 12, 16, 48, 5, 1.3
+    h = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d)) / 4
+    t_idx = np.stack([rng.choice(V, K, replace=False) for _ in range(N)])
+    t_logit = rng.standard_normal((N, K)) * 3
+    w = rng.uniform(0.5, 2.0, N)
+    w[[2, 7, 9]] = [0.0, -1.5, np.nan]
+    keep = np.ones(N, bool)
+    keep[[2, 7, 9]] = False
+    loss, lse, row_l = oracle.forward_terms(h, W, t_idx, t_logit, T, row_weight=w)
+    ref_loss, _, ref_l = oracle.forward_terms(h[keep], W, t_idx[keep], t_logit[keep], T, row_weight=w[keep])
+    assert abs(loss - ref_loss) <= 1e-12 * abs(ref_loss)
+    assert np.all(row_l[~keep] == 0.0)
+    np.testing.assert_allclose(row_l[keep], ref_l, rtol=1e-12, atol=0)
+    gh, gW = oracle.backward_terms(h, W, t_idx, t_logit, T, row_weight=w)
+    rgh, rgW = oracle.backward_terms(h[keep], W, t_idx[keep], t_logit[keep], T, row_weight=w[keep])
+    assert np.all(gh[~keep] == 0.0)
+    np.testing.assert_allclose(gh[keep], rgh, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(gW, rgW, rtol=1e-10, atol=1e-14)
