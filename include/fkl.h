@@ -60,7 +60,7 @@ typedef enum {
   FKL_OK = 0,
   FKL_EINVAL = 1,       /* bad shape, NULL or misaligned pointer */
   FKL_EWORKSPACE = 2,   /* workspace NULL or smaller than fkl_workspace_size() */
-  FKL_EINDEX = 3,       /* bad teacher lists (FKL_VALIDATE=1) */
+  FKL_EINDEX = 3,       /* bad teacher lists or loss terms (FKL_VALIDATE=1) */
   FKL_EDEVICE = 4,      /* a HIP call failed; see fkl_last_error() */
   FKL_EUNSUPPORTED = 5  /* shape outside what this build supports */
 } fkl_status;
@@ -111,14 +111,19 @@ typedef struct {
  * "choice of loss function" for the distillation loss without defining
  * variants; these are the ones the fused structure carries at no extra
  * contraction work:
- *   row_weight   fp32 [N] per-token weights w_r >= 0 (finite), multiplied by
- *                the row mask; NULL means 1. The loss is the weighted mean
- *                T^2 sum_r w_r l_r / sum_r w_r (0 when the sum is 0).
- *   label        int32 [N] hard labels y_r in [0, V) (precondition, not
- *                checked); NULL means no label term.
+ *   row_weight   fp32 [N] per-token weights (finite), multiplied by the row
+ *                mask; NULL means 1. A row whose weight is not positive
+ *                (zero, negative or NaN) takes no part, as if masked. The
+ *                loss is the weighted mean T^2 sum_r w_r l_r / sum_r w_r over
+ *                the rows with w_r > 0 (0 when there are none).
+ *   label        int32 [N] hard labels y_r in [0, V) (precondition, checked
+ *                by fkl_validate_terms and under FKL_VALIDATE=1; a label
+ *                outside the range never makes a kernel access memory out of
+ *                bounds, the loss is then undefined); NULL means no label
+ *                term.
  *   label_weight a in [0, 1]: per row l_r = (1 - a) KL(p_r || q_r) +
  *                a CE(y_r, q_r), both at the loss temperature (q = softmax(z/T)).
- * row_kl then reports l_r (0 where w_r = 0).
+ * row_kl then reports l_r (0 where w_r <= 0 or the row is masked).
  */
 typedef struct {
   const float* row_weight;
@@ -128,21 +133,72 @@ typedef struct {
 
 /*
  * Workspace bytes needed by fkl_forward and fkl_backward for this shape.
- * Pure host code. The sizes depend on the pass sizes, vslab, K, d and
- * flags, on N only where N is below a pass, and on V only through one slab:
- * with R the backward pass rows (chunk member), forward O(R * (K + 64)),
- * backward O(R * (vslab + K)), plus O(R * d) fp32 when a pass's grad_h is
- * split along the vocabulary (few rows per pass) or returned in bf16.
- * Shapes whose h pass (R x d bf16), W slab (vslab x d bf16) or
- * gradient block (R x vslab bf16) would exceed 2 GiB return
- * FKL_EUNSUPPORTED; the default vslab is capped to stay below.
+ *
+ * Defined by: the blog post, section "Two systems changes" (only one chunk
+ * of positions is ever in flight, so the extra memory is bounded by a
+ * chunk's working set) and section "Scaling to long context lengths" (peak
+ * memory of the fused loss grows with the sequence only through its inputs
+ * and outputs). Here no [chunk x V] block exists at all: a forward pass
+ * needs its teacher lists and split statistics, a backward pass the bf16
+ * gradient block of one vocabulary slab.
+ *
+ * Arguments: shape (host pointer, read only); fwd_bytes, bwd_bytes (host
+ * pointers, either may be NULL) receive the byte counts. One workspace of
+ * max(fwd_bytes, bwd_bytes) serves both calls. Pure host code: no HIP call.
+ * Sizes: with R the pass rows and S the slab (fkl_plan_info), forward
+ * O(R * (K + 64)), backward O(R * (S + K)), plus O(R * d) fp32 when a pass's
+ * grad_h is split along the vocabulary (few rows per pass) or returned in
+ * bf16; N enters only below one pass, V only through one slab.
+ * Errors: FKL_EINVAL for a NULL or malformed shape; FKL_EUNSUPPORTED when an
+ * h pass (R x d bf16), W slab (S x d bf16) or gradient block (R x S bf16)
+ * would exceed 2 GiB (the default slab is capped to stay below).
  */
 fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t* bwd_bytes);
 
 /*
- * Forward pass: loss (fp32 [1]), row_lse (fp32 [N], logsumexp over the
- * vocabulary of s = z/T, for every row including masked ones) and, if
- * row_kl is not NULL, the per-row KL (fp32 [N], 0 on masked rows).
+ * How a shape is run (host only): rows per forward and backward pass,
+ * vocabulary columns per backward slab, the pass and slab counts, and the
+ * workspace sizes of fkl_workspace_size. Results never depend on these;
+ * they describe the memory and launch plan (blog post, section "Two systems
+ * changes": the loss walks the positions one chunk at a time).
+ * Errors: those of fkl_workspace_size; FKL_EINVAL if plan is NULL.
+ */
+typedef struct {
+  int64_t fwd_rows;   /* rows per forward pass */
+  int64_t bwd_rows;   /* rows per backward pass */
+  int64_t vslab;      /* vocabulary columns per backward slab */
+  int64_t fwd_passes; /* ceil(N / fwd_rows) (0 when N = 0) */
+  int64_t bwd_passes; /* ceil(N / bwd_rows) (0 when N = 0) */
+  int64_t slabs;      /* ceil(V / vslab) */
+  size_t fwd_bytes;   /* workspace bytes of fkl_forward */
+  size_t bwd_bytes;   /* workspace bytes of fkl_backward */
+} fkl_plan;
+
+fkl_status fkl_plan_info(const fkl_shape* shape, fkl_plan* plan);
+
+/*
+ * Forward pass of the fused loss.
+ *
+ * Defined by: the blog post, section "Two systems changes": the output
+ * projection is fused into the loss, so the call takes the hidden states
+ * and the head weight rather than logits; it walks the positions one chunk
+ * at a time, projects the chunk to logits, folds them into the running loss
+ * against the cached sparse top-K teacher and drops them. The loss is the
+ * KL term of a distillation step ("drop-in replacement for the KL term":
+ * page "Making knowledge distillation cheap enough to run in production").
+ *
+ * Inputs (device): h bf16 [N, d], W bf16 [V, d], t_idx int32 [N, K],
+ * t_logit fp32 [N, K], row_mask uint8 [N] or NULL, terms (host struct
+ * pointing at device arrays) or NULL.
+ * Outputs (device, caller-allocated, overwritten): loss fp32 [1]; row_lse
+ * fp32 [N], logsumexp over the vocabulary of s = z/T for every row including
+ * masked ones; row_kl fp32 [N] (the per-row loss term, 0 on rows that take
+ * no part) or NULL.
+ * workspace: device, 256-byte aligned, at least fwd_bytes of
+ * fkl_workspace_size; stream: hipStream_t (NULL = default stream).
+ * Errors: argument errors (NULL, misaligned, bad shape, short workspace)
+ * return before any device work; FKL_EDEVICE if a launch fails;
+ * FKL_EINDEX under FKL_VALIDATE=1 for bad teacher lists or loss terms.
  * Deterministic: the same inputs give bitwise the same outputs.
  */
 fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
@@ -151,12 +207,27 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass with recomputation of the logits. row_lse is the forward's
- * output for the same inputs. grad_loss is a device fp32 [1] holding g, or
- * NULL for g = 1. grad_h (fp32 [N, d], or bf16 with FKL_GRAD_H_BF16) and
- * grad_W (fp32 [V, d]) are overwritten, or accumulated into, as shape->flags
- * says. Masked rows get exactly zero grad_h rows (unchanged rows when
+ * Backward pass of the fused loss, with recomputation.
+ *
+ * Defined by: the blog post, section "Two systems changes": backward forms
+ * each chunk's logits again instead of storing them (the projection is done
+ * twice), and yields the gradients of the hidden states and of the head
+ * that the training step needs (page "Making knowledge distillation cheap
+ * enough to run in production": a drop-in replacement for the KL term).
+ * With G = dloss/dz (the closed form in this file's header), grad_h = G W
+ * and grad_W = G^T h.
+ *
+ * Inputs (device): as fkl_forward, plus row_lse fp32 [N] from the forward of
+ * the same inputs and grad_loss fp32 [1] holding the upstream gradient g
+ * (NULL: g = 1).
+ * Outputs (device, caller-allocated): grad_h fp32 [N, d] (bf16 with
+ * FKL_GRAD_H_BF16) and grad_W fp32 [V, d], overwritten or accumulated into
+ * as shape->flags says; either may be NULL when skipped. Rows that take no
+ * part in the loss get exactly zero grad_h rows (unchanged when
  * accumulating).
+ * workspace: device, 256-byte aligned, at least bwd_bytes of
+ * fkl_workspace_size; stream as fkl_forward.
+ * Errors: as fkl_forward. Deterministic: no floating-point atomics.
  */
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
                         const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
@@ -172,6 +243,16 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W,
  */
 fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx,
                                 const float* t_logit, int32_t* bad_rows, void* stream);
+
+/*
+ * Checks the optional loss terms on the device: every hard label in [0, V)
+ * and every row weight finite. Writes the number of offending rows to
+ * bad_rows (device int32 [1]). terms may be NULL (nothing to check: 0).
+ * Errors: FKL_EINVAL for a bad shape, a NULL or misaligned bad_rows, or a
+ * label_weight outside [0, 1]; FKL_EDEVICE if the launch fails.
+ */
+fkl_status fkl_validate_terms(const fkl_shape* shape, const fkl_terms* terms, int32_t* bad_rows,
+                              void* stream);
 
 /*
  * Offline teacher-cache builder: the step before the fused loss. The blog

@@ -27,6 +27,9 @@ __all__ = [
     "forward",
     "backward",
     "validate_teacher",
+    "validate_terms",
+    "plan_info",
+    "PlanInfo",
     "FusedKLLoss",
     "Terms",
     "ACCUMULATE_GRAD_W",
@@ -51,6 +54,8 @@ EXPORTED_SYMBOLS = (
     "fkl_forward",
     "fkl_backward",
     "fkl_validate_teacher",
+    "fkl_validate_terms",
+    "fkl_plan_info",
     "fkl_topk_workspace_size",
     "fkl_topk",
     "fkl_trace_enable",
@@ -106,6 +111,21 @@ class Terms(ctypes.Structure):
     ]
 
 
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``fkl_plan``."""
+
+    _fields_ = [
+        ("fwd_rows", ctypes.c_int64),
+        ("bwd_rows", ctypes.c_int64),
+        ("vslab", ctypes.c_int64),
+        ("fwd_passes", ctypes.c_int64),
+        ("bwd_passes", ctypes.c_int64),
+        ("slabs", ctypes.c_int64),
+        ("fwd_bytes", ctypes.c_size_t),
+        ("bwd_bytes", ctypes.c_size_t),
+    ]
+
+
 class TopkShape(ctypes.Structure):
     """Mirror of ``fkl_topk_shape``."""
 
@@ -141,12 +161,15 @@ def lib() -> ctypes.CDLL:
     L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
+    L.fkl_validate_terms.argtypes = [shp, ctypes.POINTER(Terms), vp, vp]
+    L.fkl_plan_info.argtypes = [shp, ctypes.POINTER(PlanInfo)]
     tshp = ctypes.POINTER(TopkShape)
     L.fkl_topk_workspace_size.argtypes = [tshp, ctypes.POINTER(sz)]
     L.fkl_topk.argtypes = [tshp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_trace_enable.argtypes = [ctypes.c_int]
     L.fkl_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
-    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_version",
+    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_validate_terms",
+              "fkl_plan_info", "fkl_version",
               "fkl_topk_workspace_size", "fkl_topk", "fkl_trace_enable", "fkl_trace_read"):
         getattr(L, f).restype = ctypes.c_int
     L.fkl_status_string.argtypes = [ctypes.c_int]
@@ -182,6 +205,15 @@ def workspace_size(N, d, V, K, T=1.0, chunk=0, vslab=0, flags=0):
     s = make_shape(N, d, V, K, T, chunk, vslab, flags)
     _check(lib().fkl_workspace_size(ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)))
     return f.value, b.value
+
+
+def plan_info(N, d, V, K, T=1.0, chunk=0, vslab=0, flags=0) -> dict:
+    """How the library runs this shape: rows per forward / backward pass, the
+    backward slab, pass and slab counts, workspace bytes (host only)."""
+    s = make_shape(N, d, V, K, T, chunk, vslab, flags)
+    p = PlanInfo()
+    _check(lib().fkl_plan_info(ctypes.byref(s), ctypes.byref(p)))
+    return {f: int(getattr(p, f)) for f, _ in PlanInfo._fields_}
 
 
 def _torch():
@@ -393,6 +425,20 @@ def validate_teacher(t_idx, t_logit, V: int) -> int:
     with _on(t_idx.device):
         _check(lib().fkl_validate_teacher(ctypes.byref(s), _ptr(t_idx), _ptr(t_logit), _ptr(bad),
                                           _stream(t_idx.device)))
+    return int(bad.item())
+
+
+def validate_terms(N: int, V: int, row_weight=None, label=None, label_weight: float = 0.0) -> int:
+    """Number of rows whose hard label lies outside [0, V) or whose weight is not finite."""
+    torch = _torch()
+    ref = row_weight if row_weight is not None else label
+    if ref is None:
+        return 0
+    terms = _terms(N, V, row_weight, label, label_weight, ref.device)
+    s = make_shape(N, 8, V, 1, 1.0)
+    bad = torch.empty(1, dtype=torch.int32, device=ref.device)
+    with _on(ref.device):
+        _check(lib().fkl_validate_terms(ctypes.byref(s), ctypes.byref(terms), _ptr(bad), _stream(ref.device)))
     return int(bad.item())
 
 

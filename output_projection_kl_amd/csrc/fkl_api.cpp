@@ -39,12 +39,13 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // check the teacher lists on the device (the checks of fkl_validate_teacher)
 // and refuse bad ones with FKL_EINDEX. This waits for `stream` on the host: a
 // debugging aid, not for graph capture.
-fkl_status validate_if_asked(const fkl::Plan& p, const int32_t* t_idx, const float* t_logit, char* ws,
-                             hipStream_t stream) {
+fkl_status validate_if_asked(const fkl::Plan& p, const int32_t* t_idx, const float* t_logit,
+                             const float* weight, const int32_t* label, char* ws, hipStream_t stream) {
   const char* v = std::getenv("FKL_VALIDATE");
   if (!v || std::strcmp(v, "1") != 0 || p.N == 0) return FKL_OK;
   int32_t* bad = reinterpret_cast<int32_t*>(ws + p.off_scalars + fkl::kValidateCountOffset);
   hipError_t e = fkl::launch_validate(p.N, p.V, p.K, t_idx, t_logit, bad, stream);
+  if (e == hipSuccess) e = fkl::launch_validate_terms(p.N, p.V, weight, label, bad, false, stream);
   int32_t host_bad = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(&host_bad, bad, sizeof(host_bad), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -54,7 +55,8 @@ fkl_status validate_if_asked(const fkl::Plan& p, const int32_t* t_idx, const flo
   }
   if (host_bad > 0) {
     g_last_error = std::to_string(host_bad) +
-                   " teacher rows have an index outside [0, V), a repeated index or a non-finite logit";
+                   " rows rejected: a teacher index outside [0, V) or repeated within the row, a"
+                   " non-finite teacher logit, a hard label outside [0, V) or a non-finite weight";
     return FKL_EINDEX;
   }
   return FKL_OK;
@@ -63,6 +65,20 @@ fkl_status validate_if_asked(const fkl::Plan& p, const int32_t* t_idx, const flo
 }  // namespace
 
 namespace fkl {
+
+int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d) {
+  if (rows <= 0 || slab_w <= 0) return 1;
+  const int64_t nb = ceil_div(d, kTile);
+  const int64_t h_tiles = ceil_div(rows, kTile) * nb;
+  const int64_t nk_h = ceil_div(slab_w, kContractionStep);
+  const int64_t w_tiles = ceil_div(slab_w, kTile) * nb;
+  const int64_t nk_w = ceil_div(rows, kContractionStep);
+  const int64_t per_cu = ceil_div(h_tiles * nk_h + w_tiles * nk_w, kTargetBlocks);
+  int64_t sp = ceil_div(nk_h, per_cu > 0 ? per_cu : 1);
+  if (sp < 1) sp = 1;
+  if (sp > kMaxGradHSplits) sp = kMaxGradHSplits;
+  return static_cast<int>(sp);
+}
 
 fkl_status make_plan(const fkl_shape* s, Plan* p) {
   if (!s) return fail(FKL_EINVAL, "shape is NULL");
@@ -228,7 +244,8 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
   if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
-  st = validate_if_asked(p, t_idx, t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  st = validate_if_asked(p, t_idx, t_logit, weight, label, static_cast<char*>(workspace),
+                         static_cast<hipStream_t>(stream));
   if (st != FKL_OK) return st;
   fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, loss, row_lse, row_kl, static_cast<char*>(workspace)};
@@ -271,7 +288,8 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.bwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
   if (!want_w && !want_h) return FKL_OK;  // nothing asked for
-  st = validate_if_asked(p, t_idx, t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  st = validate_if_asked(p, t_idx, t_logit, weight, label, static_cast<char*>(workspace),
+                         static_cast<hipStream_t>(stream));
   if (st != FKL_OK) return st;
   fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
@@ -298,6 +316,41 @@ fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx, co
     g_last_error = std::string("validate launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
+  return FKL_OK;
+}
+
+fkl_status fkl_validate_terms(const fkl_shape* shape, const fkl_terms* terms, int32_t* bad_rows, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (!bad_rows || !aligned(bad_rows, 4)) return fail(FKL_EINVAL, "bad_rows must be a 4-byte aligned pointer");
+  const float* weight;
+  const int32_t* label;
+  float label_w;
+  st = read_terms(terms, &weight, &label, &label_w);
+  if (st != FKL_OK) return st;
+  const hipError_t e =
+      fkl::launch_validate_terms(p.N, p.V, weight, label, bad_rows, true, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("validate launch failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return FKL_OK;
+}
+
+fkl_status fkl_plan_info(const fkl_shape* shape, fkl_plan* plan) {
+  fkl::Plan p;
+  const fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  if (!plan) return fail(FKL_EINVAL, "plan is NULL");
+  plan->fwd_rows = p.chunk;
+  plan->bwd_rows = p.bchunk;
+  plan->vslab = p.vslab;
+  plan->fwd_passes = p.N > 0 ? fkl::ceil_div(p.N, p.chunk) : 0;
+  plan->bwd_passes = p.N > 0 ? fkl::ceil_div(p.N, p.bchunk) : 0;
+  plan->slabs = fkl::ceil_div(p.V, p.vslab);
+  plan->fwd_bytes = p.fwd_bytes;
+  plan->bwd_bytes = p.bwd_bytes;
   return FKL_OK;
 }
 

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fkl_internal.h"
+
 namespace fkl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -56,7 +58,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // transposed stage.
 // ---------------------------------------------------------------------------
 
-constexpr int kStageK = 32;
+constexpr int kStageK = kContractionStep;
 constexpr int kARows = 256;                                    // A operand extent of a block tile
 constexpr int kAStageBytes = kARows * kStageK * 2;             // 16 KiB
 constexpr uint32_t kOob = 0x80000000u;                         // offset past every buffer

@@ -11,6 +11,7 @@
 namespace fkl {
 
 constexpr int kTile = 256;          // rows and vocabulary columns of one logits tile
+constexpr int kContractionStep = 32;  // contraction depth of one LDS stage of the MFMA mainloop
 constexpr int kTargetBlocks = 256;  // workgroups a launch aims for (one per CU on MI355X)
 constexpr int kDefaultChunk = 4096;
 constexpr int kPassRows = 8192;  // pass rows floor (forward and backward) with the default slab
@@ -122,5 +123,9 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx,
                            const float* t_logit, int32_t* bad_rows, hipStream_t stream);
+// Rows whose label is outside [0, V) or whose weight is not finite are added
+// to *bad_rows (cleared first when `clear`).
+hipError_t launch_validate_terms(int64_t N, int64_t V, const float* weight, const int32_t* label,
+                                 int32_t* bad_rows, bool clear, hipStream_t stream);
 
 }  // namespace fkl

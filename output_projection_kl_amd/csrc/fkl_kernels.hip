@@ -51,10 +51,14 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__
   __shared__ double wpart[256];
   int64_t cnt = 0;
   double ws = 0.0;
+  // A row counts when it is unmasked; its weight enters the sum only when
+  // positive, the rule every other kernel applies (a row whose weight is zero,
+  // negative or NaN takes no part in the loss).
   for (int64_t r = threadIdx.x; r < N; r += 256) {
     const bool valid = !mask || mask[r] != 0;
     cnt += valid;
-    ws += valid ? (weight ? static_cast<double>(weight[r]) : 1.0) : 0.0;
+    const float w = weight ? weight[r] : 1.0f;
+    ws += (valid && w > 0.f) ? static_cast<double>(w) : 0.0;
   }
   part[threadIdx.x] = cnt;
   wpart[threadIdx.x] = ws;
@@ -261,9 +265,11 @@ struct Cursor {
     }
   }
 
-  // Position at the first entry >= target: 16 evenly spaced samples locate
-  // the segment, then that segment is counted (two rounds of independent
-  // loads instead of a chain of dependent ones).
+  // Position at the first entry >= target in three rounds of loads: 16
+  // evenly spaced samples locate the segment, the segment is counted, then
+  // the window is loaded. Every load of a round is issued unconditionally
+  // (index clamped into the list, out-of-range results masked afterwards),
+  // so a round costs one memory latency rather than one per load.
   __device__ __forceinline__ void init(const int32_t* i, const float* pp, int k, int target, bool on) {
     idx = i;
     p = pp;
@@ -273,26 +279,44 @@ struct Cursor {
     p0 = p1 = p2 = p3 = 0.f;
     if (!on) return;
     const int seg = (K + 15) / 16;
+    int sample[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sample[j] = idx[min(j * seg, K - 1)];
     int c1 = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = j * seg;
-      if (kk < K) c1 += idx[kk] < target;
-    }
+    for (int j = 0; j < 16; ++j) c1 += (j * seg < K) & (sample[j] < target);
     int start = 0;
     if (c1 > 0) {
+      // the first entry >= target lies in ((c1 - 1) seg, c1 seg]
       const int lo = (c1 - 1) * seg + 1;
       const int hi = min(c1 * seg, K);
       int c2 = 0;
-#pragma unroll 8
-      for (int kk = lo; kk < hi; ++kk) c2 += idx[kk] < target;
+      for (int base = lo; base < hi; base += 8) {
+        int v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = idx[min(base + e, K - 1)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c2 += (base + e < hi) & (v[e] < target);
+      }
       start = lo + c2;
     }
     pos = start;
-    load_at(pos, e0, p0);
-    load_at(pos + 1, e1, p1);
-    load_at(pos + 2, e2, p2);
-    load_at(pos + 3, e3, p3);
+    int ev[4];
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kk = min(start + e, K - 1);
+      ev[e] = idx[kk];
+      pv[e] = p[kk];
+    }
+    e0 = start < K ? ev[0] : INT_MAX;
+    p0 = start < K ? pv[0] : 0.f;
+    e1 = start + 1 < K ? ev[1] : INT_MAX;
+    p1 = start + 1 < K ? pv[1] : 0.f;
+    e2 = start + 2 < K ? ev[2] : INT_MAX;
+    p2 = start + 2 < K ? pv[2] : 0.f;
+    e3 = start + 3 < K ? ev[3] : INT_MAX;
+    p3 = start + 3 < K ? pv[3] : 0.f;
   }
 
   __device__ __forceinline__ int cur() const { return e0; }
@@ -538,18 +562,27 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
   const int row = rb * kTile + rloc;
   const int64_t grow = P.r0 + row;
 
-  float c = 0.f, lse2 = 0.f;
-  if (row < P.rows) {
-    const double wsum = P.sc->wsum;
-    const float g = P.grad_loss ? P.grad_loss[0] : 1.0f;
-    const bool valid = !P.mask || P.mask[grow] != 0;
-    const float w = valid ? (P.weight ? P.weight[grow] : 1.0f) : 0.0f;
-    c = (w > 0.f && wsum > 0.0) ? static_cast<float>(static_cast<double>(g) * P.T * w / wsum) : 0.f;
-    lse2 = P.row_lse[grow] * kLog2e;
-  }
+  // The row's mask, weight and lse are loaded unconditionally (from lse's
+  // address where an optional array is absent) so that these loads and the
+  // cursor's first round are in flight together.
+  const bool row_in = row < P.rows;
+  const int64_t grow_c = row_in ? grow : P.r0;
+  const float* lse_p = P.row_lse + grow_c;
+  const uint8_t mraw = *(P.mask ? P.mask + grow_c : reinterpret_cast<const uint8_t*>(lse_p));
+  const float wraw = *(P.weight ? P.weight + grow_c : lse_p);
+  const float lse_r = *lse_p;
   Cursor cur;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
-           P.K, static_cast<int>(P.slab0) + vt0 * kTile, c != 0.f && vt0 < vt1);
+           P.K, static_cast<int>(P.slab0) + vt0 * kTile, row_in && vt0 < vt1);
+  float c = 0.f, lse2 = 0.f;
+  if (row_in) {
+    const double wsum = P.sc->wsum;
+    const float g = P.grad_loss ? P.grad_loss[0] : 1.0f;
+    const bool valid = !P.mask || mraw != 0;
+    const float w = valid ? (P.weight ? wraw : 1.0f) : 0.0f;
+    c = (w > 0.f && wsum > 0.0) ? static_cast<float>(static_cast<double>(g) * P.T * w / wsum) : 0.f;
+    lse2 = lse_r * kLog2e;
+  }
 
   const Operand A{P.h, P.d, P.r0 + P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
@@ -701,6 +734,22 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ t_
   }
 }
 
+// Loss-term validation: one thread per row; a row is bad when its hard label
+// lies outside [0, V) or its weight is not finite.
+__global__ __launch_bounds__(256) void k_validate_terms(const float* __restrict__ weight,
+                                                        const int32_t* __restrict__ label, int64_t N,
+                                                        int64_t V, int32_t* bad_rows) {
+  const int64_t r = blockIdx.x * 256LL + threadIdx.x;
+  bool bad = false;
+  if (r < N) {
+    if (label) bad |= label[r] < 0 || label[r] >= V;
+    if (weight) bad |= !isfinite(weight[r]);
+  }
+  const unsigned long long any = __ballot(bad);
+  const int n = __popcll(any);
+  if ((threadIdx.x & 63) == 0 && n > 0) atomicAdd(bad_rows, n);
+}
+
 __global__ void k_set_int(int32_t* p, int32_t v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = v;
 }
@@ -708,20 +757,6 @@ __global__ void k_set_int(int32_t* p, int32_t v) {
 // ---------------------------------------------------------------------------
 // Launch sequences
 // ---------------------------------------------------------------------------
-
-int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d) {
-  if (rows <= 0 || slab_w <= 0) return 1;
-  const int64_t nb = ceil_div(d, kTile);
-  const int64_t h_tiles = ceil_div(rows, kTile) * nb;
-  const int64_t nk_h = ceil_div(slab_w, kStageK);
-  const int64_t w_tiles = ceil_div(slab_w, kTile) * nb;
-  const int64_t nk_w = ceil_div(rows, kStageK);
-  const int64_t per_cu = ceil_div(h_tiles * nk_h + w_tiles * nk_w, kTargetBlocks);
-  int64_t sp = ceil_div(nk_h, per_cu > 0 ? per_cu : 1);
-  if (sp < 1) sp = 1;
-  if (sp > kMaxGradHSplits) sp = kMaxGradHSplits;
-  return static_cast<int>(sp);
-}
 
 static inline int splits_for(int64_t rbs, int64_t tiles) {
   int64_t s = ceil_div(kTargetBlocks, rbs);
@@ -901,6 +936,15 @@ hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx
   hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, st, bad_rows, 0);
   if (N > 0)
     hipLaunchKernelGGL(k_validate, dim3(ceil_div(N, 4)), dim3(256), 0, st, t_idx, t_logit, N, V, K,
+                       bad_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_terms(int64_t N, int64_t V, const float* weight, const int32_t* label,
+                                 int32_t* bad_rows, bool clear, hipStream_t st) {
+  if (clear) hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, st, bad_rows, 0);
+  if (N > 0 && (weight || label))
+    hipLaunchKernelGGL(k_validate_terms, dim3(ceil_div(N, 256)), dim3(256), 0, st, weight, label, N, V,
                        bad_rows);
   return hipGetLastError();
 }

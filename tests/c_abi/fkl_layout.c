@@ -25,6 +25,10 @@ int main(void) {
   FIELD(fkl_topk_shape, N); FIELD(fkl_topk_shape, d); FIELD(fkl_topk_shape, V); FIELD(fkl_topk_shape, K);
   FIELD(fkl_topk_shape, chunk); FIELD(fkl_topk_shape, flags);
   printf("\n");
+  printf("fkl_plan %zu", sizeof(fkl_plan));
+  FIELD(fkl_plan, fwd_rows); FIELD(fkl_plan, bwd_rows); FIELD(fkl_plan, vslab); FIELD(fkl_plan, fwd_passes);
+  FIELD(fkl_plan, bwd_passes); FIELD(fkl_plan, slabs); FIELD(fkl_plan, fwd_bytes); FIELD(fkl_plan, bwd_bytes);
+  printf("\n");
   printf("fkl_kernel_stat %zu", sizeof(fkl_kernel_stat));
   FIELD(fkl_kernel_stat, name); FIELD(fkl_kernel_stat, launches); FIELD(fkl_kernel_stat, total_ms);
   FIELD(fkl_kernel_stat, min_ms); FIELD(fkl_kernel_stat, max_ms); FIELD(fkl_kernel_stat, flops);
@@ -37,6 +41,12 @@ int main(void) {
   size_t fb = 0, bb = 0;
   fkl_status st = fkl_workspace_size(&s, &fb, &bb);
   printf("workspace %d %zu %zu\n", (int)st, fb, bb);
+  fkl_plan pl;
+  memset(&pl, 0, sizeof(pl));
+  st = fkl_plan_info(&s, &pl);
+  printf("plan %d %lld %lld %lld %lld %lld %lld %zu %zu\n", (int)st, (long long)pl.fwd_rows, (long long)pl.bwd_rows,
+         (long long)pl.vslab, (long long)pl.fwd_passes, (long long)pl.bwd_passes, (long long)pl.slabs,
+         pl.fwd_bytes, pl.bwd_bytes);
   fkl_topk_shape ts;
   memset(&ts, 0, sizeof(ts));
   ts.N = 16384; ts.d = 4096; ts.V = 128256; ts.K = 100;

@@ -232,3 +232,34 @@ def test_backward_pass_rows_follow_gradient_block():
     _, bn = fkl.workspace_size(300, 64, 1000, 5, 1.0, chunk=64)
     _, bn2 = fkl.workspace_size(300, 64, 1000, 5, 1.0, chunk=300)
     assert bn == bn2
+
+
+def test_plan_info_reports_the_passes_that_run():
+    # default slab: passes of at least min(N, 8192) rows, slab sized for a 64 Mi-element block
+    p = fkl.plan_info(32768, 2880, 201088, 100, 1.0, chunk=4096)
+    assert p["fwd_rows"] == p["bwd_rows"] == 8192
+    assert p["vslab"] == 8192 and p["slabs"] == 25
+    assert p["fwd_passes"] == p["bwd_passes"] == 4
+    assert (p["fwd_bytes"], p["bwd_bytes"]) == fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096)
+    # an explicit slab keeps the caller's chunk in both directions
+    q = fkl.plan_info(8192, 3072, 128256, 100, 1.0, chunk=1024, vslab=65536)
+    assert q["fwd_rows"] == q["bwd_rows"] == 1024 and q["fwd_passes"] == 8
+    assert q["vslab"] == 65536 and q["slabs"] == 2
+    z = fkl.plan_info(0, 64, 1000, 4)
+    assert z["fwd_passes"] == z["bwd_passes"] == 0
+    L = fkl.lib()
+    s = fkl.make_shape(16, 64, 1000, 4)
+    assert L.fkl_plan_info(ctypes.byref(s), None) == 1
+
+
+def test_validate_terms_argument_errors_before_any_device_work():
+    L = fkl.lib()
+    s = fkl.make_shape(16, 64, 1000, 4)
+    t = fkl.Terms(None, None, 0.5)
+    bad = ctypes.c_void_p(0x1000)
+    assert L.fkl_validate_terms(ctypes.byref(s), ctypes.byref(t), None, None) == 1
+    assert L.fkl_validate_terms(ctypes.byref(s), ctypes.byref(t), ctypes.c_void_p(0x1002), None) == 1
+    assert L.fkl_validate_terms(None, ctypes.byref(t), bad, None) == 1
+    t2 = fkl.Terms(None, None, 1.5)
+    assert L.fkl_validate_terms(ctypes.byref(s), ctypes.byref(t2), bad, None) == 1
+    assert b"label_weight" in L.fkl_last_error()

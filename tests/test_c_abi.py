@@ -49,6 +49,7 @@ def _layout(fields):
     ("fkl_shape", fkl.Shape),
     ("fkl_terms", fkl.Terms),
     ("fkl_topk_shape", fkl.TopkShape),
+    ("fkl_plan", fkl.PlanInfo),
     ("fkl_kernel_stat", fkl.KernelStat),
 ])
 def test_struct_layouts_match_the_binding(tmp_path, cname, pytype):
@@ -64,6 +65,9 @@ def test_host_calls_from_c_agree_with_the_binding(tmp_path):
     st, fb, bb = (int(x) for x in lines["workspace"])
     assert st == 0
     assert (fb, bb) == fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096)
+    st, *plan = (int(x) for x in lines["plan"])
+    assert st == 0
+    assert plan == list(fkl.plan_info(32768, 2880, 201088, 100, 1.0, chunk=4096).values())
     st, tb = (int(x) for x in lines["topk_workspace"])
     assert st == 0 and tb == fkl.topk_workspace_size(16384, 4096, 128256, 100)
     assert lines["null_shape"] == ["1", "message"]

@@ -118,3 +118,54 @@ def test_autograd_entry_with_terms():
     assert abs(loss.item() - r_loss) <= LOSS_RTOL * abs(r_loss)
     assert _rel(h.grad.float().cpu().numpy(), r_gh) <= GRAD_TOL
     assert _rel(W.grad.float().cpu().numpy(), r_gW) <= GRAD_TOL
+
+
+def test_nonpositive_weights_take_no_part():
+    """Rows with a zero, negative or NaN weight count in neither the weighted
+    sum nor its normaliser (the rule of the oracle's forward_terms)."""
+    wl = make_workload("tiny", 4, mask="random25")
+    rng = np.random.default_rng(15)
+    w = rng.random(wl.N) + 0.25
+    w[[3, 40, 77]] = 0.0
+    w[[5, 90, 200]] = -2.0
+    w[[11, 150]] = np.nan
+    loss, gh, gW = _case(wl, 1.0, w, None, 0.0, chunk=64, vslab=1024)
+    dropped = ~(w > 0)
+    assert gh[torch.from_numpy(dropped).to(gh.device)].abs().max().item() == 0.0
+
+
+def test_bad_labels_and_weights_are_refused(monkeypatch):
+    """fkl_validate_terms counts rows whose label lies outside [0, V) or whose
+    weight is not finite; under FKL_VALIDATE=1 forward and backward refuse
+    them with FKL_EINDEX (labels -1 and V, the values an ignore index or an
+    off-by-one would leave)."""
+    dev = _dev()
+    wl = make_workload("tiny", 5, N=64, d=64, V=500, K=9)
+    h, W = _bits(wl.h_bits, dev), _bits(wl.W_bits, dev)
+    ti, tl = torch.from_numpy(wl.t_idx).to(dev), torch.from_numpy(wl.t_logit).to(dev)
+    rng = np.random.default_rng(16)
+    good_lab = _labels(wl, rng).astype(np.int32)
+    good_w = (rng.random(wl.N) + 0.5).astype(np.float32)
+    lab_t = torch.from_numpy(good_lab).to(dev)
+    w_t = torch.from_numpy(good_w).to(dev)
+    assert fkl.validate_terms(wl.N, wl.V, row_weight=w_t, label=lab_t, label_weight=0.3) == 0
+    bad_lab = good_lab.copy()
+    bad_lab[4] = -1
+    bad_lab[9] = wl.V
+    bad_w = good_w.copy()
+    bad_w[9] = np.inf                  # same row as a bad label: counted once
+    bad_w[20] = np.nan
+    bl, bw = torch.from_numpy(bad_lab).to(dev), torch.from_numpy(bad_w).to(dev)
+    assert fkl.validate_terms(wl.N, wl.V, label=bl, label_weight=0.3) == 2
+    assert fkl.validate_terms(wl.N, wl.V, row_weight=bw) == 2
+    assert fkl.validate_terms(wl.N, wl.V, row_weight=bw, label=bl, label_weight=0.3) == 3
+    monkeypatch.setenv("FKL_VALIDATE", "1")
+    loss, lse = fkl.forward(h, W, ti, tl, row_weight=w_t, label=lab_t, label_weight=0.3)
+    torch.cuda.synchronize()
+    for kw in (dict(label=bl, label_weight=0.3), dict(row_weight=bw)):
+        with pytest.raises(fkl.FklError) as e:
+            fkl.forward(h, W, ti, tl, **kw)
+        assert e.value.status == 3 and "rows rejected" in str(e.value)
+        with pytest.raises(fkl.FklError) as e:
+            fkl.backward(h, W, ti, tl, lse, **kw)
+        assert e.value.status == 3
