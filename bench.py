@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "gptoss20b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 TEACHER_RECIPES = {
     "gptoss20b": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
     "llama3b": "zipf(1.1)+uniform top-100, logits N(0,9) sorted",
@@ -78,17 +79,52 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+def _profile(path: str):
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+        with open(path) as f:
+            return json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_hash():
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    t = _profile(TRAFFIC_FILE)
+    if t is None or t.get("source_sha256") != kernel_source_hash():
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def profile_figures(kernel: str, avg_launch_ms: float) -> dict:
+    """MFMA utilisation and HBM GB/s of one kernel from the committed rocprofv3
+    counter summaries (profiles/mfma.json, profiles/traffic.json). A figure is
+    reported only while the library's code hash matches the one the counters
+    were taken on; otherwise it is null and the entry says which summary is stale.
+    HBM GB/s = the counted bytes per launch / this run's average launch time."""
+    sha = kernel_source_hash()
+    out = {"mfma_util": None, "engine_ghz": None, "hbm_gbs": None, "hbm_bytes_per_launch": None, "stale": []}
+    m = _profile(MFMA_FILE)
+    if m is None:
+        out["stale"].append("mfma: no summary")
+    elif m.get("source_sha256") != sha:
+        out["stale"].append(f"mfma: taken on code {str(m.get('source_sha256'))[:12]}")
+    else:
+        k = m.get("kernels", {}).get(kernel)
+        if k:
+            out["mfma_util"] = k.get("mfma_util")
+            out["engine_ghz"] = k.get("engine_ghz")
+    t = _profile(TRAFFIC_FILE)
+    if t is None:
+        out["stale"].append("traffic: no summary")
+    elif t.get("source_sha256") != sha:
+        out["stale"].append(f"traffic: taken on code {str(t.get('source_sha256'))[:12]}")
+    else:
+        k = t.get("kernels", {}).get(kernel)
+        if k and avg_launch_ms:
+            out["hbm_bytes_per_launch"] = k.get("bytes_per_launch")
+            out["hbm_gbs"] = round(k["bytes_per_launch"] / (avg_launch_ms * 1e-3) / 1e9, 1)
+    return out
 
 
 def _read_counter_csv(path: str):
@@ -162,19 +198,38 @@ def summarize_stats(stats_csv: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def summarize_mfma(counter_csv: str, command: str) -> str:
-    """Markdown table of MFMA utilisation per kernel from a rocprofv3 --pmc run
-    of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed
-    over the 8 XCDs, and MFMA busy cycles over the 1024 SIMDs."""
+def _short_kernel_name(name: str) -> str:
+    return name.split("(")[0].split("<")[0].split("::")[-1].replace("void ", "").strip()
+
+
+def summarize_mfma(counter_csv: str, command: str, trace_csv: str | None = None):
+    """MFMA utilisation per kernel from a rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs, MFMA busy cycles over the 1024 SIMDs). With the same run's
+    kernel_trace.csv, the engine clock per dispatch is GRBM_GUI_ACTIVE per XCD
+    over the dispatch's duration. Returns (markdown, {kernel: figures})."""
     import collections
     import csv
     per = collections.defaultdict(lambda: collections.defaultdict(list))
+    act_by_dispatch = {}
     for r in csv.DictReader(open(counter_csv)):
-        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        name = _short_kernel_name(r["Kernel_Name"])
         per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            act_by_dispatch[int(r["Dispatch_Id"])] = (name, float(r["Counter_Value"]))
+    durations = collections.defaultdict(list)
+    if trace_csv:
+        for r in csv.DictReader(open(trace_csv)):
+            did = int(r["Dispatch_Id"])
+            if did in act_by_dispatch:
+                name, act = act_by_dispatch[did]
+                ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                if ns > 0:
+                    durations[name].append(act / 8.0 / ns)
     lines = [f"Command: `{command}`", "",
-             "| kernel | dispatches | MFMA busy SIMD-cycles | active cycles per XCD | MFMA utilisation |",
-             "|---|---|---|---|---|"]
+             "| kernel | dispatches | MFMA busy SIMD-cycles | active cycles per XCD | MFMA utilisation | engine GHz |",
+             "|---|---|---|---|---|---|"]
+    figures = {}
     for name, c in per.items():
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
         act = c.get("GRBM_GUI_ACTIVE")
@@ -182,19 +237,29 @@ def summarize_mfma(counter_csv: str, command: str) -> str:
             continue
         b = sum(busy) / len(busy)
         a = sum(act) / len(act) / 8.0
-        lines.append(f"| {name} | {len(busy)} | {b:.4g} | {a:.4g} | {b / (1024.0 * a):.3f} |")
-    return "\n".join(lines) + "\n"
+        ghz = sum(durations[name]) / len(durations[name]) if durations.get(name) else None
+        key = name[2:] if name.startswith("k_") else name
+        figures[key] = {"dispatches": len(busy), "mfma_util": round(b / (1024.0 * a), 4),
+                        "engine_ghz": round(ghz, 3) if ghz else None}
+        lines.append(f"| {name} | {len(busy)} | {b:.4g} | {a:.4g} | {b / (1024.0 * a):.3f} | "
+                     f"{'%.2f' % ghz if ghz else '-'} |")
+    return "\n".join(lines) + "\n", figures
 
 
 def cpu_baseline(wl, rows: int):
     """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
     import numpy as np
     import oracle
+    affinity = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+        threads = affinity
     h = wl.h[:rows].float().cpu().numpy()
     W = wl.W.float().cpu().numpy()
     ti = wl.t_idx_np[:rows]
@@ -212,6 +277,10 @@ def cpu_baseline(wl, rows: int):
         "sample": (f"first {rows} of {wl.N} rows of the same workload, forward + backward over the full "
                    f"vocabulary in numpy fp64 (BLAS threads={threads}); {dt:.1f} s, "
                    f"{flops / dt / 1e9:.1f} GFLOP/s"),
+        "blas": blas,
+        "blas_threads": int(threads),
+        "affinity_cores": affinity,
+        "seconds": round(dt, 2),
     }
 
 
@@ -315,8 +384,9 @@ def main() -> int:
                     help="time the teacher-cache builder (fkl_topk) on the large-head shape instead")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit (no GPU)")
-    ap.add_argument("--summarize-mfma", metavar="CSV",
-                    help="print MFMA utilisation per kernel from a rocprofv3 counter run and exit (no GPU)")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="CSV",
+                    help="COUNTER_CSV [KERNEL_TRACE_CSV]: print MFMA utilisation (and engine clock) per kernel "
+                         "from a rocprofv3 counter run, write profiles/mfma.json, and exit (no GPU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE counter runs (no GPU)")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
@@ -325,7 +395,12 @@ def main() -> int:
         print(summarize_stats(args.summarize_stats, args.command), end="")
         return 0
     if args.summarize_mfma:
-        print(summarize_mfma(args.summarize_mfma, args.command), end="")
+        md, figures = summarize_mfma(args.summarize_mfma[0], args.command,
+                                     args.summarize_mfma[1] if len(args.summarize_mfma) > 1 else None)
+        with open(MFMA_FILE, "w") as f:
+            json.dump({"source_sha256": kernel_source_hash(), "command": args.command, "kernels": figures}, f,
+                      indent=1)
+        print(md, end="")
         return 0
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib or 1024, args.command)
@@ -350,6 +425,7 @@ def main() -> int:
     wl = make_device_workload(args.workload, dev)
     torch.cuda.synchronize()
     fb, bb = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, wl.T, chunk=wl.chunk)
+    plan = fkl.plan_info(wl.N, wl.d, wl.V, wl.K, wl.T, chunk=wl.chunk)
     ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     row_lse = torch.empty(wl.N, dtype=torch.float32, device=dev)
@@ -439,11 +515,14 @@ def main() -> int:
             "share": k["total_ms"] / (traced_ms * args.steps),
             "tflops": (k["flops"] / k["launches"]) / (avg / 1e3) / 1e12 if k["flops"] else None,
         }
+    for name, k in kernels.items():
+        k.update({f: v for f, v in profile_figures(name, k["avg_ms"]).items() if f != "stale"})
     mfma = [k for k in kstats if k["flops"] > 0]
     if mfma:
         dom = max(mfma, key=lambda k: k["total_ms"])
         avg_s = dom["total_ms"] / dom["launches"] / 1e3
         achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        prof = profile_figures(dom["name"], avg_s * 1e3)
         roofline = {
             "bound": "mfma",
             "kernel": dom["name"],
@@ -455,6 +534,10 @@ def main() -> int:
             "avg_launch_ms": round(avg_s * 1e3, 4),
             "flops_per_launch": dom["flops"] / dom["launches"],
             "measured_over": f"{args.steps} further steps with per-launch hipEvents on the library's stream",
+            "mfma_util": prof["mfma_util"],
+            "engine_ghz": prof["engine_ghz"],
+            "hbm_gbs": prof["hbm_gbs"],
+            "profile_stale": prof["stale"] or None,
         }
 
     out = {
@@ -472,7 +555,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.describe(), "N": wl.N, "d": wl.d, "V": wl.V, "K": wl.K, "T": wl.T,
                    "chunk": wl.chunk, "teacher": TEACHER_RECIPES[args.workload],
-                   "mask": "packed: last token of each of 8 documents" if wl.mask is not None else "none"},
+                   "mask": "packed: last token of each of 8 documents" if wl.mask is not None else "none",
+                   "passes": {"fwd_rows": plan["fwd_rows"], "bwd_rows": plan["bwd_rows"],
+                              "vslab": plan["vslab"], "fwd_passes": plan["fwd_passes"],
+                              "bwd_passes": plan["bwd_passes"], "slabs": plan["slabs"]}},
         "tflops": round(tflops, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "step_ms_median": round(step_ms[len(step_ms) // 2], 3),

@@ -34,3 +34,22 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_profile_figures_follow_the_code_hash(tmp_path, monkeypatch):
+    """MFMA utilisation and HBM GB/s are read from the counter summaries only
+    while they were taken on the current code; otherwise null and marked stale."""
+    sha = bench.kernel_source_hash()
+    mf, tf = tmp_path / "mfma.json", tmp_path / "traffic.json"
+    mf.write_text(json.dumps({"source_sha256": sha, "kernels": {"bwd_g": {"mfma_util": 0.5, "engine_ghz": 2.0}}}))
+    tf.write_text(json.dumps({"source_sha256": sha, "kernels": {"bwd_g": {"bytes_per_launch": 7.0e8}}}))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(mf))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
+    got = bench.profile_figures("bwd_g", 0.35)
+    assert got["mfma_util"] == 0.5 and got["engine_ghz"] == 2.0
+    assert got["hbm_gbs"] == round(7.0e8 / 0.35e-3 / 1e9, 1) and got["stale"] == []
+    assert bench.profile_figures("nothing", 0.35)["mfma_util"] is None
+    mf.write_text(json.dumps({"source_sha256": "0" * 64, "kernels": {"bwd_g": {"mfma_util": 0.5}}}))
+    got = bench.profile_figures("bwd_g", 0.35)
+    assert got["mfma_util"] is None and got["hbm_gbs"] is not None
+    assert len(got["stale"]) == 1 and got["stale"][0].startswith("mfma")
