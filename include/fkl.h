@@ -207,6 +207,32 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward pass without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation, kernels and results as
+ * fkl_forward, with the workspace taken from a static device array of the
+ * library, FKL_STATIC_SCRATCH_BYTES (32 MiB) on every GPU the library runs
+ * on, held until the process ends. Allocates nothing.
+ *
+ * Arguments and outputs as fkl_forward. The stream must belong to the
+ * current device (the scratch used is that device's copy).
+ * Errors: as fkl_forward; FKL_EWORKSPACE when the shape's forward workspace
+ * (fkl_workspace_size's fwd_bytes) exceeds FKL_STATIC_SCRATCH_BYTES (fewer
+ * rows per pass, chunk with an explicit vslab, lower it); FKL_EINVAL when the
+ * stream belongs to another device.
+ * Concurrency: all calls on one GPU share its scratch, so calls that overlap
+ * on one GPU (several streams or threads) race and must be serialised by the
+ * caller. Nothing in the scratch needs to start at zero: every call writes
+ * each region before reading it.
+ */
+#define FKL_STATIC_SCRATCH_BYTES (32u << 20)
+
+fkl_status fkl_forward_static(const fkl_shape* shape, const void* h, const void* W,
+                              const int32_t* t_idx, const float* t_logit, const uint8_t* row_mask,
+                              const fkl_terms* terms, float* loss, float* row_lse, float* row_kl,
+                              void* stream);
+
+/*
  * Backward pass of the fused loss, with recomputation.
  *
  * Defined by: the blog post, section "Two systems changes": backward forms

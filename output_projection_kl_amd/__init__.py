@@ -25,6 +25,8 @@ __all__ = [
     "Shape",
     "workspace_size",
     "forward",
+    "forward_static",
+    "STATIC_SCRATCH_BYTES",
     "backward",
     "validate_teacher",
     "validate_terms",
@@ -52,6 +54,7 @@ _lib = None
 EXPORTED_SYMBOLS = (
     "fkl_workspace_size",
     "fkl_forward",
+    "fkl_forward_static",
     "fkl_backward",
     "fkl_validate_teacher",
     "fkl_validate_terms",
@@ -159,6 +162,7 @@ def lib() -> ctypes.CDLL:
     shp = ctypes.POINTER(Shape)
     L.fkl_workspace_size.argtypes = [shp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.fkl_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fkl_forward_static.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.fkl_backward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_validate_teacher.argtypes = [shp, vp, vp, vp, vp]
     L.fkl_validate_terms.argtypes = [shp, ctypes.POINTER(Terms), vp, vp]
@@ -168,7 +172,7 @@ def lib() -> ctypes.CDLL:
     L.fkl_topk.argtypes = [tshp, vp, vp, vp, vp, vp, sz, vp]
     L.fkl_trace_enable.argtypes = [ctypes.c_int]
     L.fkl_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
-    for f in ("fkl_workspace_size", "fkl_forward", "fkl_backward", "fkl_validate_teacher", "fkl_validate_terms",
+    for f in ("fkl_workspace_size", "fkl_forward", "fkl_forward_static", "fkl_backward", "fkl_validate_teacher", "fkl_validate_terms",
               "fkl_plan_info", "fkl_version",
               "fkl_topk_workspace_size", "fkl_topk", "fkl_trace_enable", "fkl_trace_read"):
         getattr(L, f).restype = ctypes.c_int
@@ -324,6 +328,37 @@ def forward(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vsl
         _check(lib().fkl_forward(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
                                  None if terms is None else ctypes.byref(terms), _ptr(loss), _ptr(row_lse),
                                  _ptr(row_kl), _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream(h.device)))
+    return (loss, row_lse, row_kl) if return_row_kl else (loss, row_lse)
+
+
+STATIC_SCRATCH_BYTES = 32 << 20  # FKL_STATIC_SCRATCH_BYTES
+
+
+def forward_static(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int = 0, vslab: int = 0,
+                   loss=None, row_lse=None, row_kl=None, return_row_kl: bool = False, row_weight=None,
+                   label=None, label_weight: float = 0.0):
+    """fkl_forward_static: the forward with the library's static device scratch
+    instead of a workspace (no allocation inside the library; pass the output
+    tensors to avoid allocating them here too). Same results as forward()."""
+    torch = _torch()
+    N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
+    terms = _terms(N, V, row_weight, label, label_weight, h.device)
+    s = make_shape(N, d, V, K, T, chunk, vslab)
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    _need(loss, "loss", torch.float32, (1,), h.device)
+    if row_lse is None:
+        row_lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    _need(row_lse, "row_lse", torch.float32, (N,), h.device)
+    if return_row_kl and row_kl is None:
+        row_kl = torch.empty(N, dtype=torch.float32, device=h.device)
+    if row_kl is not None:
+        _need(row_kl, "row_kl", torch.float32, (N,), h.device)
+        return_row_kl = True
+    with _on(h.device):
+        _check(lib().fkl_forward_static(ctypes.byref(s), _ptr(h), _ptr(W), _ptr(t_idx), _ptr(t_logit), _ptr(mask),
+                                        None if terms is None else ctypes.byref(terms), _ptr(loss), _ptr(row_lse),
+                                        _ptr(row_kl), _stream(h.device)))
     return (loss, row_lse, row_kl) if return_row_kl else (loss, row_lse)
 
 

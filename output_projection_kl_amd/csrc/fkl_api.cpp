@@ -10,6 +10,8 @@
 #include "fkl.h"
 #include "fkl_internal.h"
 
+static_assert(fkl::kStaticScratchBytes == FKL_STATIC_SCRATCH_BYTES, "static scratch size differs from the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -219,18 +221,18 @@ fkl_status fkl_workspace_size(const fkl_shape* shape, size_t* fwd_bytes, size_t*
   return FKL_OK;
 }
 
-fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
-                       const float* t_logit, const uint8_t* row_mask, const fkl_terms* terms, float* loss,
-                       float* row_lse,
-                       float* row_kl, void* workspace, size_t workspace_bytes, void* stream) {
-  fkl::Plan p;
-  fkl_status st = fkl::make_plan(shape, &p);
-  if (st != FKL_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by fkl_forward and fkl_forward_static (everything but the
+// workspace), in the order the header documents; no HIP call.
+fkl_status check_forward_args(const fkl::Plan& p, const void* h, const void* W, const int32_t* t_idx,
+                              const float* t_logit, const fkl_terms* terms, const float* loss,
+                              const float* row_lse, const float* row_kl, const float** weight,
+                              const int32_t** label, float* label_w) {
   if (!loss) return fail(FKL_EINVAL, "loss is NULL");
-  const float* weight;
-  const int32_t* label;
-  float label_w;
-  st = read_terms(terms, &weight, &label, &label_w);
+  fkl_status st = read_terms(terms, weight, label, label_w);
   if (st != FKL_OK) return st;
   if (!aligned(loss, 4)) return fail(FKL_EINVAL, "loss must be 4-byte aligned");
   if (p.N > 0) {
@@ -241,20 +243,73 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, con
         (row_kl && !aligned(row_kl, 4)))
       return fail(FKL_EINVAL, "t_idx, t_logit, row_lse and row_kl must be 4-byte aligned");
   }
-  if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
-  if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
-  st = validate_if_asked(p, t_idx, t_logit, weight, label, static_cast<char*>(workspace),
-                         static_cast<hipStream_t>(stream));
+  return FKL_OK;
+}
+
+fkl_status run_forward(const fkl::Plan& p, const void* h, const void* W, const int32_t* t_idx,
+                       const float* t_logit, const uint8_t* row_mask, const float* weight, const int32_t* label,
+                       float label_w, float* loss, float* row_lse, float* row_kl, char* ws, hipStream_t stream) {
+  fkl_status st = validate_if_asked(p, t_idx, t_logit, weight, label, ws, stream);
   if (st != FKL_OK) return st;
   fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
-                 weight, label, label_w, loss, row_lse, row_kl, static_cast<char*>(workspace)};
-  const hipError_t e = fkl::launch_forward(p, a, static_cast<hipStream_t>(stream));
+                 weight, label, label_w, loss, row_lse, row_kl, ws};
+  const hipError_t e = fkl::launch_forward(p, a, stream);
   if (e != hipSuccess) {
     g_last_error = std::string("forward launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
   return FKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
+                       const float* t_logit, const uint8_t* row_mask, const fkl_terms* terms, float* loss,
+                       float* row_lse,
+                       float* row_kl, void* workspace, size_t workspace_bytes, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  const float* weight;
+  const int32_t* label;
+  float label_w;
+  st = check_forward_args(p, h, W, t_idx, t_logit, terms, loss, row_lse, row_kl, &weight, &label, &label_w);
+  if (st != FKL_OK) return st;
+  if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.fwd_bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_workspace_size()");
+  return run_forward(p, h, W, t_idx, t_logit, row_mask, weight, label, label_w, loss, row_lse, row_kl,
+                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+fkl_status fkl_forward_static(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,
+                              const float* t_logit, const uint8_t* row_mask, const fkl_terms* terms, float* loss,
+                              float* row_lse, float* row_kl, void* stream) {
+  fkl::Plan p;
+  fkl_status st = fkl::make_plan(shape, &p);
+  if (st != FKL_OK) return st;
+  const float* weight;
+  const int32_t* label;
+  float label_w;
+  st = check_forward_args(p, h, W, t_idx, t_logit, terms, loss, row_lse, row_kl, &weight, &label, &label_w);
+  if (st != FKL_OK) return st;
+  if (p.fwd_bytes > fkl::kStaticScratchBytes) {
+    g_last_error = "the shape's forward workspace (" + std::to_string(p.fwd_bytes) +
+                   " bytes) exceeds the static scratch of " + std::to_string(fkl::kStaticScratchBytes) +
+                   " bytes; use fkl_forward with a workspace, or fewer rows per pass";
+    return FKL_EWORKSPACE;
+  }
+  char* ws = nullptr;
+  const hipError_t e = fkl::static_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (e == hipErrorInvalidDevice) return fail(FKL_EINVAL, "stream must belong to the current device");
+  if (e != hipSuccess) {
+    g_last_error = std::string("static scratch lookup failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  return run_forward(p, h, W, t_idx, t_logit, row_mask, weight, label, label_w, loss, row_lse, row_kl, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, const int32_t* t_idx,

@@ -118,6 +118,14 @@ constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logit
 fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p);
 
 hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t stream);
+
+// Static scratch of the allocation-free forward (fkl_forward_static): its
+// size, and the device address of the calling device's copy. The lookup runs
+// once per device, with that device current; `stream` must belong to the
+// current device (hipErrorInvalidDevice otherwise).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch(hipStream_t stream, char** ptr);
 hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx, float* t_logit,
                        char* ws, hipStream_t stream);
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);

@@ -24,8 +24,9 @@
 //                   vocabulary into partial sums)
 //   k_reduce_grad_h grad_h[chunk] (+)= the partial sums, in split order
 #include <climits>
-#include <type_traits>
 #include <cmath>
+#include <mutex>
+#include <type_traits>
 
 #include "fkl_device.h"
 #include "fkl_internal.h"
@@ -929,6 +930,44 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
     }
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free forward
+// ---------------------------------------------------------------------------
+
+// The workspace of fkl_forward_static, for callers that cannot allocate. Every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device is handed to the
+// kernels.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, char** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx, const float* t_logit,

@@ -143,6 +143,12 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
   return hipSuccess;
 }
 
+hipError_t static_scratch(hipStream_t, char** ptr) {
+  *ptr = reinterpret_cast<char*>(uintptr_t(0x40000000));
+  g_ws_bytes = kStaticScratchBytes;
+  return hipSuccess;
+}
+
 hipError_t launch_validate(int64_t, int64_t, int32_t, const int32_t*, const float*, int32_t* bad, hipStream_t) {
   ++g_launches;
   CHECK(bad != nullptr);
@@ -233,6 +239,10 @@ void drive(const fkl_shape& s) {
   // valid calls reach the (stub) launchers with the plan checked there
   fkl::g_ws_bytes = fb;
   CHECK(fkl_forward(&s, h, W, ti, tl, nullptr, nullptr, out, out, out, ws, fb, nullptr) == FKL_OK);
+  // the allocation-free forward: the static scratch, or FKL_EWORKSPACE when the plan needs more
+  const fkl_status sst = fkl_forward_static(&s, h, W, ti, tl, nullptr, nullptr, out, out, out, nullptr);
+  CHECK(sst == (fb <= fkl::kStaticScratchBytes ? FKL_OK : FKL_EWORKSPACE));
+  CHECK(fkl_forward_static(&s, h, W, ti, tl, nullptr, nullptr, nullptr, out, out, nullptr) == FKL_EINVAL);
   fkl::g_ws_bytes = bb;
   CHECK(fkl_backward(&s, h, W, ti, tl, nullptr, nullptr, out, nullptr, out, out, ws, bb, nullptr) == FKL_OK);
   fkl_terms terms{out, static_cast<const int32_t*>(fake(0x700000)), 0.25f};

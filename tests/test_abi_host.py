@@ -263,3 +263,20 @@ def test_validate_terms_argument_errors_before_any_device_work():
     t2 = fkl.Terms(None, None, 1.5)
     assert L.fkl_validate_terms(ctypes.byref(s), ctypes.byref(t2), bad, None) == 1
     assert b"label_weight" in L.fkl_last_error()
+
+
+def test_static_forward_refuses_shapes_beyond_its_scratch():
+    """fkl_forward_static checks the shape's forward workspace against the
+    static scratch before any device call: 8192-row passes of K = 1024 teacher
+    entries need about 67 MB, more than the 32 MiB scratch."""
+    L = fkl.lib()
+    s = fkl.make_shape(32768, 2880, 201088, 1024)
+    fb, _ = fkl.workspace_size(32768, 2880, 201088, 1024)
+    assert fb > fkl.STATIC_SCRATCH_BYTES
+    p = ctypes.c_void_p(0x10000)
+    st = L.fkl_forward_static(ctypes.byref(s), p, p, p, p, None, None, p, p, None, None)
+    assert st == 2 and b"static scratch" in L.fkl_last_error()
+    assert L.fkl_forward_static(ctypes.byref(s), p, p, p, p, None, None, None, p, None, None) == 1
+    assert L.fkl_forward_static(None, p, p, p, p, None, None, p, p, None, None) == 1
+    # the headline shape fits
+    assert fkl.workspace_size(32768, 2880, 201088, 100)[0] <= fkl.STATIC_SCRATCH_BYTES
