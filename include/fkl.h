@@ -295,18 +295,23 @@ fkl_status fkl_validate_terms(const fkl_shape* shape, const fkl_terms* terms, in
  *                        goes to the lowest indices among equal logits.
  * The output is in the layout fkl_forward / fkl_backward read.
  *
- * Rows are processed `chunk` at a time (0: enough rows for a 512 MiB fp32
- * logits block, at least 256): the logits of a chunk are formed in the
- * workspace, chunk (rounded up to 256) x V (rounded up to 256) fp32, and the
- * top-K of each row is selected exactly. Each row is normally read once: a
- * threshold taken from a sample of the row keeps a few times K of its logits
- * (at most about 2048 expected) in on-chip memory, where the selection runs.
- * A threshold that keeps fewer than K or too many logits is moved and the row
- * read again; after three tries the row is selected over the whole row
- * (FKL_TOPK_DIRECT asks for that route on every row). Both routes return the
- * same result. Constraints: d a multiple of 8 (<= 65536),
- * 1 <= K <= min(V, 1024); h and W 16-byte aligned; the workspace 256-byte
- * aligned. Argument errors return before any HIP call.
+ * Default (fused) route, per pass of `chunk` rows (0: 8192, fewer for
+ * K > 128): the logits of a sample of whole vocabulary tiles (every 16th or
+ * more sparse, at most 16 tiles) give each row a threshold key aimed at about
+ * max(1024, 8K) of its logits; one sweep over the other tiles keeps only the
+ * keys at or above it (no [rows x V] block is formed), and the top K is
+ * selected exactly among them. A row for which fewer than K keys reached the
+ * threshold, or more than its candidate slots hold, makes the pass be redone
+ * by the materialised route, so the result never depends on the sample.
+ * Materialised route (FKL_TOPK_MATERIALIZE, FKL_TOPK_DIRECT): the logits of
+ * up to chunk rows at a time (0: enough rows for a 512 MiB fp32 block, at
+ * least 256) are formed in the workspace and each row's top K is selected
+ * there: normally from a threshold taken from a sample of the row (a
+ * threshold that keeps fewer than K logits or too many is moved and the row
+ * read again, three tries), with FKL_TOPK_DIRECT over the whole row. Every
+ * route returns the same result. Constraints: d a multiple of 8
+ * (<= 65536), 1 <= K <= min(V, 1024); h and W 16-byte aligned; the workspace
+ * 256-byte aligned. Argument errors return before any HIP call.
  */
 typedef struct {
   int64_t N, d, V;
@@ -315,7 +320,8 @@ typedef struct {
   uint32_t flags;  /* FKL_TOPK_* below; 0 = default */
 } fkl_topk_shape;
 
-#define FKL_TOPK_DIRECT 0x1u /* select over the whole row, no sampled threshold */
+#define FKL_TOPK_DIRECT 0x1u      /* materialised route, each row selected over the whole row */
+#define FKL_TOPK_MATERIALIZE 0x2u /* materialised route, rows selected from a sampled threshold */
 
 /* Workspace bytes of fkl_topk for this shape (host only). */
 fkl_status fkl_topk_workspace_size(const fkl_topk_shape* shape, size_t* bytes);

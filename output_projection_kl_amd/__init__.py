@@ -143,6 +143,7 @@ class TopkShape(ctypes.Structure):
 
 
 TOPK_DIRECT = 0x1
+TOPK_MATERIALIZE = 0x2
 
 
 def library_path() -> str:
@@ -485,11 +486,14 @@ def topk_workspace_size(N, d, V, K, chunk=0, flags=0) -> int:
     return b.value
 
 
-def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None, direct: bool = False):
+def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None, direct: bool = False,
+         materialize: bool = False):
     """Offline teacher cache: per row of h (bf16 [N,d]), the K largest logits of
-    h W^T (W bf16 [V,d]), descending, ties by the lower index. direct=True
-    selects over every whole row instead of from a sampled threshold (same
-    result). Returns (t_idx int32 [N,K], t_logit fp32 [N,K])."""
+    h W^T (W bf16 [V,d]), descending, ties by the lower index. By default the
+    fused route (logits filtered against a per-row threshold as they are formed);
+    materialize=True forms each block of rows' logits and selects there from a
+    sampled threshold, direct=True does so over every whole row (same result on
+    every route). Returns (t_idx int32 [N,K], t_logit fp32 [N,K])."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -497,7 +501,7 @@ def topk(h, W, K: int, chunk: int = 0, workspace=None, t_idx=None, t_logit=None,
     V = W.shape[0]
     _need(h, "h", torch.bfloat16, (N, d))
     _need(W, "W", torch.bfloat16, (V, d), h.device)
-    s = TopkShape(N, d, V, K, chunk, TOPK_DIRECT if direct else 0)
+    s = TopkShape(N, d, V, K, chunk, (TOPK_DIRECT if direct else 0) | (TOPK_MATERIALIZE if materialize else 0))
     b = ctypes.c_size_t(0)
     _check(lib().fkl_topk_workspace_size(ctypes.byref(s), ctypes.byref(b)))
     ws = _workspace(b.value, h.device, workspace)

@@ -190,21 +190,89 @@ fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
   if (s->K > 1024) return fail(FKL_EUNSUPPORTED, "K must be <= 1024");
   if (s->K > s->V) return fail(FKL_EINVAL, "K must be <= V");
   if (s->chunk < 0) return fail(FKL_EINVAL, "chunk must be >= 0");
-  if (s->flags & ~static_cast<uint32_t>(FKL_TOPK_DIRECT)) return fail(FKL_EINVAL, "unknown fkl_topk_shape flag");
+  if (s->flags & ~static_cast<uint32_t>(FKL_TOPK_DIRECT | FKL_TOPK_MATERIALIZE))
+    return fail(FKL_EINVAL, "unknown fkl_topk_shape flag");
   p->N = s->N;
   p->d = s->d;
   p->V = s->V;
   p->K = s->K;
   p->flags = s->flags;
   p->ld = round_up(s->V, kTile);
+  p->fused = !(s->flags & (FKL_TOPK_DIRECT | FKL_TOPK_MATERIALIZE));
+  // materialised block: 512 MiB of fp32 logits by default
+  int64_t block_rows = kTopkDefaultBlockElems / p->ld / kTile * kTile;
+  if (block_rows < kTile) block_rows = kTile;
+  // sample: every stride-th full tile, at most kTopkMaxSampleTiles of them
+  const int64_t n_full = s->V / kTile;
+  const int64_t stride = std::max<int64_t>(kTopkMinStride, ceil_div(n_full, kTopkMaxSampleTiles));
+  p->stride = static_cast<int32_t>(stride);
+  p->n_sample = p->fused ? static_cast<int32_t>(ceil_div(n_full, stride)) : 0;
+  // threshold: aimed at the j-th largest sampled key, so that about `target`
+  // keys of the row are expected at or above it, far enough above K that the
+  // sample's spread (relative spread 1 / sqrt(j)) rarely leaves fewer than K
+  // (j = 0: the sample is too small to aim, every key is a candidate)
+  const int64_t S = static_cast<int64_t>(p->n_sample) * kTile;
+  p->target = std::max(1024, 8 * s->K);
+  int64_t j = S > 0 ? ceil_div(static_cast<int64_t>(p->target) * S, s->V) : 0;
+  if (j >= S) j = 0;
+  p->j = static_cast<int32_t>(j);
+  // about j sampled keys reach the threshold, more only when the 24-bit prefix
+  // bin at the j-th key is crowded; a row with more than xcap is redone
+  p->xcap = static_cast<int32_t>(j > 0 ? std::min<int64_t>(S, 2 * j + 256) : S);
+  // per-row candidate slots of a full pass of R rows: 2 * splits slices
+  auto slots_per_row = [p](int64_t R) {
+    const int sp = topk_splits(*p, R);
+    return static_cast<int64_t>(2 * sp) * topk_slice_cap(*p, sp);
+  };
   int64_t chunk = s->chunk;
   if (chunk == 0) {
-    chunk = kTopkDefaultBlockElems / p->ld / kTile * kTile;
-    if (chunk < kTile) chunk = kTile;
+    if (p->fused) {
+      const int64_t per_row = slots_per_row(kTopkFusedRows) * 8;
+      const int64_t by_cand = kTopkCandBytes / per_row / kTile * kTile;
+      chunk = std::min<int64_t>(kTopkFusedRows, std::max<int64_t>(kTile, by_cand));
+    } else {
+      chunk = block_rows;
+    }
   }
   if (s->N > 0 && chunk > s->N) chunk = s->N;
   p->chunk = chunk;
-  p->bytes = align256(static_cast<size_t>(round_up(chunk, kTile)) * p->ld * 4);
+  p->fb_rows = std::min(chunk, block_rows);
+  size_t off = 0;
+  p->off_flag = off;
+  off += 256;
+  p->off_ws = off;
+  off = align256(off + static_cast<size_t>(S) * s->d * 2);
+  p->off_region = off;
+  const size_t chunk_alloc = static_cast<size_t>(round_up(chunk, kTile));
+  size_t fused_bytes = 0;
+  if (p->fused) {
+    // candidate slices: the larger of a full pass and the last, shorter one
+    // (fewer rows take more splits, hence more, smaller slices)
+    int64_t slots = 0, slices = 0;
+    for (int64_t R : {chunk, (s->N > 0 ? s->N - (ceil_div(s->N, chunk) - 1) * chunk : chunk)}) {
+      const int sp = topk_splits(*p, R);
+      slots = std::max(slots, round_up(R, kTile) * 2 * sp * topk_slice_cap(*p, sp));
+      slices = std::max(slices, round_up(R, kTile) * 2 * sp);
+    }
+    p->off_sample = off;
+    size_t o = align256(off + chunk_alloc * S * 4);
+    p->off_thr = o;
+    o = align256(o + chunk_alloc * 8);
+    p->off_cnt = o;
+    o = align256(o + static_cast<size_t>(slices) * 4);
+    p->off_cand = o;
+    o = align256(o + static_cast<size_t>(slots) * 8);
+    // the extra slice of each row: its sampled keys at or above the threshold
+    p->off_xcnt = o;
+    o = align256(o + chunk_alloc * 4);
+    p->off_xcand = o;
+    o = align256(o + chunk_alloc * p->xcap * 8);
+    fused_bytes = o - off;
+  } else {
+    p->off_sample = p->off_thr = p->off_cnt = p->off_cand = p->off_xcnt = p->off_xcand = off;
+  }
+  const size_t block_bytes = align256(static_cast<size_t>(round_up(p->fb_rows, kTile)) * p->ld * 4);
+  p->bytes = off + std::max(fused_bytes, block_bytes);
   return FKL_OK;
 }
 

@@ -103,17 +103,57 @@ class TraceScope {
   uint64_t id_;  // 0: not traced
 };
 
-// Teacher-cache builder (fkl_topk): rows per pass and the fp32 logits block.
+// Teacher-cache builder (fkl_topk). Two routes:
+//  * fused (default): per pass of `chunk` rows, the logits of a sample of
+//    whole vocabulary tiles give each row a threshold key; one sweep over the
+//    other tiles keeps the keys at or above it (candidates, at most `cap` per
+//    row); the top K is selected among them. A pass in which some row kept
+//    fewer than K keys or more than `cap` is redone by the materialised route.
+//  * materialised: the logits of fb_rows rows at a time are formed in an fp32
+//    block and each row's top K is selected there.
 struct TopkPlan {
   int64_t N, d, V;
   int32_t K;
-  int64_t chunk;  // rows per pass
-  int64_t ld;     // row stride of the logits block (V rounded up to 256)
-  size_t bytes;   // workspace: chunk rounded up to 256 rows x ld fp32
-  uint32_t flags; // FKL_TOPK_* options
+  int64_t chunk;    // rows per pass
+  int64_t fb_rows;  // rows per materialised logits block (<= chunk)
+  int64_t ld;       // row stride of the logits block (V rounded up to 256)
+  uint32_t flags;   // FKL_TOPK_* options
+  bool fused;       // the fused route runs (otherwise every pass is materialised)
+  int32_t stride;   // sampled tiles: the full vocabulary tiles t with t % stride == 0
+  int32_t n_sample; // number of sampled tiles
+  int32_t target;   // candidates per row the threshold aims at
+  int32_t j;        // the threshold is aimed at a row's j-th largest sampled key (0: every key)
+  int32_t xcap;     // slots of a row's extra slice (its sampled keys at or above the threshold)
+  // workspace offsets (bytes); the fused buffers and the logits block share
+  // the region at off_region (a pass's fused buffers are dead before its
+  // materialised redo starts)
+  size_t off_flag, off_ws, off_region, off_sample, off_thr, off_cnt, off_cand, off_xcnt, off_xcand;
+  size_t bytes;
 };
 
 constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logits block (512 MiB)
+constexpr int64_t kTopkFusedRows = 8192;                         // default rows per fused pass
+constexpr int64_t kTopkCandBytes = int64_t(512) << 20;           // bound on a pass's candidate slices
+constexpr int kTopkMaxSampleTiles = 16;
+constexpr int kTopkMinStride = 16;
+
+// Vocabulary splits of a fused pass's sweep over `rows` rows (as many
+// workgroups as fit in one round on the CUs, at most one per unsampled
+// tile), and the slots of
+// each of a row's 2 * splits candidate slices: room for four times the
+// slice's share of the target, plus 16 (candidates may cluster in parts of
+// the vocabulary).
+inline int topk_splits(const TopkPlan& p, int64_t rows) {
+  const int64_t rbs = (rows + kTile - 1) / kTile;
+  int64_t s = kTargetBlocks / rbs;  // rbs x splits stays within one round of workgroups
+  const int64_t n_u = (p.V + kTile - 1) / kTile - p.n_sample;
+  if (s > n_u) s = n_u;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+inline int topk_slice_cap(const TopkPlan& p, int splits) {
+  return static_cast<int>((2 * static_cast<int64_t>(p.target) + 2 * splits - 1) / (2 * splits)) * 2 + 16;
+}
 
 fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p);
 

@@ -5,27 +5,48 @@
 // logits per position are cached once, offline, and nothing else of its
 // distribution is kept).
 //
-// Per chunk of rows:
-//   k_topk_logits  256 x 256 MFMA tiles of z = h_chunk W^T (fp32 accumulation)
-//                  written to an fp32 logits block in the workspace
-//   k_topk_select  one workgroup per row: exact radix selection of the K
-//                  largest keys, then a bitonic sort in LDS
-//
 // Keys make every element distinct: key = (order-preserving bits of z) << 32
 // | (0xFFFFFFFF - index), so larger keys are larger logits and, for equal
 // logits, lower indices. Selection by 12-bit radix digits of the key from the
 // top, keeping only the keys that share the digits chosen so far, until the
 // digit bin at the K-th key is taken whole.
 //
-// Each row is read once in the usual case: a threshold key is taken from a
-// sample of the row (runs of contiguous logits spread over it) such that a
-// bounded number of keys, at least K and at most half the LDS buffer, is
-// expected at or above it; one pass collects those keys into LDS, and the
-// selection runs there. A threshold that keeps fewer than K keys or more than
-// the buffer holds is moved and the row read again; after three tries the row
-// is selected directly: a histogram pass over the row, a pass that takes the
-// keys above the boundary bin and copies the bin to LDS, the rest in LDS (or
-// over the row when the bin does not fit). Both routes select the same K keys.
+// Fused route (default), per pass of rows; no [rows x V] block is formed:
+//   k_topk_logits  the logits of the sampled vocabulary tiles (every stride-th
+//                  full tile, gathered once into a compact copy of W by
+//                  k_gather_tiles) for the pass's rows
+//   k_topk_thresh  one workgroup per row: the row's j-th largest sampled key,
+//                  chosen so that about cap / 2 of the row's keys are expected
+//                  at or above it
+//   k_topk_sweep   256-row block x a run of the other vocabulary tiles: MFMA
+//                  logits tile -> LDS -> the keys at or above the row's
+//                  threshold appended to the row's candidate list
+//   k_topk_pick    one workgroup per row: the top K among the candidates and
+//                  the sampled keys at or above the threshold; exact whenever
+//                  at least K keys reached the threshold and none was dropped
+//                  (a row with fewer than K, or more than cap, flags the pass)
+//   k_topk_logits + k_topk_select (materialised route) redo a flagged pass;
+//                  they return at once when the flag is clear
+//
+// Materialised route (FKL_TOPK_MATERIALIZE, FKL_TOPK_DIRECT, and the redo),
+// per block of rows:
+//   k_topk_logits  256 x 256 MFMA tiles of z = h_chunk W^T (fp32 accumulation)
+//                  written to an fp32 logits block in the workspace
+//   k_topk_select  one workgroup per row: exact radix selection of the K
+//                  largest keys, then a bitonic sort in LDS. Each row is read
+//                  once in the usual case: a threshold key is taken from a
+//                  sample of the row (runs of contiguous logits spread over
+//                  it) such that a bounded number of keys, at least K and at
+//                  most half the LDS buffer, is expected at or above it; one
+//                  pass collects those keys into LDS, and the selection runs
+//                  there. A threshold that keeps fewer than K keys or more than
+//                  the buffer holds is moved and the row read again; after
+//                  three tries (or with FKL_TOPK_DIRECT) the row is selected
+//                  directly: a histogram pass over the row, a pass that takes
+//                  the keys above the boundary bin and copies the bin to LDS,
+//                  the rest in LDS (or over the row when the bin does not fit).
+// Every route selects the same K keys: the logits come from the same MFMA
+// tile code with the same contraction order.
 #include <climits>
 
 #include "fkl_device.h"
@@ -34,8 +55,10 @@
 
 namespace fkl {
 
-__global__ __launch_bounds__(kBlockThreads, 1) void k_topk_logits(GemmAccParams P) {
+// run_if: NULL, or a flag that makes the whole launch return at once when 0.
+__global__ __launch_bounds__(kBlockThreads, 1) void k_topk_logits(GemmAccParams P, const uint32_t* run_if) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
+  if (run_if && *run_if == 0) return;
   const int tiles = P.mblocks * P.nblocks;
   gemm_acc_tile<false, false>(P, xcd_contiguous(blockIdx.x, tiles), lds);
 }
@@ -70,14 +93,15 @@ struct SelectState {
   uint32_t need;    // keys still to take among those matching prefix
 };
 
-// One digit of the selection over n keys given by key_at(i): histogram of the
-// next digit among keys matching the prefix, then the digit holding the
-// need-th largest key. Returns the number of keys in that digit's bin.
-template <class KeyAt>
+// One digit (DB bits) of the selection over n keys given by key_at(i):
+// histogram of the next digit among keys matching the prefix, then the digit
+// holding the need-th largest key. Returns the number of keys in that digit's
+// bin. hist holds 1 << DB counters.
+template <int DB = kDigitBits, class KeyAt>
 __device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* wave_tot,
                                  uint32_t* s_vals) {
   const int tid = threadIdx.x;
-  const int w = 64 - st.pbits < kDigitBits ? 64 - st.pbits : kDigitBits;
+  const int w = 64 - st.pbits < DB ? 64 - st.pbits : DB;
   const int nb = 1 << w;
   const int shift = 64 - st.pbits - w;
   for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
@@ -129,12 +153,14 @@ __device__ uint32_t select_digit(KeyAt key_at, int n, SelectState& st, uint32_t*
 }
 
 // Digits until the bin at the K-th key is taken whole (at the latest when all
-// 64 bits are fixed: keys are distinct).
-template <class KeyAt>
+// 64 bits are fixed: keys are distinct), or until max_bits are fixed: then the
+// keys whose top bits are at least the prefix are the need largest and the
+// rest of the last bin.
+template <int DB = kDigitBits, class KeyAt>
 __device__ void select_rest(KeyAt key_at, int n, SelectState& st, uint32_t* hist, uint32_t* wave_tot,
-                            uint32_t* s_vals) {
-  while (st.pbits < 64) {
-    if (select_digit(key_at, n, st, hist, wave_tot, s_vals) == st.need) break;
+                            uint32_t* s_vals, int max_bits = 64) {
+  while (st.pbits < max_bits) {
+    if (select_digit<DB>(key_at, n, st, hist, wave_tot, s_vals) == st.need) break;
   }
 }
 
@@ -191,8 +217,39 @@ __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint6
   }
 }
 
+// Bitonic sort of the Kp keys (K selected, the rest 0), descending, and the
+// row's output: the K logits and their indices.
+__device__ void sort_and_write(uint64_t* keys, int K, int Kp, int64_t out_row, int32_t* __restrict__ t_idx,
+                               float* __restrict__ t_logit) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= Kp; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < Kp; i += kSelThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t a = keys[i];
+          const uint64_t b = keys[j];
+          const bool desc = (i & size) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            keys[i] = b;
+            keys[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t out = out_row * static_cast<int64_t>(K);
+  for (int k = tid; k < K; k += kSelThreads) {
+    const uint64_t key = keys[k];
+    t_logit[out + k] = from_ordered_bits(static_cast<uint32_t>(key >> 32));
+    t_idx[out + k] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __restrict__ logits, int64_t ld,
                                                              int V, int K, int Kp, int64_t r0, int direct,
+                                                             const uint32_t* run_if,
                                                              int32_t* __restrict__ t_idx,
                                                              float* __restrict__ t_logit) {
   __shared__ uint32_t hist[kBins];
@@ -202,6 +259,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
   __shared__ uint32_t s_vals[3];
   __shared__ uint32_t s_fill, s_cand;
   const int tid = threadIdx.x;
+  if (run_if && *run_if == 0) return;
   const float* row = logits + static_cast<int64_t>(blockIdx.x) * ld;
 
   for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
@@ -335,63 +393,420 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
     select_row(row, V, K, keys, cand, hist, wave_tot, s_vals, &s_fill, &s_cand);
   }
   __syncthreads();
-  // Bitonic sort of Kp keys, descending.
-  for (int size = 2; size <= Kp; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < Kp; i += kSelThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const uint64_t a = keys[i];
-          const uint64_t b = keys[j];
-          const bool desc = (i & size) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            keys[i] = b;
-            keys[j] = a;
+  sort_and_write(keys, K, Kp, r0 + blockIdx.x, t_idx, t_logit);
+}
+
+// ---------------------------------------------------------------------------
+// Fused route
+// ---------------------------------------------------------------------------
+
+// Compact copy of the sampled tiles of W: tile s of the copy is rows
+// [s * stride * 256, + 256) of W (every sampled tile is a full tile). One
+// 16-byte chunk per thread and step.
+__global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict__ W, int64_t d, int stride,
+                                                      int n_sample, uint16_t* __restrict__ Ws) {
+  const int64_t per_row = d / 8;
+  const int64_t total = static_cast<int64_t>(n_sample) * kTile * per_row;
+  for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < total; q += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = q / per_row;  // row of the copy
+    const int64_t c = q - r * per_row;
+    const int64_t src = (r / kTile) * stride * kTile + (r % kTile);
+    reinterpret_cast<u32x4*>(Ws + r * d)[c] = reinterpret_cast<const u32x4*>(W + src * d)[c];
+  }
+}
+
+// Vocabulary index of column i of the sample (sampled tile i / 256).
+__device__ __forceinline__ int sample_col(int i, int stride) { return (i >> 8) * stride * kTile + (i & 255); }
+
+constexpr int kMaxSample = kTopkMaxSampleTiles * kTile;
+constexpr int kFusedDigitBits = 8;   // radix digits of the fused route's selections
+constexpr int kThreshBits = 24;      // the threshold is fixed to its top 24 bits
+
+// Each wave appends the keys its lanes take to list[] (room reserved with one
+// LDS atomic on *count per wave).
+__device__ __forceinline__ void wave_append(bool take, uint64_t key, uint64_t* list, uint32_t* count) {
+  const uint64_t m = __ballot(take);
+  if (m == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(count, static_cast<uint32_t>(__popcll(m)));
+  base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
+  if (take) list[base + below] = key;
+}
+
+// One workgroup per row of the pass: thr[row] = a key at or below the row's
+// j-th largest sampled key, exactly it unless the bin of 24-bit prefixes at it
+// holds more keys (then the bin's lower bound); 0 when j = 0 (every key is a
+// candidate). Any threshold gives the exact top K as long as at least K of the
+// row's keys reach it and none is dropped (the pick checks both), so aiming
+// at the j-th key need not be exact. The row's sampled keys at or above the
+// threshold go to its extra candidate slice (xcap slots; the sweep skips the
+// sampled tiles), their number to xcnt[row]. Workgroup 0 also clears the
+// pass's redo flag (the previous pass's redo has read it: launches are in
+// stream order).
+__global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __restrict__ sample, int S, int stride,
+                                                             int j, uint64_t* __restrict__ thr,
+                                                             uint32_t* __restrict__ xcnt,
+                                                             uint64_t* __restrict__ xcand, int xcap,
+                                                             uint32_t* flag) {
+  __shared__ uint32_t sv[kMaxSample];
+  __shared__ uint64_t hits[kMaxSample];
+  __shared__ uint32_t hist[1 << kFusedDigitBits];
+  __shared__ uint32_t wave_tot[kSelThreads / 64];
+  __shared__ uint32_t s_vals[3];
+  __shared__ uint32_t s_hits;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  if (row == 0 && tid == 0) *flag = 0;
+  if (tid == 0) s_hits = 0;
+  const float* zr = sample + static_cast<int64_t>(row) * S;
+  for (int i = tid * 4; i < S; i += kSelThreads * 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(zr + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[i + e] = ordered_bits(v[e]);
+  }
+  __syncthreads();
+  const uint32_t* svp = sv;
+  auto key_at = [svp, stride](int i) {
+    return (static_cast<uint64_t>(svp[i]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - sample_col(i, stride));
+  };
+  uint64_t t = 0;
+  if (j > 0) {
+    SelectState st{0, 0, static_cast<uint32_t>(j)};
+    select_rest<kFusedDigitBits>(key_at, S, st, hist, wave_tot, s_vals, kThreshBits);
+    t = st.pbits >= 64 ? st.prefix : st.prefix << (64 - st.pbits);
+  }
+  for (int i0 = 0; i0 < S; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    const uint64_t key = i < S ? key_at(i) : 0;
+    wave_append(i < S && key >= t, key, hits, &s_hits);
+  }
+  __syncthreads();
+  const uint32_t nh = s_hits;
+  uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
+  for (uint32_t i = tid; i < nh && i < static_cast<uint32_t>(xcap); i += kSelThreads) xrow[i] = hits[i];
+  if (tid == 0) {
+    thr[row] = t;
+    xcnt[row] = nh;
+  }
+}
+
+struct TopkSweepParams {
+  const uint16_t* h;  // the pass's first row
+  const uint16_t* W;
+  int64_t d, V;
+  int32_t rows;
+  int32_t n_vt;      // vocabulary tiles
+  int32_t stride, n_sample;
+  int32_t rbs, splits;
+  const uint64_t* thr;
+  uint32_t* cnt;     // [rows][2 * splits]: keys each slice found (may exceed slice_cap)
+  uint64_t* cand;    // [rows][2 * splits][slice_cap]
+  int32_t slice_cap;
+};
+
+// The u-th vocabulary tile that is not sampled (sampled: t % stride == 0 for
+// t < n_sample * stride).
+__device__ __forceinline__ int unsampled_tile(int u, int stride, int n_sample) {
+  const int in_groups = n_sample * (stride - 1);
+  if (u >= in_groups) return u + n_sample;
+  return (u / (stride - 1)) * stride + 1 + u % (stride - 1);
+}
+
+// Each thread owns one row (tid & 255) of the block and one 64-column quarter
+// (tid >> 8) of every half tile: it compares its 64 keys with the row's
+// threshold (the logit's ordered bits first, the full key only where they
+// reach the threshold's) and stores those at or above it in its own slice of
+// the row's candidate list (slice 2 * split + quarter), counting them in a
+// register, so no two threads ever write the same slot and no atomic is
+// needed. The count (which may exceed the slice) is stored at the end.
+__global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams P) {
+  __shared__ __align__(16) char lds[kKernelLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / kWN;
+  const int wn = wave % kWN;
+  int rb, split;
+  grouped_tile(xcd_contiguous(blockIdx.x, P.rbs * P.splits), P.rbs, P.splits, 8, rb, split);
+  const int n_u = P.n_vt - P.n_sample;
+  const int u0 = static_cast<int>(static_cast<int64_t>(split) * n_u / P.splits);
+  const int u1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_u / P.splits);
+  const int rloc = tid & (kTile - 1);
+  const int sub = tid >> 8;
+  const int row = rb * kTile + rloc;
+  const bool row_ok = row < P.rows;
+  const uint64_t thr = row_ok ? P.thr[row] : ~uint64_t(0);
+  const uint32_t thr_hi = static_cast<uint32_t>(thr >> 32);
+  const int slices = 2 * P.splits;
+  const int slice = 2 * split + sub;
+  uint64_t* mine = P.cand + (static_cast<int64_t>(row_ok ? row : 0) * slices + slice) * P.slice_cap;
+  uint32_t found = 0;
+  const Operand A{P.h, P.d, P.rows, P.d};
+  const Operand B{P.W, P.d, P.V, P.d};
+  const int nk = static_cast<int>((P.d + kStageK - 1) / kStageK);
+  float* stage = reinterpret_cast<float*>(lds);
+  for (int u = u0; u < u1; ++u) {
+    const int vt = unsampled_tile(u, P.stride, P.n_sample);
+    MainAcc acc;
+    zero_acc(acc);
+    gemm_mainloop<false, false, kNBW, kWN>(A, B, static_cast<int64_t>(rb) * kTile, static_cast<int64_t>(vt) * kTile,
+                                           nk, acc, lds);
+    for (int half = 0; half < 2; ++half) {
+      if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
+      __syncthreads();
+      const int cs = vt * kTile + half * 128 + sub * 64;
+      const int nvalid = row_ok ? static_cast<int>(min<int64_t>(64, P.V - cs)) : 0;
+      const float* sr = stage + rloc * kStageLd + sub * 64;
+      for (int e0 = 0; e0 < nvalid; e0 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sr + e0);
+        const uint32_t o0 = ordered_bits(x[0]), o1 = ordered_bits(x[1]);
+        const uint32_t o2 = ordered_bits(x[2]), o3 = ordered_bits(x[3]);
+        if (max(max(o0, o1), max(o2, o3)) < thr_hi) continue;  // the usual case
+        const uint32_t ob[4] = {o0, o1, o2, o3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t key = (static_cast<uint64_t>(ob[e]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - (cs + e0 + e));
+          if (e0 + e < nvalid && key >= thr) {
+            if (found < static_cast<uint32_t>(P.slice_cap)) mine[found] = key;
+            ++found;
           }
         }
       }
       __syncthreads();
     }
   }
-  const int64_t out = (r0 + blockIdx.x) * static_cast<int64_t>(K);
-  for (int k = tid; k < K; k += kSelThreads) {
-    const uint64_t key = keys[k];
-    t_logit[out + k] = from_ordered_bits(static_cast<uint32_t>(key >> 32));
-    t_idx[out + k] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-  }
+  if (row_ok) P.cnt[static_cast<int64_t>(row) * slices + slice] = found;
 }
 
-hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx, float* t_logit,
-                       char* ws, hipStream_t st) {
-  float* z = reinterpret_cast<float*>(ws);
-  int Kp = 1;
-  while (Kp < p.K) Kp <<= 1;
-  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
-    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+// One workgroup per row: the top K among the row's candidates (its 2 * splits
+// slices from the sweep and the extra slice of sampled keys from the
+// threshold). When fewer than K keys reached the threshold, or a slice
+// overflowed (keys were dropped), the row cannot be answered here: the pass's
+// redo flag is set and nothing is written.
+constexpr int kMaxSlices = 2 * kTargetBlocks;
+constexpr int kPickBatch = 6;  // slot loads issued before any is used
+
+__global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __restrict__ xcnt,
+                                                           const uint64_t* __restrict__ xcand, int xcap,
+                                                           const uint32_t* __restrict__ cnt,
+                                                           const uint64_t* __restrict__ cand_g, int slices,
+                                                           int slice_cap, int K, int Kp, int64_t r0,
+                                                           uint32_t* flag, int32_t* __restrict__ t_idx,
+                                                           float* __restrict__ t_logit) {
+  __shared__ uint32_t hist[1 << kFusedDigitBits];
+  __shared__ uint64_t keys[kMaxK];
+  __shared__ uint64_t cand[kCand];
+  __shared__ uint32_t s_cnt[kMaxSlices];
+  __shared__ uint32_t wave_tot[kSelThreads / 64];
+  __shared__ uint32_t s_vals[3];
+  __shared__ uint32_t s_fill, s_cand, s_over;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const uint32_t* crow = cnt + static_cast<int64_t>(row) * slices;
+  const uint64_t* cg = cand_g + static_cast<int64_t>(row) * slices * slice_cap;
+  const uint64_t* xg = xcand + static_cast<int64_t>(row) * xcap;
+  const uint32_t nx = xcnt[row];
+  for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
+  if (tid == 0) {
+    s_fill = 0;
+    s_cand = 0;
+    s_over = 0;
+  }
+  uint32_t n_part = 0;
+  bool over = false;
+  for (int s = tid; s < slices; s += kSelThreads) {
+    const uint32_t c = crow[s];
+    s_cnt[s] = c;
+    over |= c > static_cast<uint32_t>(slice_cap);
+    n_part += c;
+  }
+  for (int o = 32; o > 0; o >>= 1) n_part += static_cast<uint32_t>(__shfl_xor(static_cast<int>(n_part), o, 64));
+  if ((tid & 63) == 0) wave_tot[tid >> 6] = n_part;
+  __syncthreads();
+  if (over || (tid == 0 && nx > static_cast<uint32_t>(xcap))) s_over = 1;
+  __syncthreads();
+  uint32_t n = nx;
+  for (int w = 0; w < kSelThreads / 64; ++w) n += wave_tot[w];
+  const bool overflow = s_over != 0;
+  __syncthreads();  // wave_tot is reused by the selection
+  if (overflow || n < static_cast<uint32_t>(K)) {
+    if (tid == 0) *flag = 1;
+    return;
+  }
+  // every used slot of every slice, in slot order; unused slots read as 0
+  const int list = slices * slice_cap;
+  SelectState st{0, 0, static_cast<uint32_t>(K)};
+  if (n <= static_cast<uint32_t>(kCand)) {
+    for (int i0 = 0; i0 < list; i0 += kSelThreads * kPickBatch) {
+      uint64_t k[kPickBatch];
+      bool take[kPickBatch];
+#pragma unroll
+      for (int b = 0; b < kPickBatch; ++b) {
+        const int i = i0 + b * kSelThreads + tid;
+        const int sl = i / slice_cap;
+        take[b] = i < list && static_cast<uint32_t>(i - sl * slice_cap) < s_cnt[sl < slices ? sl : 0];
+        k[b] = take[b] ? cg[i] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < kPickBatch; ++b) wave_append(take[b], k[b], cand, &s_cand);
+    }
+    for (uint32_t i0 = 0; i0 < nx; i0 += kSelThreads) {
+      const uint32_t i = i0 + tid;
+      wave_append(i < nx, i < nx ? xg[i] : 0, cand, &s_cand);
+    }
+    __syncthreads();
+    const uint64_t* cp = cand;
+    auto cand_key = [cp](int i) { return cp[i]; };
+    select_rest<kFusedDigitBits>(cand_key, static_cast<int>(n), st, hist, wave_tot, s_vals);
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const uint64_t key = cand[i];
+      if ((key >> (64 - st.pbits)) >= st.prefix) {
+        const uint32_t slot = atomicAdd(&s_fill, 1u);
+        if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+      }
+    }
+  } else {
+    // More candidates than LDS holds (large K): select in place over every
+    // slot of every slice and the extra slice; unused slots count as 0 (at
+    // least K keys are larger, so they never reach the top K).
+    const uint32_t* sc = s_cnt;
+    auto key_at = [cg, sc, slice_cap, list, xg, nx](int i) -> uint64_t {
+      if (i < list) {
+        const int sl = i / slice_cap;
+        return static_cast<uint32_t>(i - sl * slice_cap) < sc[sl] ? cg[i] : 0;
+      }
+      return static_cast<uint32_t>(i - list) < nx ? xg[i - list] : 0;
+    };
+    const int total = list + static_cast<int>(nx);
+    select_rest<kFusedDigitBits>(key_at, total, st, hist, wave_tot, s_vals);
+    for (int i = tid; i < total; i += kSelThreads) {
+      const uint64_t key = key_at(i);
+      if (key != 0 && (key >> (64 - st.pbits)) >= st.prefix) {
+        const uint32_t slot = atomicAdd(&s_fill, 1u);
+        if (slot < static_cast<uint32_t>(K)) keys[slot] = key;
+      }
+    }
+  }
+  __syncthreads();
+  sort_and_write(keys, K, Kp, r0 + row, t_idx, t_logit);
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequence
+// ---------------------------------------------------------------------------
+
+// The materialised route for rows [c0, c0 + rows), in blocks of fb_rows rows
+// (run_if: NULL, or the redo flag the kernels test before doing anything).
+static void launch_materialised(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx,
+                                float* t_logit, float* z, int64_t c0, int64_t rows, int Kp,
+                                const uint32_t* run_if, hipStream_t st) {
+  for (int64_t b0 = c0; b0 < c0 + rows; b0 += p.fb_rows) {
+    const int brows = static_cast<int>(c0 + rows - b0 < p.fb_rows ? c0 + rows - b0 : p.fb_rows);
     GemmAccParams g;
-    g.A = Operand{h + c0 * p.d, p.d, rows, p.d};
+    g.A = Operand{h + b0 * p.d, p.d, brows, p.d};
     g.B = Operand{W, p.d, p.V, p.d};
     g.nk = static_cast<int32_t>(ceil_div(p.d, kStageK));
     g.C = z;
     g.ldc = p.ld;
-    g.m_lim = rows;
+    g.m_lim = brows;
     g.n_lim = p.V;
     g.beta = 0;
-    g.mblocks = static_cast<int32_t>(ceil_div(rows, kTile));
+    g.mblocks = static_cast<int32_t>(ceil_div(brows, kTile));
     g.nblocks = static_cast<int32_t>(ceil_div(p.V, kTile));
     g.splits = 1;
     g.kper = g.nk;
     g.c_split = 0;
     {
-      TraceScope ts(st, "topk_logits", 2.0 * rows * static_cast<double>(p.V) * p.d,
-                    2.0 * rows * p.d + 2.0 * p.V * p.d + 4.0 * rows * p.V);
-      hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g);
+      TraceScope ts(st, "topk_logits", 2.0 * brows * static_cast<double>(p.V) * p.d,
+                    2.0 * brows * p.d + 2.0 * p.V * p.d + 4.0 * brows * p.V);
+      hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g, run_if);
     }
     {
-      TraceScope ts(st, "topk_select", 0.0, 2.0 * 4.0 * rows * p.V + 8.0 * rows * p.K);
-      hipLaunchKernelGGL(k_topk_select, dim3(rows), dim3(kSelThreads), 0, st, z, p.ld, static_cast<int>(p.V),
-                         p.K, Kp, c0, static_cast<int>((p.flags & FKL_TOPK_DIRECT) != 0), t_idx, t_logit);
+      TraceScope ts(st, "topk_select", 0.0, 2.0 * 4.0 * brows * p.V + 8.0 * brows * p.K);
+      hipLaunchKernelGGL(k_topk_select, dim3(brows), dim3(kSelThreads), 0, st, z, p.ld, static_cast<int>(p.V), p.K,
+                         Kp, b0, static_cast<int>((p.flags & FKL_TOPK_DIRECT) != 0), run_if, t_idx, t_logit);
     }
+  }
+}
+
+hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx, float* t_logit,
+                       char* ws, hipStream_t st) {
+  int Kp = 1;
+  while (Kp < p.K) Kp <<= 1;
+  float* z = reinterpret_cast<float*>(ws + p.off_region);
+  if (!p.fused) {
+    for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
+      const int64_t rows = p.N - c0 < p.chunk ? p.N - c0 : p.chunk;
+      launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, nullptr, st);
+    }
+    return hipGetLastError();
+  }
+  uint32_t* flag = reinterpret_cast<uint32_t*>(ws + p.off_flag);
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(ws + p.off_ws);
+  float* sample = reinterpret_cast<float*>(ws + p.off_sample);
+  uint64_t* thr = reinterpret_cast<uint64_t*>(ws + p.off_thr);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + p.off_cand);
+  uint32_t* xcnt = reinterpret_cast<uint32_t*>(ws + p.off_xcnt);
+  uint64_t* xcand = reinterpret_cast<uint64_t*>(ws + p.off_xcand);
+  const int S = p.n_sample * kTile;
+  const int n_vt = static_cast<int>(ceil_div(p.V, kTile));
+  if (p.n_sample > 0) {
+    const int64_t q = static_cast<int64_t>(S) * (p.d / 8);
+    const int64_t grid = ceil_div(q, 256) < 4096 ? ceil_div(q, 256) : 4096;
+    TraceScope ts(st, "topk_gather", 0.0, 4.0 * S * p.d);
+    hipLaunchKernelGGL(k_gather_tiles, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, W, p.d, p.stride,
+                       p.n_sample, Ws);
+  }
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
+    const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
+    const int rbs = static_cast<int>(ceil_div(rows, kTile));
+    if (p.n_sample > 0) {
+      GemmAccParams g;
+      g.A = Operand{h + c0 * p.d, p.d, rows, p.d};
+      g.B = Operand{Ws, p.d, S, p.d};
+      g.nk = static_cast<int32_t>(ceil_div(p.d, kStageK));
+      g.C = sample;
+      g.ldc = S;
+      g.m_lim = rows;
+      g.n_lim = S;
+      g.beta = 0;
+      g.mblocks = rbs;
+      g.nblocks = p.n_sample;
+      g.splits = 1;
+      g.kper = g.nk;
+      g.c_split = 0;
+      TraceScope ts(st, "topk_sample", 2.0 * rows * static_cast<double>(S) * p.d,
+                    2.0 * rows * p.d + 2.0 * S * p.d + 4.0 * rows * S);
+      hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g,
+                         static_cast<const uint32_t*>(nullptr));
+    }
+    {
+      TraceScope ts(st, "topk_thresh", 0.0, 4.0 * rows * S + 8.0 * rows);
+      hipLaunchKernelGGL(k_topk_thresh, dim3(rows), dim3(kSelThreads), 0, st, sample, S, p.stride, p.j, thr, xcnt,
+                         xcand, p.xcap, flag);
+    }
+    const int splits = topk_splits(p, rows);
+    const int slice_cap = topk_slice_cap(p, splits);
+    {
+      TopkSweepParams sp{h + c0 * p.d, W, p.d, p.V, rows, n_vt, p.stride, p.n_sample, rbs, splits, thr, cnt,
+                         cand, slice_cap};
+      const double cols = static_cast<double>(p.V) - S;
+      TraceScope ts(st, "topk_sweep", 2.0 * rows * cols * p.d, 2.0 * rows * p.d + 2.0 * cols * p.d);
+      // launched even when every tile is sampled: its workgroups then store zero counts
+      hipLaunchKernelGGL(k_topk_sweep, dim3(rbs * splits), dim3(kBlockThreads), 0, st, sp);
+    }
+    {
+      TraceScope ts(st, "topk_pick", 0.0, 4.0 * rows * S + 8.0 * rows * p.K);
+      hipLaunchKernelGGL(k_topk_pick, dim3(rows), dim3(kSelThreads), 0, st, xcnt, xcand, p.xcap, cnt, cand,
+                         2 * splits, slice_cap, p.K, Kp, c0, flag, t_idx, t_logit);
+    }
+    // redo of the pass by the materialised route, only if a row flagged it
+    launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, flag, st);
   }
   return hipGetLastError();
 }

@@ -136,7 +136,42 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
   ++g_launches;
   CHECK(h && W && ti && tl && ws);
   CHECK(p.chunk >= 1 && p.ld % kTile == 0 && p.ld >= p.V);
-  CHECK(p.bytes >= static_cast<size_t>(round_up(p.chunk, kTile)) * p.ld * 4 && p.bytes <= g_ws_bytes);
+  CHECK(p.fb_rows >= 1 && p.fb_rows <= p.chunk);
+  CHECK(p.bytes <= g_ws_bytes);
+  // the materialised route's logits block (also the fused route's redo)
+  CHECK(al256(p.off_region) && p.off_region + static_cast<size_t>(round_up(p.fb_rows, kTile)) * p.ld * 4 <= p.bytes);
+  CHECK(p.off_flag + 4 <= p.off_ws && p.off_ws <= p.off_region);
+  if (p.fused) {
+    const int64_t S = static_cast<int64_t>(p.n_sample) * kTile;
+    const size_t ca = static_cast<size_t>(round_up(p.chunk, kTile));
+    CHECK(p.n_sample >= 0 && p.n_sample <= kTopkMaxSampleTiles);
+    CHECK(p.stride >= kTopkMinStride);
+    // every sampled tile is a full vocabulary tile
+    if (p.n_sample > 0) CHECK(static_cast<int64_t>(p.n_sample - 1) * p.stride < p.V / kTile);
+    CHECK(p.j >= 0 && (p.j == 0 || p.j < S));
+    CHECK(p.target >= 1024 && p.target >= 8 * p.K);
+    CHECK(p.off_ws + static_cast<size_t>(S) * p.d * 2 <= p.off_region);
+    CHECK(p.off_sample == p.off_region && p.off_sample + ca * S * 4 <= p.off_thr && al256(p.off_thr));
+    CHECK(p.off_thr + ca * 8 <= p.off_cnt && al256(p.off_cnt));
+    // every pass (full ones and the last) fits its count and slice regions
+    for (int64_t c0 : {int64_t(0), (ceil_div(p.N, p.chunk) - 1) * p.chunk}) {
+      if (p.N <= 0) break;
+      const int64_t rows = p.N - c0 < p.chunk ? p.N - c0 : p.chunk;
+      const int sp = topk_splits(p, rows);
+      const int cap = topk_slice_cap(p, sp);
+      CHECK(sp >= 1 && cap >= 16);
+      CHECK(p.off_cnt + static_cast<size_t>(rows) * 2 * sp * 4 <= p.off_cand && al256(p.off_cand));
+      CHECK(p.off_cand + static_cast<size_t>(rows) * 2 * sp * cap * 8 <= p.off_xcnt);
+      // slice offsets are formed in 64-bit; counts and slots in 32-bit
+      CHECK(static_cast<int64_t>(2 * sp) * cap < (int64_t(1) << 31));
+      CHECK(2 * sp <= 2 * kTargetBlocks);
+    }
+    CHECK(al256(p.off_xcnt) && p.off_xcnt + ca * 4 <= p.off_xcand && al256(p.off_xcand));
+    CHECK(p.xcap >= 0 && p.xcap <= S && (p.j == 0 ? p.xcap == S : p.xcap >= 2 * p.j));
+    CHECK(p.off_xcand + ca * p.xcap * 8 <= p.bytes);
+    // sweep tiles: the unsampled ones, each addressed in 32-bit tile units
+    CHECK(ceil_div(p.V, kTile) - p.n_sample >= 0);
+  }
   // both builder operands are plain: each view covers one 256-row block
   CHECK(kTile * p.d * 2 <= kMaxView);
   CHECK(p.chunk <= INT32_MAX);
@@ -314,7 +349,7 @@ int main() {
   }
   for (int i = 0; i < 20000; ++i) {
     fkl_topk_shape t{pick(Ns), pick(ds), pick(Vs), static_cast<int32_t>(pick(Ks)),
-                     static_cast<int32_t>(pick(chunks)), static_cast<uint32_t>(next() % 3)};
+                     static_cast<int32_t>(pick(chunks)), static_cast<uint32_t>(next() % 5)};
     drive_topk(t);
   }
   // NULL shapes and pointers

@@ -141,7 +141,7 @@ def test_topk_argument_errors_before_any_device_work():
     assert call(K=101) == 1       # K > V
     assert call(K=2000, V=5000) == 5
     assert call(chunk=-1) == 1
-    assert call(flags=0x2) == 1   # unknown flag
+    assert call(flags=0x4) == 1   # unknown flag
     assert call(flags=fkl.TOPK_DIRECT, ws_bytes=16) == 2  # the whole-row route is a known flag
     assert call(h=0) == 1
     assert call(W=8) == 1         # misaligned
@@ -151,11 +151,22 @@ def test_topk_argument_errors_before_any_device_work():
     assert call(N=0, h=0, W=0, ti=0, tl=0, ws=0) == 0   # nothing to do
 
 
-def test_topk_workspace_is_one_logits_block():
-    b = fkl.topk_workspace_size(16384, 4096, 128256, 100)
-    assert b <= 512 << 20 and b >= 256 * 128256 * 4
-    assert fkl.topk_workspace_size(16384, 4096, 128256, 100, chunk=256) == 256 * 128256 * 4
-    assert fkl.topk_workspace_size(1000, 64, 1000, 10, chunk=300) == 512 * 1024 * 4
+def test_topk_workspace_sizes():
+    """Materialised route: one fp32 logits block of the pass's rows (rounded up
+    to 256) x V (rounded up to 256). Fused route (default): the compact copy of
+    the sampled tiles of W, then the larger of the pass's fused buffers and the
+    logits block of its redo."""
+    M = fkl.TOPK_MATERIALIZE
+    assert fkl.topk_workspace_size(16384, 4096, 128256, 100, chunk=256, flags=M) == 256 + 256 * 128256 * 4
+    assert fkl.topk_workspace_size(1000, 64, 1000, 10, chunk=300, flags=M) == 256 + 512 * 1024 * 4
+    b = fkl.topk_workspace_size(16384, 4096, 128256, 100, flags=M)
+    assert 256 * 128256 * 4 <= b <= (512 << 20) + 256
+    # fused, large head: 16 sampled tiles (every 32nd of 501) of 256 rows x 4096
+    # bf16 = 32 MiB, then a 1024-row logits block (501 MiB) outweighs the 4096-row
+    # pass's sample (64 MiB) and candidate slices (144 MiB)
+    f = fkl.topk_workspace_size(16384, 4096, 128256, 100)
+    assert f == 256 + (16 * 256 * 4096 * 2) + 1024 * 128256 * 4
+    assert fkl.topk_workspace_size(16384, 4096, 128256, 100, flags=fkl.TOPK_DIRECT) == b
 
 
 def test_backward_flags_checked_on_the_host():

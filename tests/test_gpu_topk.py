@@ -125,30 +125,68 @@ def test_topk_integer_logits_exact_large_boundary_bin(direct):
 
 
 @pytest.mark.parametrize("N,d,V,K", [
-    (200, 64, 5000, 7),         # just above the candidate buffer: sampled threshold
-    (130, 64, 4096, 100),       # fits the buffer: every key is a candidate
-    (64, 128, 60000, 1024),     # largest K: the threshold keeps about 2048 keys
+    (200, 64, 5000, 7),         # fused: two sampled tiles; materialised: sampled threshold
+    (130, 64, 4096, 100),       # every key a candidate (the threshold cannot aim below V keys)
+    (64, 128, 60000, 1024),     # largest K: candidates beyond the LDS buffer, picked in place
     (96, 64, 128256, 100),      # the large-head vocabulary
+    (300, 64, 201088, 100),     # a partial last tile, several fused passes
 ])
-def test_topk_sampled_threshold_matches_whole_row_selection(N, d, V, K):
-    """The default route (threshold from a sample, selection among the keys it
-    keeps) and the whole-row route return identical outputs."""
+def test_topk_routes_agree(N, d, V, K):
+    """The fused route (default), the materialised route with a sampled
+    threshold and the materialised whole-row route return identical outputs:
+    the logits come from the same tile code, so the keys are the same."""
     dev = _dev()
     rng = np.random.default_rng(N + V + K)
     h, _ = _to_dev_bf16(rng.standard_normal((N, d)), dev)
     W, _ = _to_dev_bf16(rng.standard_normal((V, d)) / np.sqrt(d), dev)
     print(f"[topk-routes] N={N} d={d} V={V} K={K}", flush=True)
-    a_i, a_l = fkl.topk(h, W, K)
-    b_i, b_l = fkl.topk(h, W, K, direct=True)
+    a_i, a_l = fkl.topk(h, W, K, chunk=128 if N > 200 else 0)
+    b_i, b_l = fkl.topk(h, W, K, materialize=True)
+    c_i, c_l = fkl.topk(h, W, K, direct=True)
     torch.cuda.synchronize()
-    assert torch.equal(a_i, b_i)
-    assert torch.equal(a_l, b_l)
+    assert torch.equal(a_i, b_i) and torch.equal(a_l, b_l)
+    assert torch.equal(a_i, c_i) and torch.equal(a_l, c_l)
+
+
+def _tile_pattern(V, stride=16):
+    """Columns of the fused route's sampled tiles: every stride-th full tile."""
+    n_full = V // 256
+    cols = np.zeros(V, bool)
+    for t in range(0, n_full, stride):
+        cols[t * 256:(t + 1) * 256] = True
+    return cols
+
+
+@pytest.mark.parametrize("sampled_high", [True, False])
+def test_topk_fused_pass_redone_when_the_threshold_misses(sampled_high):
+    """Logits 1 on the sampled tiles and 0 elsewhere: the threshold (a row's
+    j-th largest sampled key) lets only j < K keys through, so every row flags
+    its pass and the materialised route redoes it. The opposite pattern lets
+    more keys through than the candidate list holds (V - S > cap): also redone.
+    Both must give the exact top K, ties by the lower index."""
+    dev = _dev()
+    N, d, V = 16, 16, 20000 if not sampled_high else 5000
+    K = 200 if sampled_high else 37
+    cols = _tile_pattern(V)
+    Wf = np.zeros((V, d), dtype=np.float32)
+    Wf[cols if sampled_high else ~cols, 0] = 1.0
+    hf = np.zeros((N, d), dtype=np.float32)
+    hf[:, 0] = 1.0
+    h, hf = _to_dev_bf16(hf, dev)
+    W, Wf = _to_dev_bf16(Wf, dev)
+    print(f"[topk-redo] V={V} K={K} sampled tiles {'high' if sampled_high else 'low'}", flush=True)
+    ti, tl = fkl.topk(h, W, K)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
+    high = np.nonzero(cols if sampled_high else ~cols)[0]
+    assert (ti.cpu().numpy() == high[:K][None, :]).all()
 
 
 def test_topk_threshold_that_keeps_too_few_keys_is_retried():
-    """Logits that are large only at the positions the threshold sample reads:
-    the first sampled threshold then keeps fewer than K keys and a lower one is
-    taken. Positions whose logits are 1 must come first, by index."""
+    """Materialised route: logits that are large only at the positions its
+    threshold sample reads, so the first sampled threshold keeps fewer than K
+    keys and a lower one is taken. Positions whose logits are 1 must come
+    first, by index."""
     dev = _dev()
     N, d, V, K = 8, 16, 30000, 1024
     # every position of the form 468 * b + i (i < 32) is high: this covers the
@@ -162,7 +200,7 @@ def test_topk_threshold_that_keeps_too_few_keys_is_retried():
     hf[:, 0] = 1.0
     h, hf = _to_dev_bf16(hf, dev)
     W, Wf = _to_dev_bf16(Wf, dev)
-    ti, tl = fkl.topk(h, W, K)
+    ti, tl = fkl.topk(h, W, K, materialize=True)
     torch.cuda.synchronize()
     _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
     assert (ti.cpu().numpy() == hi[:K][None, :]).all()
