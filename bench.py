@@ -246,6 +246,52 @@ def summarize_mfma(counter_csv: str, command: str, trace_csv: str | None = None)
     return "\n".join(lines) + "\n", figures
 
 
+def summarize_counters(counter_csv: str, command: str) -> str:
+    """Markdown from a rocprofv3 --pmc run: each kernel's counters averaged per
+    dispatch, and the ratios that say where its non-MFMA cycles go, for the
+    counters present. GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ counters
+    are summed over the whole chip; SQ_WAVE_CYCLES and SQ_WAIT_* are in units
+    of 4 cycles."""
+    import collections
+    import csv
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(counter_csv)):
+        name = _short_kernel_name(r["Kernel_Name"])
+        per[name][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[name].add(int(r["Dispatch_Id"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = [f"Command: `{command}`", "", "Per dispatch (averages):", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---|" + "---|" * len(names)]
+    for k, c in per.items():
+        n = len(disp[k])
+        lines.append(f"| {k} | {n} | " + " | ".join(f"{c[x] / n:.4g}" for x in names) + " |")
+    lines += ["", "Ratios:", "",
+              "| kernel | LDS bank-conflict cycles / LDS active cycles | LDS active, % of CU cycles | "
+              "waves waiting for issue, % of wave cycles | of which for LDS | LDS instr per MFMA | "
+              "other VALU instr per MFMA | L2 hit rate |",
+              "|---|---|---|---|---|---|---|---|"]
+
+    def ratio(a, b, scale=1.0, fmt="{:.3f}"):
+        return fmt.format(scale * a / b) if b else "-"
+
+    for k, c in per.items():
+        cu_cycles = c["GRBM_GUI_ACTIVE"] / 8.0 * 256.0
+        mf = c["SQ_INSTS_MFMA"]
+        lines.append("| " + " | ".join([
+            k,
+            ratio(c["SQ_LDS_BANK_CONFLICT"], c["SQ_LDS_IDX_ACTIVE"]),
+            ratio(c["SQ_LDS_IDX_ACTIVE"], cu_cycles, 100.0, "{:.1f}"),
+            ratio(c["SQ_WAIT_INST_ANY"], c["SQ_WAVE_CYCLES"], 100.0, "{:.1f}"),
+            ratio(c["SQ_WAIT_INST_LDS"], c["SQ_WAVE_CYCLES"], 100.0, "{:.1f}"),
+            ratio(c["SQ_INSTS_LDS"], mf, 1.0, "{:.2f}"),
+            ratio(c["SQ_INSTS_VALU"] - mf, mf, 1.0, "{:.2f}"),
+            ratio(c["TCC_HIT_sum"], c["TCC_HIT_sum"] + c["TCC_MISS_sum"]),
+        ]) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(wl, rows: int):
     """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
     import numpy as np
@@ -387,6 +433,8 @@ def main() -> int:
     ap.add_argument("--summarize-mfma", nargs="+", metavar="CSV",
                     help="COUNTER_CSV [KERNEL_TRACE_CSV]: print MFMA utilisation (and engine clock) per kernel "
                          "from a rocprofv3 counter run, write profiles/mfma.json, and exit (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="markdown of a rocprofv3 counter run: per-kernel averages and cycle ratios (no GPU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE counter runs (no GPU)")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
@@ -401,6 +449,9 @@ def main() -> int:
             json.dump({"source_sha256": kernel_source_hash(), "command": args.command, "kernels": figures}, f,
                       indent=1)
         print(md, end="")
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.command), end="")
         return 0
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib or 1024, args.command)

@@ -295,7 +295,7 @@ fkl_status fkl_validate_terms(const fkl_shape* shape, const fkl_terms* terms, in
  *                        goes to the lowest indices among equal logits.
  * The output is in the layout fkl_forward / fkl_backward read.
  *
- * Default (fused) route, per pass of `chunk` rows (0: 8192, fewer for
+ * Default (fused) route, per pass of `chunk` rows (0: 16384, fewer for
  * K > 128): the logits of a sample of whole vocabulary tiles (every 16th or
  * more sparse, at most 16 tiles) give each row a threshold key aimed at about
  * max(1024, 8K) of its logits; one sweep over the other tiles keeps only the

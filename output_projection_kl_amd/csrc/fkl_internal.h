@@ -132,8 +132,8 @@ struct TopkPlan {
 };
 
 constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logits block (512 MiB)
-constexpr int64_t kTopkFusedRows = 8192;                         // default rows per fused pass
-constexpr int64_t kTopkCandBytes = int64_t(512) << 20;           // bound on a pass's candidate slices
+constexpr int64_t kTopkFusedRows = 16384;                        // default rows per fused pass
+constexpr int64_t kTopkCandBytes = int64_t(1) << 30;             // bound on a pass's candidate slices
 constexpr int kTopkMaxSampleTiles = 16;
 constexpr int kTopkMinStride = 16;
 

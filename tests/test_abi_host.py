@@ -162,10 +162,16 @@ def test_topk_workspace_sizes():
     b = fkl.topk_workspace_size(16384, 4096, 128256, 100, flags=M)
     assert 256 * 128256 * 4 <= b <= (512 << 20) + 256
     # fused, large head: 16 sampled tiles (every 32nd of 501) of 256 rows x 4096
-    # bf16 = 32 MiB, then a 1024-row logits block (501 MiB) outweighs the 4096-row
-    # pass's sample (64 MiB) and candidate slices (144 MiB)
+    # bf16 = 32 MiB, then the one 16384-row pass's buffers, larger than the
+    # redo's 1024-row logits block (501 MiB): the sample's fp32 logits, the
+    # thresholds, 8 candidate slices per row (4 vocabulary splits x 2 column
+    # quarters) of 2 * ceil(1024 / 4) + 16 keys, their counts, and the extra
+    # slice of sampled keys (j = ceil(1024 * 4096 / 128256) = 33, 2j + 256 slots)
+    R, S = 16384, 16 * 256
+    fused = R * S * 4 + R * 8 + R * 8 * 4 + R * 8 * (2 * 256 + 16) * 8 + R * 4 + R * (2 * 33 + 256) * 8
     f = fkl.topk_workspace_size(16384, 4096, 128256, 100)
-    assert f == 256 + (16 * 256 * 4096 * 2) + 1024 * 128256 * 4
+    assert fused > 1024 * 128256 * 4
+    assert f == 256 + S * 4096 * 2 + fused
     assert fkl.topk_workspace_size(16384, 4096, 128256, 100, flags=fkl.TOPK_DIRECT) == b
 
 

@@ -53,3 +53,23 @@ def test_profile_figures_follow_the_code_hash(tmp_path, monkeypatch):
     got = bench.profile_figures("bwd_g", 0.35)
     assert got["mfma_util"] is None and got["hbm_gbs"] is not None
     assert len(got["stale"]) == 1 and got["stale"][0].startswith("mfma")
+
+
+def test_counter_summary_ratios(tmp_path):
+    """--summarize-counters: per-dispatch averages over two dispatches and the
+    cycle ratios (bank-conflict share of LDS cycles, issue waits, L2 hit rate)."""
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    for did in (7, 9):
+        for name, v in (("SQ_INSTS_MFMA", 1000), ("SQ_INSTS_VALU", 1500), ("SQ_INSTS_LDS", 300),
+                        ("SQ_LDS_BANK_CONFLICT", 10), ("SQ_LDS_IDX_ACTIVE", 100), ("GRBM_GUI_ACTIVE", 8000),
+                        ("SQ_WAVE_CYCLES", 400), ("SQ_WAIT_INST_ANY", 40), ("SQ_WAIT_INST_LDS", 4),
+                        ("TCC_HIT_sum", 90), ("TCC_MISS_sum", 10)):
+            rows.append(f"{did},fkl::k_bwd_g(Params),{name},{v}")
+    csv = tmp_path / "c.csv"
+    csv.write_text("\n".join(rows) + "\n")
+    md = bench.summarize_counters(str(csv), "cmd")
+    line = [l for l in md.splitlines() if l.startswith("| k_bwd_g |")]
+    assert line[0].startswith("| k_bwd_g | 2 | 8000 | 300 | 1000 | 1500 | 10 | 100 | 40 | 4 | 400 | 90 | 10 |")
+    # 10/100 conflicts; 100 LDS cycles over 1000 x 256 CU cycles; 40/400 and
+    # 4/400 of wave cycles waiting; 0.3 LDS and 0.5 other VALU per MFMA; 0.9 hits
+    assert line[1] == "| k_bwd_g | 0.100 | 0.0 | 10.0 | 1.0 | 0.30 | 0.50 | 0.900 |"
