@@ -1,6 +1,11 @@
 """Build libfkl.so in-tree with hipcc for gfx950.
 
-Usage: python -m output_projection_kl_amd.build [-v]
+Usage: python -m output_projection_kl_amd.build [-v] [--debug]
+
+--debug builds libfkl_debug.so instead: the same sources with FKL_DEBUG
+defined, whose kernels check their global accesses against the extents the
+host planned and whose entry points report any that fall outside
+(csrc/fkl_debug.h).
 """
 
 from __future__ import annotations
@@ -17,6 +22,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfkl.so")
+DEBUG_BUILD_DIR = os.path.join(ROOT, "_build_debug")
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libfkl_debug.so")
 
 SOURCES = ["fkl_kernels.hip", "fkl_topk.hip", "fkl_api.cpp", "fkl_trace.cpp"]
 ARCH = "gfx950"
@@ -44,14 +51,17 @@ def _common_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfkl.so next to this file. Returns its path."""
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link libfkl.so (libfkl_debug.so with debug)
+    next to this file. Returns its path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    flags = _common_flags()
+    build_dir = DEBUG_BUILD_DIR if debug else BUILD_DIR
+    lib_path = DEBUG_LIB_PATH if debug else LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
+    flags = _common_flags() + (["-DFKL_DEBUG"] if debug else [])
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"]
@@ -66,16 +76,16 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

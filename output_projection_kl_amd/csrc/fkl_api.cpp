@@ -314,10 +314,58 @@ fkl_status check_forward_args(const fkl::Plan& p, const void* h, const void* W, 
   return FKL_OK;
 }
 
+// Debug build (FKL_DEBUG): the call's violation word is cleared before its
+// first launch; after its last, the host waits for the stream and reports the
+// access classes whose bounds checks fired. The release build does neither.
+static_assert(fkl::kDebugWordOffset >= fkl::kValidateCountOffset + 4 && fkl::kDebugWordOffset + 4 <= 256,
+              "the debug word shares the 256-byte control block with the scalars and the validation count");
+
+fkl_status debug_begin(uint32_t* word, hipStream_t stream) {
+#ifdef FKL_DEBUG
+  const hipError_t e = fkl::launch_debug_clear(word, stream);
+  if (e != hipSuccess) {
+    g_last_error = std::string("debug word clear failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+#else
+  (void)word, (void)stream;
+#endif
+  return FKL_OK;
+}
+
+fkl_status debug_end(uint32_t* word, hipStream_t stream) {
+#ifdef FKL_DEBUG
+  static const char* const kNames[fkl::kDebugBits] = {
+      "teacher input rows", "sorted teacher lists", "forward split partials", "row outputs",
+      "MFMA operand views", "gradient block",       "contraction outputs",    "grad_h reduction",
+      "builder workspace",  "builder outputs"};
+  uint32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    g_last_error = std::string("debug word read failed: ") + hipGetErrorString(e);
+    return FKL_EDEVICE;
+  }
+  if (host != 0) {
+    std::string msg = "device bounds check failed (accesses skipped):";
+    for (int b = 0; b < fkl::kDebugBits; ++b)
+      if (host & (1u << b)) msg += std::string(" ") + kNames[b] + ";";
+    g_last_error = msg;
+    return FKL_EDEVICE;
+  }
+#else
+  (void)word, (void)stream;
+#endif
+  return FKL_OK;
+}
+
 fkl_status run_forward(const fkl::Plan& p, const void* h, const void* W, const int32_t* t_idx,
                        const float* t_logit, const uint8_t* row_mask, const float* weight, const int32_t* label,
                        float label_w, float* loss, float* row_lse, float* row_kl, char* ws, hipStream_t stream) {
   fkl_status st = validate_if_asked(p, t_idx, t_logit, weight, label, ws, stream);
+  if (st != FKL_OK) return st;
+  uint32_t* dword = reinterpret_cast<uint32_t*>(ws + p.off_scalars + fkl::kDebugWordOffset);
+  st = debug_begin(dword, stream);
   if (st != FKL_OK) return st;
   fkl::FwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, loss, row_lse, row_kl, ws};
@@ -326,7 +374,7 @@ fkl_status run_forward(const fkl::Plan& p, const void* h, const void* W, const i
     g_last_error = std::string("forward launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
-  return FKL_OK;
+  return debug_end(dword, stream);
 }
 
 }  // namespace
@@ -414,6 +462,10 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
   st = validate_if_asked(p, t_idx, t_logit, weight, label, static_cast<char*>(workspace),
                          static_cast<hipStream_t>(stream));
   if (st != FKL_OK) return st;
+  uint32_t* dword =
+      reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.off_scalars + fkl::kDebugWordOffset);
+  st = debug_begin(dword, static_cast<hipStream_t>(stream));
+  if (st != FKL_OK) return st;
   fkl::BwdArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx, t_logit, row_mask,
                  weight, label, label_w, row_lse, grad_loss, grad_h, grad_W, static_cast<char*>(workspace)};
   const hipError_t e = fkl::launch_backward(p, a, static_cast<hipStream_t>(stream));
@@ -421,7 +473,7 @@ fkl_status fkl_backward(const fkl_shape* shape, const void* h, const void* W, co
     g_last_error = std::string("backward launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
-  return FKL_OK;
+  return debug_end(dword, static_cast<hipStream_t>(stream));
 }
 
 fkl_status fkl_validate_teacher(const fkl_shape* shape, const int32_t* t_idx, const float* t_logit,
@@ -497,13 +549,16 @@ fkl_status fkl_topk(const fkl_topk_shape* shape, const void* h, const void* W, i
   if (!workspace) return fail(FKL_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FKL_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.bytes) return fail(FKL_EWORKSPACE, "workspace is smaller than fkl_topk_workspace_size()");
+  uint32_t* dword = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.off_flag + fkl::kDebugWordOffset);
+  const fkl_status ds = debug_begin(dword, static_cast<hipStream_t>(stream));
+  if (ds != FKL_OK) return ds;
   const hipError_t e = fkl::launch_topk(p, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), t_idx,
                                         t_logit, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("top-k launch failed: ") + hipGetErrorString(e);
     return FKL_EDEVICE;
   }
-  return FKL_OK;
+  return debug_end(dword, static_cast<hipStream_t>(stream));
 }
 
 const char* fkl_status_string(fkl_status status) {

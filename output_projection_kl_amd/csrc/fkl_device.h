@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fkl_debug.h"
 #include "fkl_internal.h"
 
 namespace fkl {
@@ -117,14 +118,32 @@ struct StageSrc {
 // buffer is based at row mn0 and sized to the valid rows, so rows past mn_lim
 // read as zero; chunks past k_lim are masked per stage. LDS: row r at r * 64
 // bytes, 16-byte chunk c at physical chunk c ^ swz_plain(r).
+// The memory a block tile's stage loads of an operand may touch (the buffer
+// view its descriptor covers): rows [mn0, mn0 + used) of a plain operand,
+// cut at mn_lim; for a transposed one, from column mn0 of k-row 0 to the end
+// of k-row k_lim - 1.
+struct OperandView {
+  const uint16_t* base;
+  int64_t bytes;
+};
+
+__device__ __forceinline__ OperandView plain_view(const Operand& op, int64_t mn0, int used) {
+  const int64_t rows = op.mn_lim - mn0 < used ? op.mn_lim - mn0 : used;
+  return OperandView{op.base + mn0 * op.ld, rows > 0 ? rows * op.ld * 2 : 0};
+}
+
+__device__ __forceinline__ OperandView trans_view(const Operand& op, int64_t mn0) {
+  const int64_t bytes = op.k_lim * op.ld * 2 - mn0 * 2;
+  return OperandView{op.base + mn0, bytes > 0 ? bytes : 0};
+}
+
 template <int R, int LW>
 __device__ __forceinline__ StageSrc<LW> make_plain_src(const Operand& op, int64_t mn0, int wave, int lane,
                                                        int used = R) {
   StageSrc<LW> s;
-  const int64_t rows = op.mn_lim - mn0 < used ? op.mn_lim - mn0 : used;
-  const int64_t bytes = rows > 0 ? rows * op.ld * 2 : 0;
-  s.base = op.base + mn0 * op.ld;
-  s.bytes = static_cast<int32_t>(bytes);
+  const OperandView v = plain_view(op, mn0, used);
+  s.base = v.base;
+  s.bytes = static_cast<int32_t>(v.bytes);
 #pragma unroll
   for (int j = 0; j < LW; ++j) {
     const int r = (wave * LW + j) * 16 + (lane >> 2);
@@ -147,9 +166,9 @@ template <int R, int LW>
 __device__ __forceinline__ StageSrc<LW> make_trans_src(const Operand& op, int64_t mn0, int wave, int lane,
                                                        int used = R) {
   StageSrc<LW> s;
-  const int64_t bytes = op.k_lim * op.ld * 2 - mn0 * 2;
-  s.base = op.base + mn0;
-  s.bytes = static_cast<int32_t>(bytes > 0 ? bytes : 0);
+  const OperandView v = trans_view(op, mn0);
+  s.base = v.base;
+  s.bytes = static_cast<int32_t>(v.bytes);
   constexpr int kChunks = R / 8;          // 16-byte chunks per k-row
   constexpr int kRowsPerLoad = 64 / kChunks;
 #pragma unroll
@@ -361,6 +380,33 @@ __device__ __forceinline__ void gemm_mainloop(const Operand& A, const Operand& B
   f.mma(acc);
   wait_vmcnt<0>();
   block_barrier();
+}
+
+// Debug build: the memory a block tile's loads of an operand can reach must
+// lie inside the operand's span: for a transposed operand its whole view; for
+// a plain one the view up to the last row's contraction extent (k_lim rounded
+// up to a 16-byte chunk), since a window along the contraction shifts the
+// view's base by k0 while every load stays below k_lim in its row.
+__device__ __forceinline__ bool dcheck_operand(const DebugCheck& d, int span, const Operand& op, int64_t mn0,
+                                               int used, bool trans) {
+  if (trans) {
+    const OperandView v = trans_view(op, mn0);
+    return dcheck_range(d, span, kDbgOperand, v.base, static_cast<uint64_t>(v.bytes));
+  }
+  const OperandView v = plain_view(op, mn0, used);
+  if (v.bytes == 0) return true;
+  const int64_t rows = v.bytes / (op.ld * 2);
+  const int64_t reach = ((rows - 1) * op.ld + ((op.k_lim + 7) / 8) * 8) * 2;
+  return dcheck_range(d, span, kDbgOperand, v.base, static_cast<uint64_t>(reach));
+}
+
+// The same for both operands of a block tile: A from row (or column) m0, B
+// from n0 with `used_b` of them.
+template <bool TA, bool TB>
+__device__ __forceinline__ void dcheck_operands(const DebugCheck& d, int a_span, int b_span, const Operand& A,
+                                                const Operand& B, int64_t m0, int64_t n0, int used_b) {
+  dcheck_operand(d, a_span, A, m0, kARows, TA);
+  dcheck_operand(d, b_span, B, n0, used_b, TB);
 }
 
 // Workgroup placement. The dispatcher hands workgroups to the eight XCDs

@@ -50,6 +50,24 @@ constexpr size_t kValidateCountOffset = 128;
 
 constexpr int kMaxGradHSplits = 8;
 
+// Debug build (FKL_DEBUG): classes of checked device accesses, the bits of a
+// call's violation word, which sits at this offset in a 256-byte control block
+// of the workspace (the loss's scalars block, the builder's flag block).
+enum DebugBit : uint32_t {
+  kDbgTeacherInput = 1u << 0,  // t_idx / t_logit / label rows read by the teacher prep
+  kDbgTeacherList = 1u << 1,   // per-pass sorted teacher lists and negentropies
+  kDbgPartial = 1u << 2,       // forward split partials
+  kDbgRowOut = 1u << 3,        // row_lse / row_kl / per-block KL sums, row inputs of the backward
+  kDbgOperand = 1u << 4,       // MFMA operand views (h, W, the gradient block, compact W)
+  kDbgGBlock = 1u << 5,        // the bf16 gradient block G
+  kDbgGemmOut = 1u << 6,       // fp32 outputs of the contractions (grad_h, grad_W, partial sums, logits)
+  kDbgReduce = 1u << 7,        // grad_h reductions and the bf16 conversion
+  kDbgTopkWork = 1u << 8,      // builder workspace: thresholds, candidate slices and counts
+  kDbgTopkOut = 1u << 9,       // builder outputs t_idx / t_logit
+};
+constexpr int kDebugBits = 10;
+constexpr size_t kDebugWordOffset = 192;
+
 // Vocabulary splits for the grad_h tiles of one backward launch (rows of the
 // chunk, slab_w columns of the slab) so that no grad_h tile is much longer than
 // the launch's average work per CU; 1 when the launch is balanced without.
@@ -171,6 +189,8 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx,
                            const float* t_logit, int32_t* bad_rows, hipStream_t stream);
+// Zero the debug build's violation word of a call (one small kernel).
+hipError_t launch_debug_clear(uint32_t* word, hipStream_t stream);
 // Rows whose label is outside [0, V) or whose weight is not finite are added
 // to *bad_rows (cleared first when `clear`).
 hipError_t launch_validate_terms(int64_t N, int64_t V, const float* weight, const int32_t* label,

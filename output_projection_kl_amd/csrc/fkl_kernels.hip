@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
                                                       int64_t r0, int32_t rows, int32_t K, int32_t L,
                                                       float invT, int32_t* __restrict__ tsort_idx,
                                                       float* __restrict__ tsort_p,
-                                                      float* __restrict__ negent) {
+                                                      float* __restrict__ negent, DebugCheck dbg) {
+  // dbg spans: 0 t_idx, 1 t_logit, 2 sorted indices, 3 sorted weights, 4 negentropies, 5 labels
   using Key = typename std::conditional<LONG, uint64_t, int32_t>::type;
   __shared__ Key skey[4][1024];
   const int wave = threadIdx.x >> 6;
@@ -116,17 +117,18 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
   float mx = -INFINITY;
   for (int k = lane; k < Kp; k += 64) {
     if constexpr (LONG) {
-      sk[k] = k < K ? (static_cast<uint64_t>(static_cast<uint32_t>(ti[k])) << 32) | static_cast<uint32_t>(k)
+      sk[k] = k < K ? (static_cast<uint64_t>(static_cast<uint32_t>(dload(dbg, 0, kDbgTeacherInput, ti + k))) << 32) |
+                          static_cast<uint32_t>(k)
                     : ~uint64_t(0);
     } else {
-      sk[k] = ti[k];
+      sk[k] = dload(dbg, 0, kDbgTeacherInput, ti + k);
     }
-    if (k < K) mx = fmaxf(mx, tl[k] * invT);
+    if (k < K) mx = fmaxf(mx, dload(dbg, 1, kDbgTeacherInput, tl + k) * invT);
   }
   __builtin_amdgcn_wave_barrier();
   mx = wave_max(mx);
   float se = 0.f;
-  for (int k = lane; k < K; k += 64) se += expf(tl[k] * invT - mx);
+  for (int k = lane; k < K; k += 64) se += expf(dload(dbg, 1, kDbgTeacherInput, tl + k) * invT - mx);
   se = wave_sum(se);
   const float lnorm = mx + logf(se);
   auto index_at = [sk](int k) -> int32_t {
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
     else return sk[k];
   };
   const bool has_label = label != nullptr;
-  const int32_t y = has_label ? label[r0 + r] : 0;
+  const int32_t y = has_label ? dload(dbg, 5, kDbgTeacherInput, label + r0 + r) : 0;
   const float keep = has_label ? 1.0f - label_w : 1.0f;
   // where y goes: the number of teacher indices below it, and whether it is one
   int below = 0, dup = 0;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
   const bool insert = has_label && dup == 0;
   float ne = 0.f;
   for (int k = lane; k < K; k += 64) {
-    const float lp = tl[k] * invT - lnorm;
+    const float lp = dload(dbg, 1, kDbgTeacherInput, tl + k) * invT - lnorm;
     ne += expf(lp) * lp;
   }
   int32_t* oi = tsort_idx + static_cast<int64_t>(r) * L;
@@ -163,8 +165,10 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
         rank += (o < key) | ((o == key) & (j < k));
       }
       if (insert && key > y) ++rank;
-      oi[rank] = key;
-      op[rank] = keep * expf(tl[k] * invT - lnorm) + ((has_label && key == y) ? label_w : 0.0f);
+      dstore(dbg, 2, kDbgTeacherList, oi + rank, key);
+      dstore(dbg, 3, kDbgTeacherList, op + rank,
+             keep * expf(dload(dbg, 1, kDbgTeacherInput, tl + k) * invT - lnorm) +
+                 ((has_label && key == y) ? label_w : 0.0f));
     }
   } else {
     for (int size = 2; size <= Kp; size <<= 1) {
@@ -187,33 +191,35 @@ __global__ __launch_bounds__(256) void k_teacher_prep(const int32_t* __restrict_
       const int32_t key = static_cast<int32_t>(v >> 32);
       const int k = static_cast<int>(v & 0xFFFFFFFFu);
       const int rank = i + ((insert && key > y) ? 1 : 0);
-      oi[rank] = key;
-      op[rank] = keep * expf(tl[k] * invT - lnorm) + ((has_label && key == y) ? label_w : 0.0f);
+      dstore(dbg, 2, kDbgTeacherList, oi + rank, key);
+      dstore(dbg, 3, kDbgTeacherList, op + rank,
+             keep * expf(dload(dbg, 1, kDbgTeacherInput, tl + k) * invT - lnorm) +
+                 ((has_label && key == y) ? label_w : 0.0f));
     }
   }
   ne = wave_sum(ne);
   if (lane == 0) {
-    negent[r] = keep * ne;
+    dstore(dbg, 4, kDbgTeacherList, negent + r, keep * ne);
     if (insert) {
-      oi[below] = y;
-      op[below] = label_w;
+      dstore(dbg, 2, kDbgTeacherList, oi + below, y);
+      dstore(dbg, 3, kDbgTeacherList, op + below, label_w);
     } else if (has_label) {
-      oi[K] = INT_MAX;
-      op[K] = 0.0f;
+      dstore(dbg, 2, kDbgTeacherList, oi + K, static_cast<int32_t>(INT_MAX));
+      dstore(dbg, 3, kDbgTeacherList, op + K, 0.0f);
     }
   }
 }
 
-hipError_t launch_teacher_prep(const int32_t* t_idx, const float* t_logit, const int32_t* label, float label_w,
-                               int64_t r0, int rows, int K, int L, float invT, int32_t* tsort_idx, float* tsort_p,
-                               float* negent, hipStream_t st) {
+// (Launch errors surface through hipGetLastError at the end of the sequence.)
+static void launch_teacher_prep(const int32_t* t_idx, const float* t_logit, const int32_t* label, float label_w,
+                                int64_t r0, int rows, int K, int L, float invT, int32_t* tsort_idx, float* tsort_p,
+                                float* negent, const DebugCheck& dbg, hipStream_t st) {
   if (K <= kPrepRankMaxK)
     hipLaunchKernelGGL(k_teacher_prep<false>, dim3(ceil_div(rows, 4)), dim3(256), 0, st, t_idx, t_logit, label,
-                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent);
+                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent, dbg);
   else
     hipLaunchKernelGGL(k_teacher_prep<true>, dim3(ceil_div(rows, 4)), dim3(256), 0, st, t_idx, t_logit, label,
-                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent);
-  return hipGetLastError();
+                       label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent, dbg);
 }
 
 __global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, Scalars* sc) {
@@ -255,11 +261,15 @@ struct Cursor {
   int K, pos;  // pos: index of entry e0
   int e0, e1, e2, e3;
   float p0, p1, p2, p3;
+  DebugCheck dbg;  // debug build: span 0 = the pass's sorted indices, 1 = their weights
+
+  __device__ __forceinline__ int32_t ld_idx(int k) const { return dload(dbg, 0, kDbgTeacherList, idx + k); }
+  __device__ __forceinline__ float ld_p(int k) const { return dload(dbg, 1, kDbgTeacherList, p + k); }
 
   __device__ __forceinline__ void load_at(int k, int& e, float& q) const {
     if (k < K) {
-      e = idx[k];
-      q = p[k];
+      e = ld_idx(k);
+      q = ld_p(k);
     } else {
       e = INT_MAX;
       q = 0.f;
@@ -282,7 +292,7 @@ struct Cursor {
     const int seg = (K + 15) / 16;
     int sample[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sample[j] = idx[min(j * seg, K - 1)];
+    for (int j = 0; j < 16; ++j) sample[j] = ld_idx(min(j * seg, K - 1));
     int c1 = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) c1 += (j * seg < K) & (sample[j] < target);
@@ -295,7 +305,7 @@ struct Cursor {
       for (int base = lo; base < hi; base += 8) {
         int v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = idx[min(base + e, K - 1)];
+        for (int e = 0; e < 8; ++e) v[e] = ld_idx(min(base + e, K - 1));
 #pragma unroll
         for (int e = 0; e < 8; ++e) c2 += (base + e < hi) & (v[e] < target);
       }
@@ -307,8 +317,8 @@ struct Cursor {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kk = min(start + e, K - 1);
-      ev[e] = idx[kk];
-      pv[e] = p[kk];
+      ev[e] = ld_idx(kk);
+      pv[e] = ld_p(kk);
     }
     e0 = start < K ? ev[0] : INT_MAX;
     p0 = start < K ? pv[0] : 0.f;
@@ -358,6 +368,7 @@ struct FwdSweepParams {
   int32_t n_vt;
   int32_t rbs, splits;  // tile grid: row blocks x vocabulary splits (splits <= n_vt)
   f32x4* partial;  // [splits][2][rbs * 256]: (offset m2 in log2 units, sum of exp2(s log2 e - m2), sum p*z)
+  DebugCheck dbg;  // debug build: spans 0, 1 sorted lists, 2 partials, 3 h, 4 W
 };
 
 // Each thread owns one row (tid & 255) of the block and one 64-column quarter
@@ -381,6 +392,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
   const bool row_ok = row < P.rows;
 
   Cursor cur;
+  cur.dbg = P.dbg;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
            P.K, vt0 * kTile, row_ok && vt0 < vt1);
 
@@ -393,6 +405,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
   for (int vt = vt0; vt < vt1; ++vt) {
     MainAcc acc;
     zero_acc(acc);
+    dcheck_operands<false, false>(P.dbg, 3, 4, A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
+                                  static_cast<int64_t>(vt) * kTile, kTile);
     gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile,
                                            static_cast<int64_t>(vt) * kTile, nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_fwd_sweep(FwdSweepParams P
     cur.refill();
   }
   const int ld = P.rbs * kTile;
-  P.partial[static_cast<int64_t>(split * 2 + sub) * ld + row] = f32x4{m2, se, gz, 0.f};
+  dstore(P.dbg, 2, kDbgPartial, P.partial + static_cast<int64_t>(split * 2 + sub) * ld + row, f32x4{m2, se, gz, 0.f});
 }
 
 // Sixteen lanes per row of the chunk merge the split statistics (each lane a
@@ -470,7 +484,8 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
                                                      const float* __restrict__ weight, float invT,
                                                      float* __restrict__ row_lse,
                                                      float* __restrict__ row_kl,
-                                                     double* __restrict__ block_sum) {
+                                                     double* __restrict__ block_sum, DebugCheck dbg) {
+  // dbg spans: 0 partials, 1 row_lse, 2 row_kl, 3 block sums, 4 negentropies
   __shared__ double red[kCombineRows];
   const int l16 = threadIdx.x & 15;
   const int rl = threadIdx.x >> 4;
@@ -478,13 +493,14 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
   const bool ok = r < rows;
   float M = -INFINITY;
   if (ok)
-    for (int s = l16; s < parts; s += 16) M = fmaxf(M, partial[static_cast<int64_t>(s) * ld + r][0]);
+    for (int s = l16; s < parts; s += 16)
+      M = fmaxf(M, dload(dbg, 0, kDbgPartial, partial + static_cast<int64_t>(s) * ld + r)[0]);
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
   float sum = 0.f, gz = 0.f;
   if (ok) {
     for (int s = l16; s < parts; s += 16) {
-      const f32x4 pr = partial[static_cast<int64_t>(s) * ld + r];
+      const f32x4 pr = dload(dbg, 0, kDbgPartial, partial + static_cast<int64_t>(s) * ld + r);
       if (pr[1] > 0.f) sum += pr[1] * exp2f(pr[0] - M);
       gz += pr[2];
     }
@@ -497,11 +513,11 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
   double kl_d = 0.0;
   if (ok && l16 == 0) {
     const float lse = (M + log2f(sum)) * kLn2;
-    const float kl = negent[r] - gz * invT + lse;
+    const float kl = dload(dbg, 4, kDbgTeacherList, negent + r) - gz * invT + lse;
     const bool valid = !mask || mask[r0 + r] != 0;
     const float w = valid ? (weight ? weight[r0 + r] : 1.0f) : 0.0f;
-    row_lse[r0 + r] = lse;
-    if (row_kl) row_kl[r0 + r] = w > 0.f ? kl : 0.f;
+    dstore(dbg, 1, kDbgRowOut, row_lse + r0 + r, lse);
+    if (row_kl) dstore(dbg, 2, kDbgRowOut, row_kl + r0 + r, w > 0.f ? kl : 0.f);
     kl_d = w > 0.f ? static_cast<double>(w) * kl : 0.0;
   }
   if (l16 == 0) red[rl] = kl_d;
@@ -509,7 +525,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const f32x4* __restrict__ p
   if (threadIdx.x == 0) {
     double t = 0.0;
     for (int i = 0; i < kCombineRows; ++i) t += red[i];
-    block_sum[blockIdx.x] = t;
+    dstore(dbg, 3, kDbgRowOut, block_sum + blockIdx.x, t);
   }
 }
 
@@ -537,6 +553,7 @@ struct BwdGParams {
   uint16_t* G;   // G [pass rows][vslab], row-major
   int32_t n_vt;
   int32_t rbs, splits;  // splits <= n_vt
+  DebugCheck dbg;       // debug build: spans 0, 1 sorted lists, 2 G, 3 h, 4 W, 5 row_lse
 };
 
 // One 256 x 256 tile of G = c_r (softmax(z/T) - p~) per step. The logits tile
@@ -571,8 +588,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
   const float* lse_p = P.row_lse + grow_c;
   const uint8_t mraw = *(P.mask ? P.mask + grow_c : reinterpret_cast<const uint8_t*>(lse_p));
   const float wraw = *(P.weight ? P.weight + grow_c : lse_p);
-  const float lse_r = *lse_p;
+  const float lse_r = dload(P.dbg, 5, kDbgRowOut, lse_p);
   Cursor cur;
+  cur.dbg = P.dbg;
   cur.init(P.tsort_idx + static_cast<int64_t>(row) * P.K, P.tsort_p + static_cast<int64_t>(row) * P.K,
            P.K, static_cast<int>(P.slab0) + vt0 * kTile, row_in && vt0 < vt1);
   float c = 0.f, lse2 = 0.f;
@@ -595,6 +613,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
     MainAcc acc;
     zero_acc(acc);
     const int vbase = static_cast<int>(P.slab0) + vt * kTile;
+    dcheck_operands<false, false>(P.dbg, 3, 4, A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, kTile);
     gemm_mainloop<false, false, kNBW, kWN>(A, B, P.r0 + static_cast<int64_t>(rb) * kTile, vbase, nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
       if ((wn >> 1) == half) stage_half_tile(acc, stage, wm, wn, lane);
@@ -638,8 +657,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
         const int q = tid + i * kBlockThreads;
         const int r = q >> 4;
         const int j = q & 15;
-        *reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(r) * P.ld_g + j * 8) =
-            *reinterpret_cast<const u32x4*>(sb + r * (kStageLd * 4) + (j < 8 ? j * 16 : 256 + (j - 8) * 16));
+        dstore(P.dbg, 2, kDbgGBlock, reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(r) * P.ld_g + j * 8),
+               *reinterpret_cast<const u32x4*>(sb + r * (kStageLd * 4) + (j < 8 ? j * 16 : 256 + (j - 8) * 16)));
       }
       __syncthreads();
     }
@@ -671,35 +690,37 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
 }
 
 // grad_h[rows] (+)= sum over s of the split partial sums, in split order.
+// dbg spans: 0 partial sums, 1 grad_h rows.
 __global__ __launch_bounds__(256) void k_reduce_grad_h(const f32x4* __restrict__ part, int splits,
                                                        int64_t split_stride4, int64_t n4,
-                                                       f32x4* __restrict__ out, int beta) {
+                                                       f32x4* __restrict__ out, int beta, DebugCheck dbg) {
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
-    f32x4 a = beta ? out[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 a = beta ? dload(dbg, 1, kDbgReduce, out + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sp = 0; sp < splits; ++sp) {
-      const f32x4 v = part[sp * split_stride4 + i];
+      const f32x4 v = dload(dbg, 0, kDbgReduce, part + sp * split_stride4 + i);
       a = f32x4{a[0] + v[0], a[1] + v[1], a[2] + v[2], a[3] + v[3]};
     }
-    out[i] = a;
+    dstore(dbg, 1, kDbgReduce, out + i, a);
   }
 }
 
 // bf16 grad_h rows from the fp32 accumulator (round to nearest even), adding
 // the old bf16 values in fp32 first when accumulating.
+// dbg spans: 0 the fp32 accumulator, 1 grad_h rows.
 __global__ __launch_bounds__(256) void k_grad_h_to_bf16(const f32x4* __restrict__ src, int64_t n4,
-                                                        uint16_t* __restrict__ dst, int accumulate) {
+                                                        uint16_t* __restrict__ dst, int accumulate, DebugCheck dbg) {
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
-    f32x4 v = src[i];
+    f32x4 v = dload(dbg, 0, kDbgReduce, src + i);
     bf16x4* o = reinterpret_cast<bf16x4*>(dst) + i;
     if (accumulate) {
-      const bf16x4 old = *o;
+      const bf16x4 old = dload(dbg, 1, kDbgReduce, static_cast<const bf16x4*>(o));
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += static_cast<float>(old[e]);
     }
     bf16x4 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(v[e]);
-    *o = r;
+    dstore(dbg, 1, kDbgReduce, o, r);
   }
 }
 
@@ -766,6 +787,31 @@ static inline int splits_for(int64_t rbs, int64_t tiles) {
   return static_cast<int>(s);
 }
 
+// Extents of the workspace regions and caller buffers of one call, for the
+// debug build's checks (sizes as the plan lays them out).
+struct CallSpans {
+  uint32_t* word;
+  HostSpan t_idx, t_logit, label, list_idx, list_p, negent, h, W;
+};
+
+static CallSpans call_spans(const Plan& p, char* ws, const uint16_t* h, const uint16_t* W, const int32_t* t_idx,
+                            const float* t_logit, const int32_t* label) {
+  const uint64_t list = static_cast<uint64_t>(p.bchunk_alloc) * (p.K + 1) * 4;
+  return CallSpans{reinterpret_cast<uint32_t*>(ws + p.off_scalars + kDebugWordOffset),
+                   {t_idx, static_cast<uint64_t>(p.N) * p.K * 4},
+                   {t_logit, static_cast<uint64_t>(p.N) * p.K * 4},
+                   {label, label ? static_cast<uint64_t>(p.N) * 4 : 0},
+                   {ws + p.off_tidx, list},
+                   {ws + p.off_tp, list},
+                   {ws + p.off_negent, static_cast<uint64_t>(p.bchunk_alloc) * 4},
+                   {h, static_cast<uint64_t>(p.N) * p.d * 2},
+                   {W, static_cast<uint64_t>(p.V) * p.d * 2}};
+}
+
+static DebugCheck prep_check(const CallSpans& c) {
+  return make_debug_check(c.word, {c.t_idx, c.t_logit, c.list_idx, c.list_p, c.negent, c.label});
+}
+
 hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
   Scalars* sc = reinterpret_cast<Scalars*>(a.ws + p.off_scalars);
   float* negent = reinterpret_cast<float*>(a.ws + p.off_negent);
@@ -776,6 +822,12 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
   const float invT = 1.0f / p.T;
   const float k2 = kLog2e / p.T;
   const int32_t L = p.K + (a.label ? 1 : 0);  // teacher list entries per row
+  const CallSpans cs = call_spans(p, a.ws, a.h, a.W, a.t_idx, a.t_logit, a.label);
+  const HostSpan partial_span{partial, static_cast<uint64_t>(kTargetBlocks + p.chunk_alloc / kTile) * 2 * kTile * 16};
+  const HostSpan bsum_span{bsum, static_cast<uint64_t>(p.chunk_alloc / kCombineRows) * 8};
+  const DebugCheck combine_dbg = make_debug_check(
+      cs.word, {partial_span, {a.row_lse, static_cast<uint64_t>(p.N) * 4},
+                {a.row_kl, a.row_kl ? static_cast<uint64_t>(p.N) * 4 : 0}, bsum_span, cs.negent});
 
   hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, a.weight, p.N, sc);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
@@ -784,11 +836,12 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
       launch_teacher_prep(a.t_idx, a.t_logit, a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent,
-                          st);
+                          prep_check(cs), st);
     }
     const int splits = splits_for(rbs, p.n_vt);
     FwdSweepParams fp{a.h, a.W, p.d, p.V, c0, rows, L, k2, tidx, tp,
-                      static_cast<int32_t>(p.n_vt), rbs, splits, partial};
+                      static_cast<int32_t>(p.n_vt), rbs, splits, partial,
+                      make_debug_check(cs.word, {cs.list_idx, cs.list_p, partial_span, cs.h, cs.W})};
     {
       const double dd = static_cast<double>(p.d);
       TraceScope ts(st, "fwd_sweep", 2.0 * rows * static_cast<double>(p.V) * dd,
@@ -800,7 +853,7 @@ hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t st) {
       TraceScope ts(st, "fwd_combine", 0.0, 16.0 * splits * rows + 16.0 * rows);
       hipLaunchKernelGGL(k_fwd_combine, dim3(cblocks), dim3(256), 0, st, partial, 2 * splits,
                          static_cast<int64_t>(rbs) * kTile, rows, c0, negent, a.mask, a.weight, invT, a.row_lse,
-                         a.row_kl, bsum);
+                         a.row_kl, bsum, combine_dbg);
     }
     hipLaunchKernelGGL(k_accumulate, dim3(1), dim3(64), 0, st, bsum, cblocks, sc);
   }
@@ -826,6 +879,10 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
   // fp32 destination of grad_h while the slabs of a chunk are summed: the
   // caller's grad_h, or the workspace accumulator when grad_h is bf16
   float* gh32 = reinterpret_cast<float*>(a.ws + p.off_gh32);
+  const CallSpans cs = call_spans(p, a.ws, a.h, a.W, a.t_idx, a.t_logit, a.label);
+  const HostSpan g_span{G, debug_g_bytes(static_cast<uint64_t>(p.bchunk_alloc) * p.vslab * 2)};
+  const HostSpan ghp_span{a.ws + p.off_ghp, static_cast<uint64_t>(p.ghp_rows) * p.d * 4};
+  const HostSpan gh32_span{gh32, h_bf16 ? static_cast<uint64_t>(p.bchunk_alloc) * p.d * 4 : 0};
 
   if (!want_w && !want_h) return hipGetLastError();
   hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, a.mask, a.weight, p.N, sc);
@@ -841,16 +898,21 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
     {
       TraceScope ts(st, "teacher_prep", 0.0, 16.0 * rows * p.K);
       launch_teacher_prep(a.t_idx, a.t_logit, a.label, a.label_weight, c0, rows, p.K, L, invT, tidx, tp, negent,
-                          st);
+                          prep_check(cs), st);
     }
     const double dd = static_cast<double>(p.d);
+    // this pass's grad_h rows (fp32 or bf16 in the caller's buffer)
+    const HostSpan gh_rows{static_cast<char*>(a.grad_h) + c0 * p.d * (h_bf16 ? 2 : 4),
+                           static_cast<uint64_t>(rows) * p.d * (h_bf16 ? 2 : 4)};
     for (int64_t s = 0; s < n_slabs; ++s) {
       const int64_t slab0 = s * p.vslab;
       const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
       const int nvt = static_cast<int>(ceil_div(slab_w, kTile));
       const int splits = splits_for(rbs, nvt);
       BwdGParams gp{a.h, a.W, p.d, p.V, c0, rows, L, k2, p.T, tidx, tp, a.row_lse, a.mask, a.weight,
-                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, rbs, splits};
+                    a.grad_loss, sc, slab0, slab_w, p.vslab, G, nvt, rbs, splits,
+                    make_debug_check(cs.word, {cs.list_idx, cs.list_p, g_span, cs.h, cs.W,
+                                               {a.row_lse, static_cast<uint64_t>(p.N) * 4}})};
       {
         TraceScope ts(st, "bwd_g", 2.0 * rows * slab_w * dd,
                       2.0 * rows * dd + 2.0 * slab_w * dd + 2.0 * rows * slab_w + 8.0 * rows * p.K);
@@ -885,6 +947,7 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
         hp.beta = s > 0 || (acc_h && !h_bf16);
         hp.c_split = 0;
       }
+      hp.dbg = make_debug_check(cs.word, {hsplits > 1 ? ghp_span : (h_bf16 ? gh32_span : gh_rows), g_span, cs.W});
       GemmAccParams& wp = gp2.gw;
       wp.A = Operand{G, p.vslab, slab_w, rows_written};
       wp.B = Operand{a.h + c0 * p.d, p.d, p.d, rows};
@@ -899,6 +962,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.splits = 1;
       wp.kper = wp.nk;
       wp.c_split = 0;
+      wp.dbg = make_debug_check(
+          cs.word, {{a.grad_W + slab0 * p.d, static_cast<uint64_t>(slab_w) * p.d * 4}, g_span, cs.h});
       gp2.h_tiles = want_h ? hp.mblocks * hp.nblocks * hsplits : 0;
       gp2.w_tiles = want_w ? wp.mblocks * wp.nblocks : 0;
       {
@@ -917,7 +982,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
                            dim3(256), 0, st, reinterpret_cast<const f32x4*>(a.ws + p.off_ghp), hsplits,
                            rows_written * p.d / 4, n4,
                            reinterpret_cast<f32x4*>(h_bf16 ? gh32 : static_cast<float*>(a.grad_h) + c0 * p.d),
-                           static_cast<int>(s > 0 || (acc_h && !h_bf16)));
+                           static_cast<int>(s > 0 || (acc_h && !h_bf16)),
+                           make_debug_check(cs.word, {ghp_span, h_bf16 ? gh32_span : gh_rows}));
       }
     }
     if (want_h && h_bf16) {
@@ -926,7 +992,8 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       TraceScope ts(st, "grad_h_to_bf16", 0.0, (acc_h ? 8.0 : 6.0) * rows * p.d);
       hipLaunchKernelGGL(k_grad_h_to_bf16, dim3(static_cast<unsigned>(cgrid)), dim3(256), 0, st,
                          reinterpret_cast<const f32x4*>(gh32), n4,
-                         static_cast<uint16_t*>(a.grad_h) + c0 * p.d, static_cast<int>(acc_h));
+                         static_cast<uint16_t*>(a.grad_h) + c0 * p.d, static_cast<int>(acc_h),
+                         make_debug_check(cs.word, {gh32_span, gh_rows}));
     }
   }
   return hipGetLastError();
@@ -968,6 +1035,11 @@ hipError_t static_scratch(hipStream_t stream, char** ptr) {
   }
   *ptr = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+hipError_t launch_debug_clear(uint32_t* word, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_int, dim3(1), dim3(64), 0, st, reinterpret_cast<int32_t*>(word), 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_validate(int64_t N, int64_t V, int32_t K, const int32_t* t_idx, const float* t_logit,

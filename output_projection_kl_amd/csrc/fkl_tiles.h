@@ -52,6 +52,7 @@ struct GemmAccParams {
   // and writes its own C + s * c_split (splits = 1: no split).
   int32_t splits, kper;
   int64_t c_split;
+  DebugCheck dbg;  // debug build: span 0 = C (with every split), 1 = A, 2 = B
 };
 
 // Operand restricted to contraction indices [k0, k0 + klen).
@@ -89,6 +90,7 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
   const int wave = tid >> 6;
   f32x4 acc[2][4];
   zero_acc(acc);
+  dcheck_operands<TA, TB>(P.dbg, 1, 2, A, B, m0, n0, kNarrowN);
   gemm_mainloop<TA, TB, 2, 1, 1>(A, B, m0, n0, nk, acc, lds);
   const int rmax = static_cast<int>(min<int64_t>(kTile, P.m_lim - m0));
   const int cmax = static_cast<int>(P.n_lim - n0);
@@ -101,7 +103,8 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
     const int r = q >> 4;
     const int c4 = (q & 15) * 4;
     old[i] = (P.beta && r < rmax && c4 < cmax)
-                 ? *reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4)
+                 ? dload(P.dbg, 0, kDbgGemmOut,
+                         reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4))
                  : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float* stage = reinterpret_cast<float*>(lds);
@@ -120,8 +123,8 @@ __device__ __forceinline__ void narrow_acc_tile(const GemmAccParams& P, const Op
     const int c4 = (q & 15) * 4;
     if (r < rmax && c4 < cmax) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kNarrowLd + c4);
-      *reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4) =
-          f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]};
+      dstore(P.dbg, 0, kDbgGemmOut, reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4),
+             f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]});
     }
   }
   __syncthreads();
@@ -156,8 +159,10 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
   }
   MainAcc acc;
   zero_acc(acc);
-  gemm_mainloop<TA, TB, kNBW, kWN>(k_window<TA>(P.A, k0, klen), k_window<TB>(P.B, k0, klen), m0, n0, nk,
-                                   acc, lds);
+  const Operand Aw = k_window<TA>(P.A, k0, klen);
+  const Operand Bw = k_window<TB>(P.B, k0, klen);
+  dcheck_operands<TA, TB>(P.dbg, 1, 2, Aw, Bw, m0, n0, kTile);
+  gemm_mainloop<TA, TB, kNBW, kWN>(Aw, Bw, m0, n0, nk, acc, lds);
   // Epilogue through LDS: each 256 x 128 half tile is staged in fp32, then
   // 32 lanes per row move 512 contiguous bytes with 16-byte accesses. When
   // accumulating, all of a thread's old values for the half are loaded before
@@ -177,7 +182,8 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
         const int r = q >> 5;
         const int c4 = (q & 31) * 4;
         old[i] = (r < rmax && c4 < cmax)
-                     ? *reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4)
+                     ? dload(P.dbg, 0, kDbgGemmOut,
+                             reinterpret_cast<const f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4))
                      : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     } else {
@@ -193,8 +199,8 @@ __device__ __forceinline__ void gemm_acc_tile(const GemmAccParams& P, int local,
       const int c4 = (q & 31) * 4;
       if (r < rmax && c4 < cmax) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStageLd + c4);
-        *reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4) =
-            f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]};
+        dstore(P.dbg, 0, kDbgGemmOut, reinterpret_cast<f32x4*>(ctile + static_cast<int64_t>(r) * P.ldc + c4),
+               f32x4{old[i][0] + v[0], old[i][1] + v[1], old[i][2] + v[2], old[i][3] + v[3]});
       }
     }
     __syncthreads();

@@ -219,8 +219,9 @@ __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint6
 
 // Bitonic sort of the Kp keys (K selected, the rest 0), descending, and the
 // row's output: the K logits and their indices.
+// (dbg spans 4 and 5: t_idx and t_logit.)
 __device__ void sort_and_write(uint64_t* keys, int K, int Kp, int64_t out_row, int32_t* __restrict__ t_idx,
-                               float* __restrict__ t_logit) {
+                               float* __restrict__ t_logit, const DebugCheck& dbg) {
   const int tid = threadIdx.x;
   for (int size = 2; size <= Kp; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -242,8 +243,8 @@ __device__ void sort_and_write(uint64_t* keys, int K, int Kp, int64_t out_row, i
   const int64_t out = out_row * static_cast<int64_t>(K);
   for (int k = tid; k < K; k += kSelThreads) {
     const uint64_t key = keys[k];
-    t_logit[out + k] = from_ordered_bits(static_cast<uint32_t>(key >> 32));
-    t_idx[out + k] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+    dstore(dbg, 5, kDbgTopkOut, t_logit + out + k, from_ordered_bits(static_cast<uint32_t>(key >> 32)));
+    dstore(dbg, 4, kDbgTopkOut, t_idx + out + k, static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)));
   }
 }
 
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
                                                              int V, int K, int Kp, int64_t r0, int direct,
                                                              const uint32_t* run_if,
                                                              int32_t* __restrict__ t_idx,
-                                                             float* __restrict__ t_logit) {
+                                                             float* __restrict__ t_logit, DebugCheck dbg) {
+  // dbg spans: 0 the logits block, 4 t_idx, 5 t_logit
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t keys[kMaxK];
   __shared__ uint64_t cand[kCand];
@@ -261,6 +263,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
   const int tid = threadIdx.x;
   if (run_if && *run_if == 0) return;
   const float* row = logits + static_cast<int64_t>(blockIdx.x) * ld;
+  if (!dcheck_range(dbg, 0, kDbgTopkWork, row, static_cast<uint64_t>((V + 3) & ~3) * 4)) return;
 
   for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
   if (tid == 0) {
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
     select_row(row, V, K, keys, cand, hist, wave_tot, s_vals, &s_fill, &s_cand);
   }
   __syncthreads();
-  sort_and_write(keys, K, Kp, r0 + blockIdx.x, t_idx, t_logit);
+  sort_and_write(keys, K, Kp, r0 + blockIdx.x, t_idx, t_logit, dbg);
 }
 
 // ---------------------------------------------------------------------------
@@ -403,15 +406,17 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const float* __rest
 // Compact copy of the sampled tiles of W: tile s of the copy is rows
 // [s * stride * 256, + 256) of W (every sampled tile is a full tile). One
 // 16-byte chunk per thread and step.
+// (dbg spans: 0 the compact copy, 1 W.)
 __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict__ W, int64_t d, int stride,
-                                                      int n_sample, uint16_t* __restrict__ Ws) {
+                                                      int n_sample, uint16_t* __restrict__ Ws, DebugCheck dbg) {
   const int64_t per_row = d / 8;
   const int64_t total = static_cast<int64_t>(n_sample) * kTile * per_row;
   for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < total; q += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t r = q / per_row;  // row of the copy
     const int64_t c = q - r * per_row;
     const int64_t src = (r / kTile) * stride * kTile + (r % kTile);
-    reinterpret_cast<u32x4*>(Ws + r * d)[c] = reinterpret_cast<const u32x4*>(W + src * d)[c];
+    dstore(dbg, 0, kDbgTopkWork, reinterpret_cast<u32x4*>(Ws + r * d) + c,
+           dload(dbg, 1, kDbgOperand, reinterpret_cast<const u32x4*>(W + src * d) + c));
   }
 }
 
@@ -451,7 +456,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
                                                              int j, uint64_t* __restrict__ thr,
                                                              uint32_t* __restrict__ xcnt,
                                                              uint64_t* __restrict__ xcand, int xcap,
-                                                             uint32_t* flag) {
+                                                             uint32_t* flag, DebugCheck dbg) {
+  // dbg spans: 0 the sample's logits, 1 extra slices, 2 thresholds, 3 extra-slice counts
   __shared__ uint32_t sv[kMaxSample];
   __shared__ uint64_t hits[kMaxSample];
   __shared__ uint32_t hist[1 << kFusedDigitBits];
@@ -463,6 +469,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
   if (row == 0 && tid == 0) *flag = 0;
   if (tid == 0) s_hits = 0;
   const float* zr = sample + static_cast<int64_t>(row) * S;
+  if (!dcheck_range(dbg, 0, kDbgTopkWork, zr, static_cast<uint64_t>(S) * 4)) return;
   for (int i = tid * 4; i < S; i += kSelThreads * 4) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(zr + i);
 #pragma unroll
@@ -487,10 +494,11 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
   __syncthreads();
   const uint32_t nh = s_hits;
   uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
-  for (uint32_t i = tid; i < nh && i < static_cast<uint32_t>(xcap); i += kSelThreads) xrow[i] = hits[i];
+  for (uint32_t i = tid; i < nh && i < static_cast<uint32_t>(xcap); i += kSelThreads)
+    dstore(dbg, 1, kDbgTopkWork, xrow + i, hits[i]);
   if (tid == 0) {
-    thr[row] = t;
-    xcnt[row] = nh;
+    dstore(dbg, 2, kDbgTopkWork, thr + row, t);
+    dstore(dbg, 3, kDbgTopkWork, xcnt + row, nh);
   }
 }
 
@@ -506,6 +514,7 @@ struct TopkSweepParams {
   uint32_t* cnt;     // [rows][2 * splits]: keys each slice found (may exceed slice_cap)
   uint64_t* cand;    // [rows][2 * splits][slice_cap]
   int32_t slice_cap;
+  DebugCheck dbg;    // debug build: spans 0 thresholds, 1 candidate slices, 2 counts, 3 h, 4 W
 };
 
 // The u-th vocabulary tile that is not sampled (sampled: t % stride == 0 for
@@ -539,11 +548,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
   const int sub = tid >> 8;
   const int row = rb * kTile + rloc;
   const bool row_ok = row < P.rows;
-  const uint64_t thr = row_ok ? P.thr[row] : ~uint64_t(0);
+  const uint64_t thr = row_ok ? dload(P.dbg, 0, kDbgTopkWork, P.thr + row) : ~uint64_t(0);
   const uint32_t thr_hi = static_cast<uint32_t>(thr >> 32);
   const int slices = 2 * P.splits;
   const int slice = 2 * split + sub;
   uint64_t* mine = P.cand + (static_cast<int64_t>(row_ok ? row : 0) * slices + slice) * P.slice_cap;
+  const bool mine_ok = dcheck_range(P.dbg, 1, kDbgTopkWork, mine, static_cast<uint64_t>(P.slice_cap) * 8);
   uint32_t found = 0;
   const Operand A{P.h, P.d, P.rows, P.d};
   const Operand B{P.W, P.d, P.V, P.d};
@@ -553,6 +563,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
     const int vt = unsampled_tile(u, P.stride, P.n_sample);
     MainAcc acc;
     zero_acc(acc);
+    dcheck_operands<false, false>(P.dbg, 3, 4, A, B, static_cast<int64_t>(rb) * kTile,
+                                  static_cast<int64_t>(vt) * kTile, kTile);
     gemm_mainloop<false, false, kNBW, kWN>(A, B, static_cast<int64_t>(rb) * kTile, static_cast<int64_t>(vt) * kTile,
                                            nk, acc, lds);
     for (int half = 0; half < 2; ++half) {
@@ -571,7 +583,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
         for (int e = 0; e < 4; ++e) {
           const uint64_t key = (static_cast<uint64_t>(ob[e]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - (cs + e0 + e));
           if (e0 + e < nvalid && key >= thr) {
-            if (found < static_cast<uint32_t>(P.slice_cap)) mine[found] = key;
+            if (found < static_cast<uint32_t>(P.slice_cap) && mine_ok) mine[found] = key;
             ++found;
           }
         }
@@ -579,7 +591,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
       __syncthreads();
     }
   }
-  if (row_ok) P.cnt[static_cast<int64_t>(row) * slices + slice] = found;
+  if (row_ok) dstore(P.dbg, 2, kDbgTopkWork, P.cnt + static_cast<int64_t>(row) * slices + slice, found);
 }
 
 // One workgroup per row: the top K among the row's candidates (its 2 * splits
@@ -596,7 +608,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
                                                            const uint64_t* __restrict__ cand_g, int slices,
                                                            int slice_cap, int K, int Kp, int64_t r0,
                                                            uint32_t* flag, int32_t* __restrict__ t_idx,
-                                                           float* __restrict__ t_logit) {
+                                                           float* __restrict__ t_logit, DebugCheck dbg) {
+  // dbg spans: 0 extra-slice counts, 1 extra slices, 2 slice counts, 3 candidate slices, 4 t_idx, 5 t_logit
   __shared__ uint32_t hist[1 << kFusedDigitBits];
   __shared__ uint64_t keys[kMaxK];
   __shared__ uint64_t cand[kCand];
@@ -609,7 +622,11 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   const uint32_t* crow = cnt + static_cast<int64_t>(row) * slices;
   const uint64_t* cg = cand_g + static_cast<int64_t>(row) * slices * slice_cap;
   const uint64_t* xg = xcand + static_cast<int64_t>(row) * xcap;
-  const uint32_t nx = xcnt[row];
+  if (!dcheck_range(dbg, 1, kDbgTopkWork, xg, static_cast<uint64_t>(xcap) * 8) ||
+      !dcheck_range(dbg, 2, kDbgTopkWork, crow, static_cast<uint64_t>(slices) * 4) ||
+      !dcheck_range(dbg, 3, kDbgTopkWork, cg, static_cast<uint64_t>(slices) * slice_cap * 8))
+    return;
+  const uint32_t nx = dload(dbg, 0, kDbgTopkWork, xcnt + row);
   for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
   if (tid == 0) {
     s_fill = 0;
@@ -692,7 +709,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
     }
   }
   __syncthreads();
-  sort_and_write(keys, K, Kp, r0 + row, t_idx, t_logit);
+  sort_and_write(keys, K, Kp, r0 + row, t_idx, t_logit, dbg);
 }
 
 // ---------------------------------------------------------------------------
@@ -701,9 +718,15 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
 
 // The materialised route for rows [c0, c0 + rows), in blocks of fb_rows rows
 // (run_if: NULL, or the redo flag the kernels test before doing anything).
+// Extents for the debug build's checks: the call's control word and buffers.
+struct TopkSpans {
+  uint32_t* word;
+  HostSpan h, W, t_idx, t_logit, z;
+};
+
 static void launch_materialised(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx,
                                 float* t_logit, float* z, int64_t c0, int64_t rows, int Kp,
-                                const uint32_t* run_if, hipStream_t st) {
+                                const uint32_t* run_if, const TopkSpans& sp, hipStream_t st) {
   for (int64_t b0 = c0; b0 < c0 + rows; b0 += p.fb_rows) {
     const int brows = static_cast<int>(c0 + rows - b0 < p.fb_rows ? c0 + rows - b0 : p.fb_rows);
     GemmAccParams g;
@@ -720,6 +743,7 @@ static void launch_materialised(const TopkPlan& p, const uint16_t* h, const uint
     g.splits = 1;
     g.kper = g.nk;
     g.c_split = 0;
+    g.dbg = make_debug_check(sp.word, {sp.z, sp.h, sp.W});
     {
       TraceScope ts(st, "topk_logits", 2.0 * brows * static_cast<double>(p.V) * p.d,
                     2.0 * brows * p.d + 2.0 * p.V * p.d + 4.0 * brows * p.V);
@@ -728,7 +752,8 @@ static void launch_materialised(const TopkPlan& p, const uint16_t* h, const uint
     {
       TraceScope ts(st, "topk_select", 0.0, 2.0 * 4.0 * brows * p.V + 8.0 * brows * p.K);
       hipLaunchKernelGGL(k_topk_select, dim3(brows), dim3(kSelThreads), 0, st, z, p.ld, static_cast<int>(p.V), p.K,
-                         Kp, b0, static_cast<int>((p.flags & FKL_TOPK_DIRECT) != 0), run_if, t_idx, t_logit);
+                         Kp, b0, static_cast<int>((p.flags & FKL_TOPK_DIRECT) != 0), run_if, t_idx, t_logit,
+                         make_debug_check(sp.word, {sp.z, {}, {}, {}, sp.t_idx, sp.t_logit}));
     }
   }
 }
@@ -738,10 +763,17 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
   int Kp = 1;
   while (Kp < p.K) Kp <<= 1;
   float* z = reinterpret_cast<float*>(ws + p.off_region);
+  const uint64_t out_bytes = static_cast<uint64_t>(p.N) * p.K * 4;
+  const TopkSpans sp{reinterpret_cast<uint32_t*>(ws + p.off_flag + kDebugWordOffset),
+                     {h, static_cast<uint64_t>(p.N) * p.d * 2},
+                     {W, static_cast<uint64_t>(p.V) * p.d * 2},
+                     {t_idx, out_bytes},
+                     {t_logit, out_bytes},
+                     {z, static_cast<uint64_t>(round_up(p.fb_rows, kTile)) * p.ld * 4}};
   if (!p.fused) {
     for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
       const int64_t rows = p.N - c0 < p.chunk ? p.N - c0 : p.chunk;
-      launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, nullptr, st);
+      launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, nullptr, sp, st);
     }
     return hipGetLastError();
   }
@@ -755,12 +787,20 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
   uint64_t* xcand = reinterpret_cast<uint64_t*>(ws + p.off_xcand);
   const int S = p.n_sample * kTile;
   const int n_vt = static_cast<int>(ceil_div(p.V, kTile));
+  const uint64_t chunk_alloc = static_cast<uint64_t>(round_up(p.chunk, kTile));
+  const HostSpan ws_span{Ws, static_cast<uint64_t>(S) * p.d * 2};
+  const HostSpan sample_span{sample, chunk_alloc * S * 4};
+  const HostSpan thr_span{thr, chunk_alloc * 8};
+  const HostSpan cnt_span{cnt, p.off_cand - p.off_cnt};
+  const HostSpan cand_span{cand, p.off_xcnt - p.off_cand};
+  const HostSpan xcnt_span{xcnt, chunk_alloc * 4};
+  const HostSpan xcand_span{xcand, chunk_alloc * p.xcap * 8};
   if (p.n_sample > 0) {
     const int64_t q = static_cast<int64_t>(S) * (p.d / 8);
     const int64_t grid = ceil_div(q, 256) < 4096 ? ceil_div(q, 256) : 4096;
     TraceScope ts(st, "topk_gather", 0.0, 4.0 * S * p.d);
     hipLaunchKernelGGL(k_gather_tiles, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, W, p.d, p.stride,
-                       p.n_sample, Ws);
+                       p.n_sample, Ws, make_debug_check(sp.word, {ws_span, sp.W}));
   }
   for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
     const int rows = static_cast<int>(p.N - c0 < p.chunk ? p.N - c0 : p.chunk);
@@ -780,6 +820,7 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
       g.splits = 1;
       g.kper = g.nk;
       g.c_split = 0;
+      g.dbg = make_debug_check(sp.word, {sample_span, sp.h, ws_span});
       TraceScope ts(st, "topk_sample", 2.0 * rows * static_cast<double>(S) * p.d,
                     2.0 * rows * p.d + 2.0 * S * p.d + 4.0 * rows * S);
       hipLaunchKernelGGL(k_topk_logits, dim3(g.mblocks * g.nblocks), dim3(kBlockThreads), 0, st, g,
@@ -788,25 +829,27 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
     {
       TraceScope ts(st, "topk_thresh", 0.0, 4.0 * rows * S + 8.0 * rows);
       hipLaunchKernelGGL(k_topk_thresh, dim3(rows), dim3(kSelThreads), 0, st, sample, S, p.stride, p.j, thr, xcnt,
-                         xcand, p.xcap, flag);
+                         xcand, p.xcap, flag,
+                         make_debug_check(sp.word, {sample_span, xcand_span, thr_span, xcnt_span}));
     }
     const int splits = topk_splits(p, rows);
     const int slice_cap = topk_slice_cap(p, splits);
     {
-      TopkSweepParams sp{h + c0 * p.d, W, p.d, p.V, rows, n_vt, p.stride, p.n_sample, rbs, splits, thr, cnt,
-                         cand, slice_cap};
+      TopkSweepParams swp{h + c0 * p.d, W, p.d, p.V, rows, n_vt, p.stride, p.n_sample, rbs, splits, thr, cnt,
+                          cand, slice_cap, make_debug_check(sp.word, {thr_span, cand_span, cnt_span, sp.h, sp.W})};
       const double cols = static_cast<double>(p.V) - S;
       TraceScope ts(st, "topk_sweep", 2.0 * rows * cols * p.d, 2.0 * rows * p.d + 2.0 * cols * p.d);
       // launched even when every tile is sampled: its workgroups then store zero counts
-      hipLaunchKernelGGL(k_topk_sweep, dim3(rbs * splits), dim3(kBlockThreads), 0, st, sp);
+      hipLaunchKernelGGL(k_topk_sweep, dim3(rbs * splits), dim3(kBlockThreads), 0, st, swp);
     }
     {
       TraceScope ts(st, "topk_pick", 0.0, 4.0 * rows * S + 8.0 * rows * p.K);
       hipLaunchKernelGGL(k_topk_pick, dim3(rows), dim3(kSelThreads), 0, st, xcnt, xcand, p.xcap, cnt, cand,
-                         2 * splits, slice_cap, p.K, Kp, c0, flag, t_idx, t_logit);
+                         2 * splits, slice_cap, p.K, Kp, c0, flag, t_idx, t_logit,
+                         make_debug_check(sp.word, {xcnt_span, xcand_span, cnt_span, cand_span, sp.t_idx, sp.t_logit}));
     }
     // redo of the pass by the materialised route, only if a row flagged it
-    launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, flag, st);
+    launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, flag, sp, st);
   }
   return hipGetLastError();
 }
