@@ -130,6 +130,8 @@ def test_topk_integer_logits_exact_large_boundary_bin(direct):
     (64, 128, 60000, 1024),     # largest K: candidates beyond the LDS buffer, picked in place
     (96, 64, 128256, 100),      # the large-head vocabulary
     (300, 64, 201088, 100),     # a partial last tile, several fused passes
+    (16684, 64, 20000, 100),    # default passes: one of 16384 rows, then a ragged one of 300
+    (8200, 32, 9000, 700),      # K > 128: shorter default passes (5888 rows, then 2312)
 ])
 def test_topk_routes_agree(N, d, V, K):
     """The fused route (default), the materialised route with a sampled
@@ -140,7 +142,7 @@ def test_topk_routes_agree(N, d, V, K):
     h, _ = _to_dev_bf16(rng.standard_normal((N, d)), dev)
     W, _ = _to_dev_bf16(rng.standard_normal((V, d)) / np.sqrt(d), dev)
     print(f"[topk-routes] N={N} d={d} V={V} K={K}", flush=True)
-    a_i, a_l = fkl.topk(h, W, K, chunk=128 if N > 200 else 0)
+    a_i, a_l = fkl.topk(h, W, K, chunk=128 if 200 < N < 1000 else 0)
     b_i, b_l = fkl.topk(h, W, K, materialize=True)
     c_i, c_l = fkl.topk(h, W, K, direct=True)
     torch.cuda.synchronize()
