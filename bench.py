@@ -433,6 +433,9 @@ def main() -> int:
     ap.add_argument("--summarize-mfma", nargs="+", metavar="CSV",
                     help="COUNTER_CSV [KERNEL_TRACE_CSV]: print MFMA utilisation (and engine clock) per kernel "
                          "from a rocprofv3 counter run, write profiles/mfma.json, and exit (no GPU)")
+    ap.add_argument("--mfma-json", default=MFMA_FILE,
+                    help="where --summarize-mfma writes its figures (default profiles/mfma.json, the file the "
+                         "bench line reads)")
     ap.add_argument("--summarize-counters", metavar="CSV",
                     help="markdown of a rocprofv3 counter run: per-kernel averages and cycle ratios (no GPU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -445,7 +448,7 @@ def main() -> int:
     if args.summarize_mfma:
         md, figures = summarize_mfma(args.summarize_mfma[0], args.command,
                                      args.summarize_mfma[1] if len(args.summarize_mfma) > 1 else None)
-        with open(MFMA_FILE, "w") as f:
+        with open(args.mfma_json, "w") as f:
             json.dump({"source_sha256": kernel_source_hash(), "command": args.command, "kernels": figures}, f,
                       indent=1)
         print(md, end="")
