@@ -132,6 +132,8 @@ def test_topk_integer_logits_exact_large_boundary_bin(direct):
     (300, 64, 201088, 100),     # a partial last tile, several fused passes
     (16684, 64, 20000, 100),    # default passes: one of 16384 rows, then a ragged one of 300
     (8200, 32, 9000, 700),      # K > 128: shorter default passes (5888 rows, then 2312)
+    (64, 65536, 1000, 10),      # the largest hidden size: 2048 contraction stages per tile
+    (5, 64, 1, 1),              # V = K = 1: no sampled tile, one column
 ])
 def test_topk_routes_agree(N, d, V, K):
     """The fused route (default), the materialised route with a sampled
