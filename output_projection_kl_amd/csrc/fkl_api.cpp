@@ -273,6 +273,14 @@ fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
   }
   const size_t block_bytes = align256(static_cast<size_t>(round_up(p->fb_rows, kTile)) * p->ld * 4);
   p->bytes = off + std::max(fused_bytes, block_bytes);
+  // the redo's blocks may fill the whole region: fewer launches when no row
+  // is flagged (each then returns at once)
+  p->redo_rows = p->fb_rows;
+  if (p->fused) {
+    const int64_t fit = static_cast<int64_t>(std::max(fused_bytes, block_bytes) / (static_cast<size_t>(p->ld) * 4)) /
+                        kTile * kTile;
+    if (fit > p->redo_rows) p->redo_rows = std::min(fit, chunk);
+  }
   return FKL_OK;
 }
 

@@ -134,6 +134,8 @@ struct TopkPlan {
   int32_t K;
   int64_t chunk;    // rows per pass
   int64_t fb_rows;  // rows per materialised logits block (<= chunk)
+  int64_t redo_rows;  // rows per block of the fused route's guarded redo (>= fb_rows, <= chunk): as
+                      // many as the pass's fused buffers, which the redo's block replaces, make room for
   int64_t ld;       // row stride of the logits block (V rounded up to 256)
   uint32_t flags;   // FKL_TOPK_* options
   bool fused;       // the fused route runs (otherwise every pass is materialised)

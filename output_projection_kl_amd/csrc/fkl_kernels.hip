@@ -222,12 +222,17 @@ static void launch_teacher_prep(const int32_t* t_idx, const float* t_logit, cons
                        label_w, r0, rows, K, L, invT, tsort_idx, tsort_p, negent, dbg);
 }
 
+// One wave: lane l sums block sums l, l + 64, ... in order, then the 64
+// lane sums are combined by a fixed butterfly, so the result does not depend
+// on timing (the loads of all lanes are in flight together).
 __global__ void k_accumulate(const double* __restrict__ block_sum, int nblocks, Scalars* sc) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double a = sc->acc;
-    for (int i = 0; i < nblocks; ++i) a += block_sum[i];
-    sc->acc = a;
-  }
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64 || blockIdx.x != 0) return;
+  double a = 0.0;
+  for (int i = lane; i < nblocks; i += 64) a += block_sum[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+  if (lane == 0) sc->acc += a;
 }
 
 __global__ void k_finalize(const Scalars* sc, float T, float* loss) {

@@ -716,7 +716,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
 // Launch sequence
 // ---------------------------------------------------------------------------
 
-// The materialised route for rows [c0, c0 + rows), in blocks of fb_rows rows
+// The materialised route for rows [c0, c0 + rows), in blocks of block_rows rows
 // (run_if: NULL, or the redo flag the kernels test before doing anything).
 // Extents for the debug build's checks: the call's control word and buffers.
 struct TopkSpans {
@@ -725,10 +725,10 @@ struct TopkSpans {
 };
 
 static void launch_materialised(const TopkPlan& p, const uint16_t* h, const uint16_t* W, int32_t* t_idx,
-                                float* t_logit, float* z, int64_t c0, int64_t rows, int Kp,
+                                float* t_logit, float* z, int64_t c0, int64_t rows, int64_t block_rows, int Kp,
                                 const uint32_t* run_if, const TopkSpans& sp, hipStream_t st) {
-  for (int64_t b0 = c0; b0 < c0 + rows; b0 += p.fb_rows) {
-    const int brows = static_cast<int>(c0 + rows - b0 < p.fb_rows ? c0 + rows - b0 : p.fb_rows);
+  for (int64_t b0 = c0; b0 < c0 + rows; b0 += block_rows) {
+    const int brows = static_cast<int>(c0 + rows - b0 < block_rows ? c0 + rows - b0 : block_rows);
     GemmAccParams g;
     g.A = Operand{h + b0 * p.d, p.d, brows, p.d};
     g.B = Operand{W, p.d, p.V, p.d};
@@ -769,11 +769,11 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
                      {W, static_cast<uint64_t>(p.V) * p.d * 2},
                      {t_idx, out_bytes},
                      {t_logit, out_bytes},
-                     {z, static_cast<uint64_t>(round_up(p.fb_rows, kTile)) * p.ld * 4}};
+                     {z, static_cast<uint64_t>(round_up(p.fused ? p.redo_rows : p.fb_rows, kTile)) * p.ld * 4}};
   if (!p.fused) {
     for (int64_t c0 = 0; c0 < p.N; c0 += p.chunk) {
       const int64_t rows = p.N - c0 < p.chunk ? p.N - c0 : p.chunk;
-      launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, nullptr, sp, st);
+      launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, p.fb_rows, Kp, nullptr, sp, st);
     }
     return hipGetLastError();
   }
@@ -849,7 +849,7 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
                          make_debug_check(sp.word, {xcnt_span, xcand_span, cnt_span, cand_span, sp.t_idx, sp.t_logit}));
     }
     // redo of the pass by the materialised route, only if a row flagged it
-    launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, Kp, flag, sp, st);
+    launch_materialised(p, h, W, t_idx, t_logit, z, c0, rows, p.redo_rows, Kp, flag, sp, st);
   }
   return hipGetLastError();
 }

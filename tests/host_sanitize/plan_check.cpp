@@ -137,9 +137,11 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
   CHECK(h && W && ti && tl && ws);
   CHECK(p.chunk >= 1 && p.ld % kTile == 0 && p.ld >= p.V);
   CHECK(p.fb_rows >= 1 && p.fb_rows <= p.chunk);
+  CHECK(p.redo_rows >= p.fb_rows && p.redo_rows <= p.chunk && (!p.fused ? p.redo_rows == p.fb_rows : true));
   CHECK(p.bytes <= g_ws_bytes);
   // the materialised route's logits block (also the fused route's redo)
   CHECK(al256(p.off_region) && p.off_region + static_cast<size_t>(round_up(p.fb_rows, kTile)) * p.ld * 4 <= p.bytes);
+  CHECK(p.off_region + static_cast<size_t>(round_up(p.redo_rows, kTile)) * p.ld * 4 <= p.bytes);
   CHECK(p.off_flag + 4 <= p.off_ws && p.off_ws <= p.off_region);
   if (p.fused) {
     const int64_t S = static_cast<int64_t>(p.n_sample) * kTile;

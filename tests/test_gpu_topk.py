@@ -238,3 +238,29 @@ def test_topk_fullsize_sampled_rows():
     hf = wl.h[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
     Wf = Wt.float().cpu().numpy()
     _check(ti.cpu().numpy()[rows], tl.cpu().numpy()[rows], hf, Wf, 100)
+
+
+def test_topk_fused_redo_spans_several_blocks_at_the_large_head():
+    """A 16384-row pass over the large-head vocabulary in which every row is
+    flagged (logits 1 on the sampled tiles, 0 elsewhere: too few keys reach
+    the threshold), so the guarded redo runs over the whole pass in blocks as
+    large as the pass's fused buffers allow (more rows than the materialised
+    route's own blocks). Its output must equal the materialised route's and be
+    the K lowest indices of the sampled tiles."""
+    dev = _dev()
+    N, d, V, K = 16384, 16, 128256, 100
+    cols = _tile_pattern(V, stride=32)  # 501 full tiles: every 32nd is sampled
+    Wf = np.zeros((V, d), dtype=np.float32)
+    Wf[cols, 0] = 1.0
+    hf = np.zeros((N, d), dtype=np.float32)
+    hf[:, 0] = 1.0
+    h, _ = _to_dev_bf16(hf, dev)
+    W, _ = _to_dev_bf16(Wf, dev)
+    print(f"[topk-redo-blocks] N={N} V={V} K={K}", flush=True)
+    a_i, a_l = fkl.topk(h, W, K)
+    b_i, b_l = fkl.topk(h, W, K, materialize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_i, b_i) and torch.equal(a_l, b_l)
+    high = np.nonzero(cols)[0]
+    assert (a_i.cpu().numpy() == high[:K][None, :]).all()
+    assert (a_l.cpu().numpy() == 1.0).all()
