@@ -907,8 +907,10 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
     }
     const double dd = static_cast<double>(p.d);
     // this pass's grad_h rows (fp32 or bf16 in the caller's buffer)
-    const HostSpan gh_rows{static_cast<char*>(a.grad_h) + c0 * p.d * (h_bf16 ? 2 : 4),
-                           static_cast<uint64_t>(rows) * p.d * (h_bf16 ? 2 : 4)};
+    // (grad_h is NULL when it is skipped: no kernel then writes it)
+    const HostSpan gh_rows = want_h ? HostSpan{static_cast<char*>(a.grad_h) + c0 * p.d * (h_bf16 ? 2 : 4),
+                                               static_cast<uint64_t>(rows) * p.d * (h_bf16 ? 2 : 4)}
+                                    : HostSpan{nullptr, 0};
     for (int64_t s = 0; s < n_slabs; ++s) {
       const int64_t slab0 = s * p.vslab;
       const int slab_w = static_cast<int>(p.V - slab0 < p.vslab ? p.V - slab0 : p.vslab);
@@ -967,8 +969,9 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
       wp.splits = 1;
       wp.kper = wp.nk;
       wp.c_split = 0;
-      wp.dbg = make_debug_check(
-          cs.word, {{a.grad_W + slab0 * p.d, static_cast<uint64_t>(slab_w) * p.d * 4}, g_span, cs.h});
+      wp.dbg = make_debug_check(cs.word, {want_w ? HostSpan{a.grad_W + slab0 * p.d, static_cast<uint64_t>(slab_w) * p.d * 4}
+                                                 : HostSpan{nullptr, 0},
+                                          g_span, cs.h});
       gp2.h_tiles = want_h ? hp.mblocks * hp.nblocks * hsplits : 0;
       gp2.w_tiles = want_w ? wp.mblocks * wp.nblocks : 0;
       {

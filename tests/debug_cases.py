@@ -66,6 +66,17 @@ def case_terms_k1024(fkl, torch, dev):
     return {"loss": _np(loss), "lse": _np(lse), "kl": _np(kl), "gh": _np(gh), "gW": _np(gW)}
 
 
+def case_skips(fkl, torch, dev):
+    """Each gradient skipped in turn (a frozen head; a frozen body)."""
+    from workloads import make_workload
+    wl = make_workload("tiny", N=260, d=64, V=1100, K=9)
+    h, W, ti, tl, _ = _dev_inputs(wl, torch, dev)
+    _, lse = fkl.forward(h, W, ti, tl, chunk=128)
+    gh, _ = fkl.backward(h, W, ti, tl, lse, chunk=128, need_grad_W=False)
+    _, gW = fkl.backward(h, W, ti, tl, lse, chunk=128, need_grad_h=False)
+    return {"gh": _np(gh), "gW": _np(gW)}
+
+
 def case_topk(fkl, torch, dev):
     """The teacher-cache builder on every route: fused (with a ragged last
     tile and several passes), materialised with a sampled threshold, whole-row,
@@ -118,7 +129,7 @@ def case_planted(fkl, torch, dev):
     return {"planted_msg": np.array(msg)}
 
 
-CASES = {"ragged": case_ragged, "terms_k1024": case_terms_k1024, "topk": case_topk}
+CASES = {"ragged": case_ragged, "terms_k1024": case_terms_k1024, "skips": case_skips, "topk": case_topk}
 
 
 def run_all(planted: bool = False) -> dict:
