@@ -163,10 +163,11 @@ def _tile_pattern(V, stride=16):
 
 @pytest.mark.parametrize("sampled_high", [True, False])
 def test_topk_fused_pass_redone_when_the_threshold_misses(sampled_high):
-    """Logits 1 on the sampled tiles and 0 elsewhere: the threshold (a row's
-    j-th largest sampled key) lets only j < K keys through, so every row flags
-    its pass and the materialised route redoes it. The opposite pattern lets
-    more keys through than the candidate list holds (V - S > cap): also redone.
+    """Logits 1 on the sampled tiles and 0 elsewhere: every sampled logit is
+    equal, so the threshold (cut to the 24-bit prefix of the row's j-th
+    largest sampled key) lets all S sampled keys through, more than the extra
+    slice holds, and every row flags its pass. The opposite pattern lets more
+    keys through than the candidate slices hold (V - S > cap): also redone.
     Both must give the exact top K, ties by the lower index."""
     dev = _dev()
     N, d, V = 16, 16, 20000 if not sampled_high else 5000
@@ -184,6 +185,35 @@ def test_topk_fused_pass_redone_when_the_threshold_misses(sampled_high):
     _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
     high = np.nonzero(cols if sampled_high else ~cols)[0]
     assert (ti.cpu().numpy() == high[:K][None, :]).all()
+
+
+def test_topk_fused_pass_redone_when_fewer_than_k_keys_reach_the_threshold():
+    """Sampled-tile logits 3 (104 columns), 2 (the 105th) and 1 (the rest),
+    all other logits 0: the threshold is exactly the j = 105th largest sampled
+    key, so 105 keys reach it, within the extra slice (466 slots) but fewer
+    than K = 120: the pass is flagged by the count alone and redone. The top
+    K: the 3s and the 2 by index, then the lowest-index 1s."""
+    dev = _dev()
+    N, d, V, K = 16, 16, 5000, 120
+    cols = np.nonzero(_tile_pattern(V))[0]   # 512 sampled columns (tiles 0 and 16)
+    S = cols.size
+    j = -(-max(1024, 8 * K) * S // V)        # the plan's j = ceil(target * S / V)
+    assert S == 512 and j == 105 and j < K and 2 * j + 256 >= j
+    val = np.zeros(V, np.float32)
+    val[cols] = 1.0
+    val[cols[:j - 1]] = 3.0
+    val[cols[j - 1]] = 2.0
+    Wf = np.zeros((V, d), dtype=np.float32)
+    Wf[:, 0] = val
+    hf = np.zeros((N, d), dtype=np.float32)
+    hf[:, 0] = 1.0
+    h, hf = _to_dev_bf16(hf, dev)
+    W, Wf = _to_dev_bf16(Wf, dev)
+    print(f"[topk-redo-count] V={V} K={K} j={j}", flush=True)
+    ti, tl = fkl.topk(h, W, K)
+    torch.cuda.synchronize()
+    _check(ti.cpu().numpy(), tl.cpu().numpy(), hf, Wf, K, exact=True)
+    assert (ti.cpu().numpy() == cols[:K][None, :]).all()
 
 
 def test_topk_threshold_that_keeps_too_few_keys_is_retried():
