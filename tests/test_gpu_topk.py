@@ -216,6 +216,37 @@ def test_topk_fused_pass_redone_when_fewer_than_k_keys_reach_the_threshold():
     assert (ti.cpu().numpy() == cols[:K][None, :]).all()
 
 
+def test_topk_fused_pass_redone_when_a_candidate_slice_overflows():
+    """As above, but every unsampled logit is 2.5, above the threshold: 4096
+    rows make 16 row blocks, so 16 vocabulary splits share the 18 unsampled
+    tiles and some slices receive 256 keys against 144 slots. The count and
+    the extra slice are fine; only the overflow flags the pass. The top K: the
+    3s, then the lowest-index 2.5s."""
+    dev = _dev()
+    N, d, V, K = 4096, 16, 5000, 120
+    cols = np.nonzero(_tile_pattern(V))[0]
+    j = -(-max(1024, 8 * K) * cols.size // V)
+    assert j == 105
+    val = np.full(V, 2.5, np.float32)
+    val[cols] = 1.0
+    val[cols[:j - 1]] = 3.0
+    val[cols[j - 1]] = 2.0
+    Wf = np.zeros((V, d), dtype=np.float32)
+    Wf[:, 0] = val
+    hf = np.zeros((N, d), dtype=np.float32)
+    hf[:, 0] = 1.0
+    h, _ = _to_dev_bf16(hf, dev)
+    W, _ = _to_dev_bf16(Wf, dev)
+    print(f"[topk-redo-slice] N={N} V={V} K={K}", flush=True)
+    ti, tl = fkl.topk(h, W, K)
+    b_i, b_l = fkl.topk(h, W, K, materialize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, b_i) and torch.equal(tl, b_l)
+    rest = np.setdiff1d(np.arange(V), cols)
+    want = np.concatenate([cols[:j - 1], rest[:K - (j - 1)]])
+    assert (ti.cpu().numpy() == want[None, :]).all()
+
+
 def test_topk_threshold_that_keeps_too_few_keys_is_retried():
     """Materialised route: logits that are large only at the positions its
     threshold sample reads, so the first sampled threshold keeps fewer than K
