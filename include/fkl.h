@@ -45,6 +45,12 @@
  *   - Argument errors are reported before any device work is enqueued; such
  *     calls never touch the device, so they are safe without a GPU.
  *   - The same workspace must not be used by two calls in flight at once.
+ *   - The debug build (libfkl_debug.so, compiled with FKL_DEBUG) has the same
+ *     interface and results. Its kernels also check every global store, list
+ *     read and operand view against the extents the host planned, skipping
+ *     any access outside them. Each call then waits for its stream and
+ *     returns FKL_EDEVICE naming the access classes that fired. The release
+ *     build does no such checks.
  */
 #ifndef FKL_H
 #define FKL_H
@@ -61,7 +67,7 @@ typedef enum {
   FKL_EINVAL = 1,       /* bad shape, NULL or misaligned pointer */
   FKL_EWORKSPACE = 2,   /* workspace NULL or smaller than fkl_workspace_size() */
   FKL_EINDEX = 3,       /* bad teacher lists or loss terms (FKL_VALIDATE=1) */
-  FKL_EDEVICE = 4,      /* a HIP call failed; see fkl_last_error() */
+  FKL_EDEVICE = 4,      /* a HIP call failed, or (debug build) a bounds check fired; see fkl_last_error() */
   FKL_EUNSUPPORTED = 5  /* shape outside what this build supports */
 } fkl_status;
 
@@ -323,9 +329,26 @@ typedef struct {
 #define FKL_TOPK_DIRECT 0x1u      /* materialised route, each row selected over the whole row */
 #define FKL_TOPK_MATERIALIZE 0x2u /* materialised route, rows selected from a sampled threshold */
 
-/* Workspace bytes of fkl_topk for this shape (host only). */
+/*
+ * Workspace bytes of fkl_topk for this shape (host only; bytes may be NULL).
+ * The default fused pass of 16384 rows over a 128256-entry vocabulary needs
+ * about 857 MiB (the sample's logits and the candidate slices); a smaller
+ * chunk needs proportionally less. The materialised routes need one logits
+ * block (512 MiB by default, chunk x V rounded up x 4 bytes otherwise).
+ * Errors: FKL_EINVAL for a NULL or malformed shape or an unknown flag;
+ * FKL_EUNSUPPORTED for K > 1024, d > 65536 or N, V beyond 32-bit indexing.
+ */
 fkl_status fkl_topk_workspace_size(const fkl_topk_shape* shape, size_t* bytes);
 
+/*
+ * Builds the cache described above: h, W device inputs; t_idx, t_logit
+ * device outputs (overwritten); workspace device, at least
+ * fkl_topk_workspace_size bytes. Nothing is enqueued when N = 0.
+ * Errors: those of fkl_topk_workspace_size; FKL_EINVAL for NULL or
+ * misaligned arrays; FKL_EWORKSPACE for a NULL, misaligned or short
+ * workspace; FKL_EDEVICE if a launch fails. Deterministic: the output does
+ * not depend on the route, the chunk or timing.
+ */
 fkl_status fkl_topk(const fkl_topk_shape* shape, const void* h, const void* W,
                     int32_t* t_idx, float* t_logit,
                     void* workspace, size_t workspace_bytes, void* stream);
@@ -366,7 +389,9 @@ const char* fkl_status_string(fkl_status status);
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* fkl_last_error(void);
 
-/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH (0.2.0: the plan
+ * query, loss-term validation, the allocation-free forward and the fused
+ * top-K builder). */
 int fkl_version(void);
 
 #ifdef __cplusplus

@@ -583,6 +583,6 @@ const char* fkl_status_string(fkl_status status) {
 
 const char* fkl_last_error(void) { return g_last_error.c_str(); }
 
-int fkl_version(void) { return 100; }
+int fkl_version(void) { return 200; }
 
 }  // extern "C"
