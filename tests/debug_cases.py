@@ -5,10 +5,11 @@ outputs as numpy arrays; the debug build must report no bounds violation and
 return the release build's results (up to the rounding order the compiler
 picks for each build).
 
-Run as a script: python tests/debug_cases.py OUT.npz [--planted]
+Run as a script: python tests/debug_cases.py OUT.npz [--planted] [--fullsize]
 (the library is whatever FKL_LIBRARY names). --planted adds the case whose
 gradient-block extent is narrowed (FKL_DEBUG_SHRINK_G=1), which the debug
-build must report as an error naming the gradient block.
+build must report as an error naming the gradient block. --fullsize adds the
+headline shape and the builder's default pass at the large head.
 """
 
 import os
@@ -109,6 +110,28 @@ def case_topk(fkl, torch, dev):
     return out
 
 
+def case_fullsize(fkl, torch, dev):
+    """The headline shape (four 8192-row passes, 25 slabs of 8192 columns,
+    the full gradient block) and the builder's default 16384-row pass at the
+    large head. Summaries of every output (sums and largest magnitudes in
+    fp64), and the builder's indices exactly."""
+    from workloads.device import make_device_workload, perturbed_head
+    wl = make_device_workload("gptoss20b", dev)
+    loss, lse = fkl.forward(wl.h, wl.W, wl.t_idx, wl.t_logit, T=wl.T, chunk=wl.chunk)
+    gh, gW = fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, lse, T=wl.T, chunk=wl.chunk)
+    out = {"loss": _np(loss)}
+    for name, t in (("lse", lse), ("gh", gh), ("gW", gW)):
+        t64 = t.double()
+        out[f"{name}_sum"] = np.array([t64.sum().item(), t64.abs().sum().item(), t64.abs().max().item()])
+    del gh, gW, lse, wl
+    tw = make_device_workload("temp", dev, N=16384)
+    Wt = perturbed_head(tw.W, 4242, dev)
+    ti, tl = fkl.topk(tw.h, Wt, 100)
+    out["topk_idx"] = _np(ti)
+    out["topk_logit_sum"] = np.array([tl.double().sum().item()])
+    return out
+
+
 def case_planted(fkl, torch, dev):
     """Backward whose gradient block is exactly full (512 rows x 2048 columns),
     with its span narrowed by 4 KiB: the debug build must skip the last row's
@@ -132,13 +155,17 @@ def case_planted(fkl, torch, dev):
 CASES = {"ragged": case_ragged, "terms_k1024": case_terms_k1024, "skips": case_skips, "topk": case_topk}
 
 
-def run_all(planted: bool = False) -> dict:
+def run_all(planted: bool = False, fullsize: bool = False) -> dict:
     import torch
 
     import output_projection_kl_amd as fkl
     dev = torch.device("cuda", 0)
     out = {}
-    cases = dict(CASES, planted=case_planted) if planted else CASES
+    cases = dict(CASES)
+    if fullsize:
+        cases["fullsize"] = case_fullsize
+    if planted:
+        cases["planted"] = case_planted
     for name, fn in cases.items():
         print(f"[debug-cases] {name} with {fkl.library_path()}", flush=True)
         res = fn(fkl, torch, dev)
@@ -148,6 +175,6 @@ def run_all(planted: bool = False) -> dict:
 
 
 if __name__ == "__main__":
-    res = run_all(planted="--planted" in sys.argv)
+    res = run_all(planted="--planted" in sys.argv, fullsize="--fullsize" in sys.argv)
     np.savez(sys.argv[1], **res)
     print("[debug-cases] done", flush=True)
