@@ -70,3 +70,56 @@ def test_forward_backward_replay_in_a_graph():
         l2, lse2 = fkl.forward(h2, W, ti2, tl2, T=0.8, chunk=128)
         fkl.backward(h2, W, ti2, tl2, lse2, T=0.8, chunk=128)
         torch.cuda.synchronize()
+
+
+def test_static_forward_and_builder_replay_in_a_graph():
+    """fkl_forward_static (no workspace argument, its scratch is the library's
+    static array) and the teacher-cache builder (fused route, whose guarded
+    redo kernels test a device flag) captured together and replayed: every
+    replay reproduces the eager outputs, with eager builder and static-forward
+    calls on other inputs in between (they share the static scratch and must
+    not leave anything a replay depends on)."""
+    dev = _dev()
+    wl = make_workload("tiny", N=300, d=136, V=5000, K=7, mask="random25")
+    h, W = _bits(wl.h_bits, dev), _bits(wl.W_bits, dev)
+    ti, tl = torch.from_numpy(wl.t_idx).to(dev), torch.from_numpy(wl.t_logit).to(dev)
+    m = torch.from_numpy(wl.mask).to(dev)
+    K = 50
+    tb = fkl.topk_workspace_size(wl.N, wl.d, wl.V, K)
+    tws = torch.empty(tb, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    ci = torch.empty((wl.N, K), dtype=torch.int32, device=dev)
+    cl = torch.empty((wl.N, K), dtype=torch.float32, device=dev)
+
+    def step():
+        fkl.forward_static(h, W, ti, tl, T=0.8, mask=m, chunk=128, loss=loss, row_lse=lse)
+        fkl.topk(h, W, K, workspace=tws, t_idx=ci, t_logit=cl)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = (loss.clone(), lse.clone(), ci.clone(), cl.clone())
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = make_workload("tiny", 2, N=280, d=136, V=5000, K=7)
+    h2, ti2, tl2 = _bits(other.h_bits, dev), torch.from_numpy(other.t_idx).to(dev), torch.from_numpy(other.t_logit).to(dev)
+    for rep in range(3):
+        for t in (loss, lse, cl):
+            t.fill_(float("nan"))
+        ci.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph-static-builder] replay {rep}", flush=True)
+        for got, want in zip((loss, lse, ci, cl), ref):
+            assert torch.equal(got, want)
+        fkl.forward_static(h2, W, ti2, tl2, T=1.1, chunk=64)
+        fkl.topk(h2, W, 9)
+        torch.cuda.synchronize()
