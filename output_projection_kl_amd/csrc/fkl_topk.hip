@@ -217,12 +217,65 @@ __device__ void select_row(const float* row, int V, int K, uint64_t* keys, uint6
   }
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), mask, 64));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), mask, 64));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Bitonic sort of the Kp keys (K selected, the rest 0), descending, and the
-// row's output: the K logits and their indices.
+// row's output: the K logits and their indices. Up to 128 keys are sorted by
+// the first wave alone in registers (two keys per lane, element e = 2 lane +
+// j; partners more than one element apart are exchanged with shuffles), with
+// zeros past Kp, which sort last (no key is 0): no block barrier. Longer
+// lists are sorted by the whole workgroup through LDS. Called after a block
+// barrier that makes keys[] complete; the kernel ends after it.
 // (dbg spans 4 and 5: t_idx and t_logit.)
 __device__ void sort_and_write(uint64_t* keys, int K, int Kp, int64_t out_row, int32_t* __restrict__ t_idx,
                                float* __restrict__ t_logit, const DebugCheck& dbg) {
   const int tid = threadIdx.x;
+  const int64_t out = out_row * static_cast<int64_t>(K);
+  if (Kp <= 128) {
+    if (tid >= 64) return;
+    const int lane = tid;
+    uint64_t v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) v[j] = 2 * lane + j < Kp ? keys[2 * lane + j] : 0;
+#pragma unroll
+    for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        if (stride == 1) {
+          // partners 2 lane and 2 lane + 1: the lower element keeps the
+          // larger key where the block of `size` sorts descending
+          const bool desc = ((2 * lane) & size) == 0;
+          const uint64_t hi = v[0] > v[1] ? v[0] : v[1];
+          const uint64_t lo = v[0] > v[1] ? v[1] : v[0];
+          v[0] = desc ? hi : lo;
+          v[1] = desc ? lo : hi;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int e = 2 * lane + j;
+            const int partner = e ^ stride;
+            const uint64_t other = shfl_xor_u64(v[j], stride >> 1);
+            const int lower = e < partner ? e : partner;
+            const bool keep_max = (e == lower) == ((lower & size) == 0);
+            v[j] = keep_max ? (v[j] > other ? v[j] : other) : (v[j] > other ? other : v[j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = 2 * lane + j;
+      if (k < K) {
+        dstore(dbg, 5, kDbgTopkOut, t_logit + out + k, from_ordered_bits(static_cast<uint32_t>(v[j] >> 32)));
+        dstore(dbg, 4, kDbgTopkOut, t_idx + out + k, static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(v[j])));
+      }
+    }
+    return;
+  }
   for (int size = 2; size <= Kp; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < Kp; i += kSelThreads) {
@@ -240,7 +293,6 @@ __device__ void sort_and_write(uint64_t* keys, int K, int Kp, int64_t out_row, i
       __syncthreads();
     }
   }
-  const int64_t out = out_row * static_cast<int64_t>(K);
   for (int k = tid; k < K; k += kSelThreads) {
     const uint64_t key = keys[k];
     dstore(dbg, 5, kDbgTopkOut, t_logit + out + k, from_ordered_bits(static_cast<uint32_t>(key >> 32)));
@@ -459,7 +511,6 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
                                                              uint32_t* flag, DebugCheck dbg) {
   // dbg spans: 0 the sample's logits, 1 extra slices, 2 thresholds, 3 extra-slice counts
   __shared__ uint32_t sv[kMaxSample];
-  __shared__ uint64_t hits[kMaxSample];
   __shared__ uint32_t hist[1 << kFusedDigitBits];
   __shared__ uint32_t wave_tot[kSelThreads / 64];
   __shared__ uint32_t s_vals[3];
@@ -486,16 +537,26 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
     select_rest<kFusedDigitBits>(key_at, S, st, hist, wave_tot, s_vals, kThreshBits);
     t = st.pbits >= 64 ? st.prefix : st.prefix << (64 - st.pbits);
   }
+  // the keys at or above the threshold go straight to the row's extra slice
+  // (in no particular order; the first xcap of them), counted in s_hits
+  uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
   for (int i0 = 0; i0 < S; i0 += kSelThreads) {
     const int i = i0 + tid;
     const uint64_t key = i < S ? key_at(i) : 0;
-    wave_append(i < S && key >= t, key, hits, &s_hits);
+    const bool take = i < S && key >= t;
+    const uint64_t m = __ballot(take);
+    if (m == 0) continue;
+    const int lane = tid & 63;
+    const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(&s_hits, static_cast<uint32_t>(__popcll(m)));
+    base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
+    if (take && base + below < static_cast<uint32_t>(xcap)) dstore(dbg, 1, kDbgTopkWork, xrow + base + below, key);
   }
   __syncthreads();
   const uint32_t nh = s_hits;
-  uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
-  for (uint32_t i = tid; i < nh && i < static_cast<uint32_t>(xcap); i += kSelThreads)
-    dstore(dbg, 1, kDbgTopkWork, xrow + i, hits[i]);
   if (tid == 0) {
     dstore(dbg, 2, kDbgTopkWork, thr + row, t);
     dstore(dbg, 3, kDbgTopkWork, xcnt + row, nh);
@@ -601,6 +662,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
 // redo flag is set and nothing is written.
 constexpr int kMaxSlices = 2 * kTargetBlocks;
 constexpr int kPickBatch = 6;  // slot loads issued before any is used
+// candidates gathered into LDS (more are selected in place): room for the
+// usual count (the 1024 targeted for K <= 128) with a small workgroup
+// footprint, so that four rows' workgroups share a CU
+constexpr int kPickCand = 3072;
 
 __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __restrict__ xcnt,
                                                            const uint64_t* __restrict__ xcand, int xcap,
@@ -612,9 +677,10 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   // dbg spans: 0 extra-slice counts, 1 extra slices, 2 slice counts, 3 candidate slices, 4 t_idx, 5 t_logit
   __shared__ uint32_t hist[1 << kFusedDigitBits];
   __shared__ uint64_t keys[kMaxK];
-  __shared__ uint64_t cand[kCand];
+  __shared__ uint64_t cand[kPickCand];
   __shared__ uint32_t s_cnt[kMaxSlices];
   __shared__ uint32_t wave_tot[kSelThreads / 64];
+  __shared__ uint64_t s_and[kSelThreads / 64], s_or[kSelThreads / 64];
   __shared__ uint32_t s_vals[3];
   __shared__ uint32_t s_fill, s_cand, s_over;
   const int tid = threadIdx.x;
@@ -657,7 +723,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   // every used slot of every slice, in slot order; unused slots read as 0
   const int list = slices * slice_cap;
   SelectState st{0, 0, static_cast<uint32_t>(K)};
-  if (n <= static_cast<uint32_t>(kCand)) {
+  if (n <= static_cast<uint32_t>(kPickCand)) {
     for (int i0 = 0; i0 < list; i0 += kSelThreads * kPickBatch) {
       uint64_t k[kPickBatch];
       bool take[kPickBatch];
@@ -676,6 +742,39 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
       wave_append(i < nx, i < nx ? xg[i] : 0, cand, &s_cand);
     }
     __syncthreads();
+    // The candidates all lie at or above the threshold, so their leading bits
+    // (the logit's sign, exponent and first mantissa bits) are mostly shared:
+    // the digits every candidate has in common are fixed up front instead of
+    // being selected one histogram at a time over a single crowded bin.
+    uint64_t all_and = ~uint64_t(0), all_or = 0;
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      all_and &= cand[i];
+      all_or |= cand[i];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      all_and &= shfl_xor_u64(all_and, o);
+      all_or |= shfl_xor_u64(all_or, o);
+    }
+    if ((tid & 63) == 0) {
+      s_and[tid >> 6] = all_and;
+      s_or[tid >> 6] = all_or;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      all_and &= s_and[w];
+      all_or |= s_or[w];
+    }
+    const uint64_t differ = all_and ^ all_or;
+    // length of the common prefix (keys are distinct, so it is shorter than
+    // 64 bits whenever n > 1); the next digit starts at the first bit that
+    // differs
+    const int common = differ == 0 ? 64 : __clzll(static_cast<long long>(differ));
+    if (common > 0) {
+      st.pbits = common;
+      st.prefix = common >= 64 ? all_and : all_and >> (64 - common);
+    }
     const uint64_t* cp = cand;
     auto cand_key = [cp](int i) { return cp[i]; };
     select_rest<kFusedDigitBits>(cand_key, static_cast<int>(n), st, hist, wave_tot, s_vals);
