@@ -302,9 +302,10 @@ fkl_status fkl_validate_terms(const fkl_shape* shape, const fkl_terms* terms, in
  * The output is in the layout fkl_forward / fkl_backward read.
  *
  * Default (fused) route, per pass of `chunk` rows (0: 16384, fewer for
- * K > 128): the logits of a sample of whole vocabulary tiles (every 16th or
+ * large K): the logits of a sample of whole vocabulary tiles (every 16th or
  * more sparse, at most 16 tiles) give each row a threshold key aimed at about
- * max(1024, 8K) of its logits; one sweep over the other tiles keeps only the
+ * T of its logits, T >= 1024 chosen so that a row keeps fewer than K only
+ * with probability below 1e-12; one sweep over the other tiles keeps only the
  * keys at or above it (no [rows x V] block is formed), and the top K is
  * selected exactly among them. A row for which fewer than K keys reached the
  * threshold, or more than its candidate slots hold, makes the pass be redone

@@ -178,6 +178,19 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   return FKL_OK;
 }
 
+// P(X >= j) for X ~ Poisson(mu), summed from the pmf at j (log space).
+double poisson_tail(double mu, int64_t j) {
+  if (j <= 0) return 1.0;
+  double term = std::exp(-mu + static_cast<double>(j) * std::log(mu) - std::lgamma(static_cast<double>(j) + 1.0));
+  double sum = 0.0;
+  for (int64_t k = j; k < j + 100000; ++k) {
+    sum += term;
+    term *= mu / static_cast<double>(k + 1);
+    if (term <= sum * 1e-17) break;
+  }
+  return sum;
+}
+
 fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
   if (!s) return fail(FKL_EINVAL, "shape is NULL");
   if (s->N < 0) return fail(FKL_EINVAL, "N must be >= 0");
@@ -207,12 +220,23 @@ fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p) {
   const int64_t stride = std::max<int64_t>(kTopkMinStride, ceil_div(n_full, kTopkMaxSampleTiles));
   p->stride = static_cast<int32_t>(stride);
   p->n_sample = p->fused ? static_cast<int32_t>(ceil_div(n_full, stride)) : 0;
-  // threshold: aimed at the j-th largest sampled key, so that about `target`
-  // keys of the row are expected at or above it, far enough above K that the
-  // sample's spread (relative spread 1 / sqrt(j)) rarely leaves fewer than K
-  // (j = 0: the sample is too small to aim, every key is a candidate)
+  // threshold: aimed at the j-th largest sampled key, j = ceil(target S / V),
+  // so that about `target` keys of the row are expected at or above it (j = 0:
+  // the sample is too small to aim, every key is a candidate). A row has
+  // fewer than K keys at or above it only when j of its sampled keys lie
+  // among its K largest; their number is about Poisson(K S / V) distributed,
+  // so the target is the smallest count (at least 1024, and at least 16 V / S
+  // so that j >= 16) whose j leaves that tail below kTopkMissTail per row.
+  // (The other way out, more keys than the candidate slices hold, needs about
+  // four times the target, which j >= 16 makes at least as improbable.)
   const int64_t S = static_cast<int64_t>(p->n_sample) * kTile;
-  p->target = std::max(1024, 8 * s->K);
+  int64_t target = std::max<int64_t>({1024, s->K + 1, S > 0 ? ceil_div(16 * s->V, S) : 0});
+  if (S > 0) {
+    const double mu = static_cast<double>(s->K) * static_cast<double>(S) / static_cast<double>(s->V);
+    while (target < s->V && poisson_tail(mu, ceil_div(target * S, s->V)) > kTopkMissTail)
+      target += std::max<int64_t>(16, target / 64);
+  }
+  p->target = static_cast<int32_t>(std::min<int64_t>(target, std::max<int64_t>(s->V, 1024)));
   int64_t j = S > 0 ? ceil_div(static_cast<int64_t>(p->target) * S, s->V) : 0;
   if (j >= S) j = 0;
   p->j = static_cast<int32_t>(j);

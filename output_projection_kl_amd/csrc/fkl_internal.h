@@ -155,6 +155,7 @@ constexpr int64_t kTopkDefaultBlockElems = int64_t(128) << 20;  // default logit
 constexpr int64_t kTopkFusedRows = 16384;                        // default rows per fused pass
 constexpr int64_t kTopkCandBytes = int64_t(1) << 30;             // bound on a pass's candidate slices
 constexpr int kTopkMaxSampleTiles = 16;
+constexpr double kTopkMissTail = 1e-12;  // per-row probability of too few keys at the threshold
 constexpr int kTopkMinStride = 16;
 
 // Vocabulary splits of a fused pass's sweep over `rows` rows (as many
@@ -176,6 +177,8 @@ inline int topk_slice_cap(const TopkPlan& p, int splits) {
 }
 
 fkl_status make_topk_plan(const fkl_topk_shape* s, TopkPlan* p);
+// P(X >= j) for X ~ Poisson(mu) (host; the builder's target uses it).
+double poisson_tail(double mu, int64_t j);
 
 hipError_t launch_forward(const Plan& p, const FwdArgs& a, hipStream_t stream);
 

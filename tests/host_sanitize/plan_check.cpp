@@ -9,6 +9,7 @@
 // a HIP stub aborts if it is ever reached. main() drives every entry point
 // over edge shapes and a seeded random sweep; any sanitizer report, failed
 // check or unexpected status ends the program with a non-zero exit code.
+#include <algorithm>
 #include <cinttypes>
 #include <cmath>
 #include <cstdio>
@@ -151,7 +152,21 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
     // every sampled tile is a full vocabulary tile
     if (p.n_sample > 0) CHECK(static_cast<int64_t>(p.n_sample - 1) * p.stride < p.V / kTile);
     CHECK(p.j >= 0 && (p.j == 0 || p.j < S));
-    CHECK(p.target >= 1024 && p.target >= 8 * p.K);
+    CHECK(p.target >= 1024 && p.target > p.K);
+    // unless the target reached V (or j = 0): j >= 16, and fewer than K keys
+    // at the threshold (j sampled keys among the K largest, about
+    // Poisson(K S / V) of them) has probability <= kTopkMissTail, by a term
+    // sum of its own here
+    if (p.j > 0 && p.target < p.V) {
+      CHECK(p.j >= 16);
+      const double mu = double(p.K) * S / p.V;
+      double tail = 0.0, term = std::exp(-mu);
+      for (int64_t k = 0; k < p.j + 2000; ++k) {
+        if (k >= p.j) tail += term;
+        term *= mu / double(k + 1);
+      }
+      CHECK(tail <= kTopkMissTail * 1.000001);
+    }
     CHECK(p.off_ws + static_cast<size_t>(S) * p.d * 2 <= p.off_region);
     CHECK(p.off_sample == p.off_region && p.off_sample + ca * S * 4 <= p.off_thr && al256(p.off_thr));
     CHECK(p.off_thr + ca * 8 <= p.off_cnt && al256(p.off_cnt));
@@ -169,7 +184,8 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
       CHECK(2 * sp <= 2 * kTargetBlocks);
     }
     CHECK(al256(p.off_xcnt) && p.off_xcnt + ca * 4 <= p.off_xcand && al256(p.off_xcand));
-    CHECK(p.xcap >= 0 && p.xcap <= S && (p.j == 0 ? p.xcap == S : p.xcap >= 2 * p.j));
+    // the extra slice holds all S sampled keys, or at least 2j of them
+    CHECK(p.xcap >= 0 && p.xcap <= S && (p.j == 0 ? p.xcap == S : p.xcap >= std::min<int64_t>(S, 2 * p.j)));
     CHECK(p.off_xcand + ca * p.xcap * 8 <= p.bytes);
     // sweep tiles: the unsampled ones, each addressed in 32-bit tile units
     CHECK(ceil_div(p.V, kTile) - p.n_sample >= 0);
