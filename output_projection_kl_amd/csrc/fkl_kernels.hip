@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t* __restrict__
   wpart[threadIdx.x] = ws;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
+    if (static_cast<int>(threadIdx.x) < s) {
       part[threadIdx.x] += part[threadIdx.x + s];
       wpart[threadIdx.x] += wpart[threadIdx.x + s];
     }
