@@ -676,21 +676,25 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_g(BwdGParams P) {
 // ---------------------------------------------------------------------------
 
 // grad_h[chunk] (+)= G W_slab and grad_W[slab] (+)= G^T h_chunk in one
-// launch: the first h_tiles workgroups take grad_h tiles (the longer
-// contraction, dispatched first; h_tiles counts tiles x vocabulary splits),
-// the rest grad_W tiles.
+// launch (h_tiles counts grad_h tiles x vocabulary splits). The contraction
+// whose tiles are longer is dispatched first, so the shorter tiles fill the
+// launch's last round: with w_first the first w_tiles workgroups take grad_W
+// tiles and the rest grad_h tiles, otherwise the other way round.
 struct GradParams {
   GemmAccParams gh, gw;
   int32_t h_tiles, w_tiles;
+  int32_t w_first;
 };
 
 __global__ __launch_bounds__(kBlockThreads, 1) void k_bwd_grads(GradParams P) {
   __shared__ __align__(16) char lds[kKernelLdsBytes];
   const int w = blockIdx.x;
-  if (w < P.h_tiles) {
-    gemm_acc_tile<false, true>(P.gh, xcd_contiguous_range(w, 0, P.h_tiles), lds);
+  const int h0 = P.w_first ? P.w_tiles : 0;  // first workgroup of the grad_h range
+  const int w0 = P.w_first ? 0 : P.h_tiles;  // first workgroup of the grad_W range
+  if (w >= h0 && w < h0 + P.h_tiles) {
+    gemm_acc_tile<false, true>(P.gh, xcd_contiguous_range(w, h0, P.h_tiles), lds);
   } else {
-    gemm_acc_tile<true, true>(P.gw, xcd_contiguous_range(w, P.h_tiles, P.w_tiles), lds);
+    gemm_acc_tile<true, true>(P.gw, xcd_contiguous_range(w, w0, P.w_tiles), lds);
   }
 }
 
@@ -974,6 +978,9 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t st) {
                                           g_span, cs.h});
       gp2.h_tiles = want_h ? hp.mblocks * hp.nblocks * hsplits : 0;
       gp2.w_tiles = want_w ? wp.mblocks * wp.nblocks : 0;
+      // longer tiles first: grad_h tiles contract over kper stages of the
+      // slab, grad_W tiles over the pass's rows
+      gp2.w_first = wp.nk > hp.kper ? 1 : 0;
       {
         const double hw = (want_h ? 1.0 : 0.0) + (want_w ? 1.0 : 0.0);
         TraceScope ts(st, "bwd_grads", 2.0 * hw * rows * slab_w * dd,
