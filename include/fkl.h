@@ -77,12 +77,14 @@ typedef struct {
   int64_t V;     /* vocabulary size; V >= 1 */
   int32_t K;     /* cached teacher entries per row */
   float T;       /* temperature */
-  int32_t chunk; /* rows per pass; 0 = 4096. With vslab = 0 passes are at
-                    least min(N, 8192) rows in both directions: no
-                    [rows x V] block is ever formed, so a pass costs only a
-                    few MiB forward and the gradient block (whose size vslab
-                    fixes) backward. With an explicit vslab both directions
-                    take passes of chunk rows. Results do not depend on it. */
+  int32_t chunk; /* rows per pass; 0 = 4096. With vslab = 0 forward passes
+                    are at least min(N, 16384) rows and backward passes at
+                    least min(N, 8192) (either floor lowered where an h pass
+                    would reach 2 GiB): no [rows x V] block is ever formed,
+                    so a pass costs only its teacher lists forward and the
+                    gradient block (whose size vslab fixes) backward. With
+                    an explicit vslab both directions take passes of chunk
+                    rows. Results do not depend on it. */
   int32_t vslab; /* vocabulary columns per backward pass; 0 = chosen so that
                     a pass's gradient block holds about 64 Mi elements.
                     Rounded up to a multiple of 256. Results do not depend

@@ -108,22 +108,27 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   // Passes: no [rows x V] block is ever formed, so a forward pass costs only
   // its teacher lists and split statistics (a few MiB at 8192 rows) and a
   // backward pass its gradient block (rows x vslab). With the default slab
-  // both directions take passes of at least min(N, kPassRows) rows (the
-  // forward's W stream is then shared by more rows; a narrower slab keeps the
-  // gradient block's size); an explicit vslab keeps the caller's chunk.
+  // the forward takes passes of at least min(N, kFwdPassRows) rows and the
+  // backward of at least min(N, kPassRows) (more rows share each W stream; a
+  // narrower slab keeps the gradient block's size); an explicit vslab keeps
+  // the caller's chunk in both directions.
+  // The kernels address each operand view (an h chunk, a W slab, the
+  // gradient block) through a buffer descriptor with a 32-bit byte size; a
+  // raised floor stays under that limit.
+  const int64_t kMaxView = (int64_t(1) << 31) - 1;
+  const int64_t view_rows = kMaxView / (2 * s->d) / kTile * kTile;
+  int64_t bchunk = chunk;
   if (s->vslab == 0 && s->N > 0) {
-    const int64_t floor_rows = s->N < kPassRows ? s->N : kPassRows;
-    if (chunk < floor_rows) chunk = floor_rows;
+    chunk = std::max(chunk, std::min<int64_t>({s->N, kFwdPassRows, view_rows}));
+    bchunk = std::max(bchunk, std::min<int64_t>({s->N, kPassRows, view_rows}));
   }
   p->chunk = chunk;
   p->chunk_alloc = round_up(chunk, kTile);
-  int64_t bchunk = chunk;
   p->bchunk = bchunk;
   p->bchunk_alloc = round_up(bchunk, kTile);
-  // The kernels address each operand view (an h chunk, a W slab, the
-  // gradient block) through a buffer descriptor with a 32-bit byte size.
-  const int64_t kMaxView = (int64_t(1) << 31) - 1;
-  if (p->bchunk_alloc * s->d * 2 > kMaxView)
+  // the teacher lists serve the larger of the two directions' passes
+  p->list_rows = std::max(p->chunk_alloc, p->bchunk_alloc);
+  if (p->list_rows * s->d * 2 > kMaxView)
     return fail(FKL_EUNSUPPORTED, "chunk x d too large: a chunk of h must stay under 2 GiB");
   const int64_t slab_cap = std::min(kMaxView / (2 * s->d), kMaxView / (2 * p->bchunk_alloc)) / kTile * kTile;
   int64_t vslab = s->vslab ? s->vslab : std::min<int64_t>(kDefaultSlabElems / p->bchunk_alloc, slab_cap);
@@ -140,13 +145,13 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   p->off_scalars = off;
   off += 256;
   p->off_negent = off;
-  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * 4);
+  off = align256(off + static_cast<size_t>(p->list_rows) * 4);
   p->off_tidx = off;
   // teacher lists hold K entries, or K + 1 with hard labels (rows of the
   // larger of the forward and backward passes)
-  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * (p->K + 1) * 4);
+  off = align256(off + static_cast<size_t>(p->list_rows) * (p->K + 1) * 4);
   p->off_tp = off;
-  off = align256(off + static_cast<size_t>(p->bchunk_alloc) * (p->K + 1) * 4);
+  off = align256(off + static_cast<size_t>(p->list_rows) * (p->K + 1) * 4);
   const size_t shared_end = off;
   // forward: split partials (two per row per workgroup) for up to (256 + rbs)
   // workgroups' rows, then one fp64 KL sum per kCombineRows rows

@@ -14,7 +14,8 @@ constexpr int kTile = 256;          // rows and vocabulary columns of one logits
 constexpr int kContractionStep = 32;  // contraction depth of one LDS stage of the MFMA mainloop
 constexpr int kTargetBlocks = 256;  // workgroups a launch aims for (one per CU on MI355X)
 constexpr int kDefaultChunk = 4096;
-constexpr int kPassRows = 8192;  // pass rows floor (forward and backward) with the default slab
+constexpr int kPassRows = 8192;      // backward pass rows floor with the default slab
+constexpr int kFwdPassRows = 16384;  // forward pass rows floor with the default slab
 constexpr int64_t kDefaultSlabElems = int64_t(64) << 20;  // gradient block of ~64 Mi bf16 (128 MiB)
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -29,6 +30,7 @@ struct Plan {
   int64_t chunk_alloc;  // chunk rounded up to 256
   int64_t bchunk;       // rows per backward pass (>= chunk)
   int64_t bchunk_alloc; // bchunk rounded up to 256
+  int64_t list_rows;    // rows of the teacher lists and negentropies: max(chunk_alloc, bchunk_alloc)
   int64_t vslab;        // vocabulary columns per backward pass, multiple of 256
   int64_t n_vt;         // ceil(V / 256): logits tiles along the vocabulary
   // workspace offsets (bytes)

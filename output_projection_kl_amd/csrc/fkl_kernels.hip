@@ -805,14 +805,14 @@ struct CallSpans {
 
 static CallSpans call_spans(const Plan& p, char* ws, const uint16_t* h, const uint16_t* W, const int32_t* t_idx,
                             const float* t_logit, const int32_t* label) {
-  const uint64_t list = static_cast<uint64_t>(p.bchunk_alloc) * (p.K + 1) * 4;
+  const uint64_t list = static_cast<uint64_t>(p.list_rows) * (p.K + 1) * 4;
   return CallSpans{reinterpret_cast<uint32_t*>(ws + p.off_scalars + kDebugWordOffset),
                    {t_idx, static_cast<uint64_t>(p.N) * p.K * 4},
                    {t_logit, static_cast<uint64_t>(p.N) * p.K * 4},
                    {label, label ? static_cast<uint64_t>(p.N) * 4 : 0},
                    {ws + p.off_tidx, list},
                    {ws + p.off_tp, list},
-                   {ws + p.off_negent, static_cast<uint64_t>(p.bchunk_alloc) * 4},
+                   {ws + p.off_negent, static_cast<uint64_t>(p.list_rows) * 4},
                    {h, static_cast<uint64_t>(p.N) * p.d * 2},
                    {W, static_cast<uint64_t>(p.V) * p.d * 2}};
 }

@@ -49,15 +49,20 @@ int64_t splits_for(int64_t rbs, int64_t tiles) {
 void check_shared(const fkl::Plan& p) {
   CHECK(p.off_scalars == 0);
   CHECK(p.off_negent >= 256 && al256(p.off_negent));
-  CHECK(al256(p.off_tidx) && p.off_tidx >= p.off_negent + static_cast<size_t>(p.bchunk_alloc) * 4);
-  CHECK(al256(p.off_tp) && p.off_tp >= p.off_tidx + static_cast<size_t>(p.bchunk_alloc) * (p.K + 1) * 4);
-  CHECK(p.chunk >= 1 && p.bchunk == p.chunk);
+  // the lists serve the longer of the forward and backward passes
+  CHECK(p.list_rows >= p.chunk_alloc && p.list_rows >= p.bchunk_alloc);
+  CHECK(al256(p.off_tidx) && p.off_tidx >= p.off_negent + static_cast<size_t>(p.list_rows) * 4);
+  CHECK(al256(p.off_tp) && p.off_tp >= p.off_tidx + static_cast<size_t>(p.list_rows) * (p.K + 1) * 4);
+  // the forward's passes are at least as long as the backward's; they differ
+  // only where the forward's floor raised its rows
+  CHECK(p.bchunk >= 1 && p.chunk >= p.bchunk);
+  if (p.chunk != p.bchunk) CHECK(p.chunk <= fkl::kFwdPassRows && p.chunk <= p.N);
   CHECK(p.chunk_alloc % fkl::kTile == 0 && p.chunk_alloc >= p.chunk && p.chunk_alloc - p.chunk < fkl::kTile);
   CHECK(p.bchunk_alloc % fkl::kTile == 0 && p.bchunk_alloc >= p.bchunk);
   CHECK(p.vslab % fkl::kTile == 0 && p.vslab >= fkl::kTile && p.vslab <= fkl::round_up(p.V, fkl::kTile));
   CHECK(p.n_vt == fkl::ceil_div(p.V, fkl::kTile));
   // operand views addressed through 32-bit buffer descriptors
-  CHECK(p.bchunk_alloc * p.d * 2 <= kMaxView);
+  CHECK(p.list_rows * p.d * 2 <= kMaxView);
   CHECK(p.vslab * p.d * 2 <= kMaxView);
   CHECK(p.bchunk_alloc * p.vslab * 2 <= kMaxView);
 }
@@ -65,7 +70,7 @@ void check_shared(const fkl::Plan& p) {
 void check_forward(const fkl::Plan& p, size_t ws_bytes) {
   check_shared(p);
   CHECK(p.fwd_bytes <= ws_bytes);
-  const size_t tp_end = p.off_tp + static_cast<size_t>(p.bchunk_alloc) * (p.K + 1) * 4;
+  const size_t tp_end = p.off_tp + static_cast<size_t>(p.list_rows) * (p.K + 1) * 4;
   CHECK(p.off_partial >= tp_end && al256(p.off_partial));
   const int64_t rbs_max = p.chunk_alloc / fkl::kTile;
   CHECK(p.off_blocksum >=
@@ -87,7 +92,7 @@ void check_forward(const fkl::Plan& p, size_t ws_bytes) {
 void check_backward(const fkl::Plan& p, size_t ws_bytes) {
   check_shared(p);
   CHECK(p.bwd_bytes <= ws_bytes);
-  const size_t tp_end = p.off_tp + static_cast<size_t>(p.bchunk_alloc) * (p.K + 1) * 4;
+  const size_t tp_end = p.off_tp + static_cast<size_t>(p.list_rows) * (p.K + 1) * 4;
   CHECK(p.off_G >= tp_end && al256(p.off_G));
   CHECK(p.off_ghp >= p.off_G + static_cast<size_t>(p.bchunk_alloc) * p.vslab * 2 && al256(p.off_ghp));
   CHECK(p.off_gh32 >= p.off_ghp + static_cast<size_t>(p.ghp_rows) * p.d * 4 && al256(p.off_gh32));

@@ -230,9 +230,10 @@ def test_operand_views_stay_under_2_gib():
 
 
 def test_backward_pass_rows_follow_gradient_block():
-    """With the default slab both directions take passes of max(chunk, min(N, 8192))
-    rows, so a small chunk does not shrink the passes or grow the workspace; an
-    explicit slab keeps chunk-row passes."""
+    """With the default slab the forward takes passes of max(chunk, min(N, 16384))
+    rows and the backward of max(chunk, min(N, 8192)), so a small chunk does not
+    shrink the passes or grow the workspace; an explicit slab keeps chunk-row
+    passes."""
     f1024, b1024 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=1024)
     f4096, b4096 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=4096)
     f8192, b8192 = fkl.workspace_size(65536, 3072, 128256, 100, 1.0, chunk=8192)
@@ -252,11 +253,18 @@ def test_backward_pass_rows_follow_gradient_block():
 
 
 def test_plan_info_reports_the_passes_that_run():
-    # default slab: passes of at least min(N, 8192) rows, slab sized for a 64 Mi-element block
+    # default slab: forward passes of at least min(N, 16384) rows, backward
+    # passes of at least min(N, 8192), slab sized for a 64 Mi-element block
     p = fkl.plan_info(32768, 2880, 201088, 100, 1.0, chunk=4096)
-    assert p["fwd_rows"] == p["bwd_rows"] == 8192
+    assert p["fwd_rows"] == 16384 and p["bwd_rows"] == 8192
     assert p["vslab"] == 8192 and p["slabs"] == 25
-    assert p["fwd_passes"] == p["bwd_passes"] == 4
+    assert p["fwd_passes"] == 2 and p["bwd_passes"] == 4
+    # N between the two floors: one forward pass, backward passes of 8192
+    r = fkl.plan_info(12000, 2880, 201088, 100, 1.0)
+    assert (r["fwd_rows"], r["fwd_passes"], r["bwd_rows"], r["bwd_passes"]) == (12000, 1, 8192, 2)
+    # at the largest hidden size the floors stay under the 2 GiB operand view
+    w = fkl.plan_info(65536, 65536, 1000, 4, 1.0)
+    assert w["fwd_rows"] * 65536 * 2 < (1 << 31) and w["bwd_rows"] == 8192
     assert (p["fwd_bytes"], p["bwd_bytes"]) == fkl.workspace_size(32768, 2880, 201088, 100, 1.0, chunk=4096)
     # an explicit slab keeps the caller's chunk in both directions
     q = fkl.plan_info(8192, 3072, 128256, 100, 1.0, chunk=1024, vslab=65536)
