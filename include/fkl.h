@@ -220,14 +220,18 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
  * that forbid allocation): the same computation, kernels and results as
  * fkl_forward, with the workspace taken from a static device array of the
  * library, FKL_STATIC_SCRATCH_BYTES (32 MiB) on every GPU the library runs
- * on, held until the process ends. Allocates nothing.
+ * on, held until the process ends. Allocates nothing. With vslab = 0, where
+ * fkl_forward's passes of at least min(N, 16384) rows would need more than
+ * the scratch (fwd_bytes of fkl_workspace_size), passes of at least
+ * min(N, 8192) rows are taken instead; the results then differ from
+ * fkl_forward's only in fp32 summation order.
  *
  * Arguments and outputs as fkl_forward. The stream must belong to the
  * current device (the scratch used is that device's copy).
- * Errors: as fkl_forward; FKL_EWORKSPACE when the shape's forward workspace
- * (fkl_workspace_size's fwd_bytes) exceeds FKL_STATIC_SCRATCH_BYTES (fewer
- * rows per pass, chunk with an explicit vslab, lower it); FKL_EINVAL when the
- * stream belongs to another device.
+ * Errors: as fkl_forward; FKL_EWORKSPACE when the forward workspace of the
+ * passes taken still exceeds FKL_STATIC_SCRATCH_BYTES (fewer rows per pass,
+ * chunk with an explicit vslab, lower it); FKL_EINVAL when the stream
+ * belongs to another device.
  * Concurrency: all calls on one GPU share its scratch, so calls that overlap
  * on one GPU (several streams or threads) race and must be serialised by the
  * caller. Nothing in the scratch needs to start at zero: every call writes

@@ -340,7 +340,9 @@ def forward_static(h, W, t_idx, t_logit, T: float = 1.0, mask=None, chunk: int =
                    label=None, label_weight: float = 0.0):
     """fkl_forward_static: the forward with the library's static device scratch
     instead of a workspace (no allocation inside the library; pass the output
-    tensors to avoid allocating them here too). Same results as forward()."""
+    tensors to avoid allocating them here too). Same results as forward(), up
+    to fp32 summation order where the default slab's forward passes do not fit
+    the scratch and the library takes 8192-row passes instead."""
     torch = _torch()
     N, d, V, K = _inputs(h, W, t_idx, t_logit, mask)
     terms = _terms(N, V, row_weight, label, label_weight, h.device)

@@ -82,7 +82,7 @@ int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d) {
   return static_cast<int>(sp);
 }
 
-fkl_status make_plan(const fkl_shape* s, Plan* p) {
+fkl_status make_plan(const fkl_shape* s, Plan* p, int64_t fwd_floor_rows) {
   if (!s) return fail(FKL_EINVAL, "shape is NULL");
   if (s->N < 0) return fail(FKL_EINVAL, "N must be >= 0");
   if (s->N > (int64_t(1) << 31) - 1) return fail(FKL_EUNSUPPORTED, "N must be < 2^31");
@@ -108,7 +108,7 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   // Passes: no [rows x V] block is ever formed, so a forward pass costs only
   // its teacher lists and split statistics (a few MiB at 8192 rows) and a
   // backward pass its gradient block (rows x vslab). With the default slab
-  // the forward takes passes of at least min(N, kFwdPassRows) rows and the
+  // the forward takes passes of at least min(N, fwd_floor_rows) rows and the
   // backward of at least min(N, kPassRows) (more rows share each W stream; a
   // narrower slab keeps the gradient block's size); an explicit vslab keeps
   // the caller's chunk in both directions.
@@ -119,7 +119,7 @@ fkl_status make_plan(const fkl_shape* s, Plan* p) {
   const int64_t view_rows = kMaxView / (2 * s->d) / kTile * kTile;
   int64_t bchunk = chunk;
   if (s->vslab == 0 && s->N > 0) {
-    chunk = std::max(chunk, std::min<int64_t>({s->N, kFwdPassRows, view_rows}));
+    chunk = std::max(chunk, std::min<int64_t>({s->N, fwd_floor_rows, view_rows}));
     bchunk = std::max(bchunk, std::min<int64_t>({s->N, kPassRows, view_rows}));
   }
   p->chunk = chunk;
@@ -443,6 +443,13 @@ fkl_status fkl_forward_static(const fkl_shape* shape, const void* h, const void*
   fkl::Plan p;
   fkl_status st = fkl::make_plan(shape, &p);
   if (st != FKL_OK) return st;
+  // A forward pass's rows do not change its results: where the default
+  // slab's longer forward passes need more than the scratch, take passes of
+  // the backward's rows (smaller teacher lists).
+  if (p.fwd_bytes > fkl::kStaticScratchBytes && shape->vslab == 0) {
+    fkl::Plan q;
+    if (fkl::make_plan(shape, &q, fkl::kPassRows) == FKL_OK && q.fwd_bytes < p.fwd_bytes) p = q;
+  }
   const float* weight;
   const int32_t* label;
   float label_w;

@@ -75,7 +75,10 @@ constexpr size_t kDebugWordOffset = 192;
 // the launch's average work per CU; 1 when the launch is balanced without.
 int grad_h_splits(int64_t rows, int64_t slab_w, int64_t d);
 
-fkl_status make_plan(const fkl_shape* s, Plan* p);
+// fwd_floor_rows: the forward's pass rows floor with the default slab
+// (kFwdPassRows; the allocation-free forward lowers it to kPassRows when its
+// scratch cannot hold the longer passes' teacher lists).
+fkl_status make_plan(const fkl_shape* s, Plan* p, int64_t fwd_floor_rows = kFwdPassRows);
 
 // Per-call device pointers of the forward pass.
 struct FwdArgs {

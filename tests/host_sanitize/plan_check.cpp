@@ -298,8 +298,17 @@ void drive(const fkl_shape& s) {
   fkl::g_ws_bytes = fb;
   CHECK(fkl_forward(&s, h, W, ti, tl, nullptr, nullptr, out, out, out, ws, fb, nullptr) == FKL_OK);
   // the allocation-free forward: the static scratch, or FKL_EWORKSPACE when the plan needs more
+  // (with the default slab it falls back to the backward's pass rows)
+  size_t static_bytes = fb;
+  if (fb > fkl::kStaticScratchBytes && s.vslab == 0) {
+    fkl::Plan q;
+    CHECK(fkl::make_plan(&s, &q, fkl::kPassRows) == FKL_OK);
+    CHECK(q.fwd_bytes <= fb && q.bchunk == p.bchunk);
+    check_shared(q);
+    static_bytes = q.fwd_bytes;
+  }
   const fkl_status sst = fkl_forward_static(&s, h, W, ti, tl, nullptr, nullptr, out, out, out, nullptr);
-  CHECK(sst == (fb <= fkl::kStaticScratchBytes ? FKL_OK : FKL_EWORKSPACE));
+  CHECK(sst == (static_bytes <= fkl::kStaticScratchBytes ? FKL_OK : FKL_EWORKSPACE));
   CHECK(fkl_forward_static(&s, h, W, ti, tl, nullptr, nullptr, nullptr, out, out, nullptr) == FKL_EINVAL);
   fkl::g_ws_bytes = bb;
   CHECK(fkl_backward(&s, h, W, ti, tl, nullptr, nullptr, out, nullptr, out, out, ws, bb, nullptr) == FKL_OK);
@@ -343,7 +352,7 @@ int main() {
   const std::vector<int64_t> ds = {8, 16, 64, 136, 264, 2880, 3072, 4096, 65536, 65544, 0, 7, 12};
   const std::vector<int64_t> Vs = {1, 2, 100, 255, 256, 257, 4096, 5000, 128256, 201088, 1000000,
                                    (int64_t(1) << 31) - 1025, (int64_t(1) << 31) - 1024, 0};
-  const std::vector<int64_t> Ks = {1, 7, 16, 100, 128, 129, 700, 1024, 1025, 0};
+  const std::vector<int64_t> Ks = {1, 7, 16, 100, 128, 129, 300, 700, 1024, 1025, 0};
   const std::vector<int64_t> chunks = {0, 1, 64, 100, 256, 1000, 1024, 4096, 8192, 65536,
                                        (int64_t(1) << 31) - 1, -5};
   const std::vector<int64_t> slabs = {0, 1, 256, 768, 1024, 2048, 8192, 65536, 1 << 20, (int64_t(1) << 31) - 1,
@@ -374,6 +383,21 @@ int main() {
     fkl_topk_shape t{pick(Ns), pick(ds), pick(Vs), static_cast<int32_t>(pick(Ks)),
                      static_cast<int32_t>(pick(chunks)), static_cast<uint32_t>(next() % 5)};
     drive_topk(t);
+  }
+  // the allocation-free forward's fallback: 16384-row teacher lists of K = 300
+  // exceed its scratch, 8192-row ones fit
+  {
+    const fkl_shape s{16384, 64, 5000, 300, 1.0f, 0, 0, 0};
+    size_t fb = 0;
+    CHECK(fkl_workspace_size(&s, &fb, nullptr) == FKL_OK && fb > fkl::kStaticScratchBytes);
+    const long before = g_launches;
+    drive(s);
+    float* out = static_cast<float*>(fake(0x500000));
+    CHECK(fkl_forward_static(&s, fake(0x100000), fake(0x200000), static_cast<const int32_t*>(fake(0x300000)),
+                             static_cast<const float*>(fake(0x400000)), nullptr, nullptr, out, out, nullptr,
+                             nullptr) == FKL_OK);
+    CHECK(g_launches > before);
+    ++shapes;
   }
   // NULL shapes and pointers
   CHECK(fkl_workspace_size(nullptr, nullptr, nullptr) == FKL_EINVAL);

@@ -62,7 +62,8 @@ def test_static_forward_matches_workspace_forward_twice_then_smaller():
 
 def test_static_forward_at_the_headline_shape():
     """N=32768, d=2880, V=201088, K=100 in the bench's launch configuration
-    (8192-row passes, 8.6 MiB of scratch): bit for bit the workspace forward."""
+    (16384-row forward passes, 15.2 MiB of scratch): bit for bit the workspace
+    forward."""
     from workloads.device import make_device_workload
     dev = _dev()
     wl = make_device_workload("gptoss20b", dev)
@@ -74,3 +75,26 @@ def test_static_forward_at_the_headline_shape():
     torch.cuda.synchronize()
     assert torch.equal(loss_s, loss_w) and torch.equal(lse_s, lse_w) and torch.equal(kl_s, kl_w)
     assert torch.isfinite(lse_s).all().item()
+
+
+def test_static_forward_falls_back_to_shorter_passes():
+    """K = 300 over 16384 rows: the default 16384-row forward pass needs more
+    than the 32 MiB scratch for its teacher lists, so the static forward takes
+    8192-row passes. It must equal fkl_forward run with 8192-row passes (an
+    explicit slab keeps the caller's chunk) bit for bit, and the oracle to the
+    parity bar."""
+    dev = _dev()
+    wl = make_workload("tiny", 5, N=16384, d=64, V=5000, K=300, mask="random25")
+    fb, _ = fkl.workspace_size(wl.N, wl.d, wl.V, wl.K, 1.0)
+    assert fb > fkl.STATIC_SCRATCH_BYTES
+    print(f"[no-alloc] fallback N={wl.N} K={wl.K}: default forward workspace {fb} bytes", flush=True)
+    h, W, ti, tl, m = _upload(wl, dev)
+    loss_s, lse_s, kl_s = _outputs(wl.N, dev)
+    fkl.forward_static(h, W, ti, tl, T=1.0, mask=m, loss=loss_s, row_lse=lse_s, row_kl=kl_s)
+    loss_w, lse_w, kl_w = fkl.forward(h, W, ti, tl, T=1.0, mask=m, chunk=8192, vslab=1024, return_row_kl=True)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_s, loss_w) and torch.equal(lse_s, lse_w) and torch.equal(kl_s, kl_w)
+    r_loss, r_lse, r_kl = oracle.forward(wl.h(), wl.W(), wl.t_idx, wl.t_logit, 1.0, wl.mask)
+    assert abs(loss_s.item() - r_loss) <= 1e-3 * abs(r_loss)
+    assert float(np.abs(lse_s.cpu().numpy() - r_lse).max()) <= 1e-3
+    assert float(np.abs(kl_s.cpu().numpy() - r_kl).max()) <= 1e-3 * max(1.0, float(np.abs(r_kl).max()))
