@@ -106,7 +106,7 @@ fkl_status make_plan(const fkl_shape* s, Plan* p, int64_t fwd_floor_rows) {
   int64_t chunk = s->chunk ? s->chunk : kDefaultChunk;
   if (s->N > 0 && chunk > s->N) chunk = s->N;
   // Passes: no [rows x V] block is ever formed, so a forward pass costs only
-  // its teacher lists and split statistics (a few MiB at 8192 rows) and a
+  // its teacher lists and split statistics (15 MiB at 16384 rows, K = 100) and a
   // backward pass its gradient block (rows x vslab). With the default slab
   // the forward takes passes of at least min(N, fwd_floor_rows) rows and the
   // backward of at least min(N, kPassRows) (more rows share each W stream; a

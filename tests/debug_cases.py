@@ -111,8 +111,8 @@ def case_topk(fkl, torch, dev):
 
 
 def case_fullsize(fkl, torch, dev):
-    """The headline shape (four 8192-row passes, 25 slabs of 8192 columns,
-    the full gradient block) and the builder's default 16384-row pass at the
+    """The headline shape (two 16384-row forward passes, four 8192-row
+    backward passes over 25 slabs of 8192 columns, the full gradient block) and the builder's default 16384-row pass at the
     large head. Summaries of every output (sums and largest magnitudes in
     fp64), and the builder's indices exactly."""
     from workloads.device import make_device_workload, perturbed_head

@@ -292,8 +292,8 @@ def test_validate_terms_argument_errors_before_any_device_work():
 
 def test_static_forward_refuses_shapes_beyond_its_scratch():
     """fkl_forward_static checks the shape's forward workspace against the
-    static scratch before any device call: 8192-row passes of K = 1024 teacher
-    entries need about 67 MB, more than the 32 MiB scratch."""
+    static scratch before any device call: even its shorter 8192-row passes of
+    K = 1024 teacher entries need about 67 MB, more than the 32 MiB scratch."""
     L = fkl.lib()
     s = fkl.make_shape(32768, 2880, 201088, 1024)
     fb, _ = fkl.workspace_size(32768, 2880, 201088, 1024)
