@@ -272,8 +272,8 @@ def test_chunk_invariance():
     dev = _dev()
     wl = make_workload("tiny", seed_offset=5, mask="random25")
     h, W, ti, tl, m = _upload(wl, dev)
-    # with vslab = 0 the backward takes passes of max(chunk, min(N, 8192))
-    # rows; an explicit vslab keeps chunk-row backward passes
+    # with vslab = 0 the passes are at least min(N, 16384) rows forward and
+    # min(N, 8192) backward; an explicit vslab keeps chunk-row passes
     outs = [_run_gpu(h, W, ti, tl, m, 1.0, chunk=c) for c in (64, 100, 256)]
     outs += [_run_gpu(h, W, ti, tl, m, 1.0, chunk=c, vslab=1024) for c in (64, 100)]
     for o in outs[1:]:
@@ -309,6 +309,34 @@ def test_chunk_invariance_explicit_slab_8192_rows():
         assert np.abs(o[1] - r_lse).max() <= LSE_ATOL
         assert _rel_max(o[3], r_gh) <= GRAD_TOL
         assert _rel_max(o[4], r_gW) <= GRAD_TOL
+
+
+def test_forward_and_backward_pass_rows_differ():
+    """12000 rows with the default slab: the forward runs one pass of 12000
+    rows (its floor is 16384), the backward two passes of 8192 and 3808 rows
+    (a ragged last row block in both). Against the oracle at the parity bar,
+    and against the same call with 1024-row passes in both directions."""
+    wl = make_workload("tiny", seed_offset=8, N=12000, d=136, V=3000, K=16, mask="random25")
+    dev = _dev()
+    p = fkl.plan_info(wl.N, wl.d, wl.V, wl.K, 1.0)
+    assert (p["fwd_rows"], p["fwd_passes"], p["bwd_rows"], p["bwd_passes"]) == (12000, 1, 8192, 2)
+    print(f"[pass-rows] N={wl.N}: forward {p['fwd_passes']} x {p['fwd_rows']}, "
+          f"backward {p['bwd_passes']} x {p['bwd_rows']}", flush=True)
+    h, W, ti, tl, m = _upload(wl, dev)
+    got = _run_gpu(h, W, ti, tl, m, 1.0)
+    alt = _run_gpu(h, W, ti, tl, m, 1.0, chunk=1024, vslab=1024)
+    assert abs(got[0] - alt[0]) <= 1e-6 * abs(alt[0])
+    assert np.abs(got[1] - alt[1]).max() <= 1e-5
+    assert _rel_max(got[3], alt[3]) <= 1e-3
+    assert _rel_max(got[4], alt[4]) <= 1e-3
+    r_loss, r_lse, _ = oracle.forward(wl.h(), wl.W(), wl.t_idx, wl.t_logit, 1.0, wl.mask)
+    r_gh, r_gW = oracle.backward(wl.h(), wl.W(), wl.t_idx, wl.t_logit, 1.0, wl.mask)
+    assert abs(got[0] - r_loss) <= LOSS_RTOL * abs(r_loss)
+    assert np.abs(got[1] - r_lse).max() <= LSE_ATOL
+    assert _rel_max(got[3], r_gh) <= GRAD_TOL
+    assert _rel_max(got[4], r_gW) <= GRAD_TOL
+    # masked rows: exactly zero gradient rows
+    assert np.all(got[3][~wl.mask.astype(bool)] == 0.0)
 
 
 def test_bitwise_determinism():
