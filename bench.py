@@ -510,9 +510,16 @@ def main() -> int:
         fkl.backward(wl.h, wl.W, wl.t_idx, wl.t_logit, row_lse, T=wl.T, mask=wl.mask, chunk=wl.chunk,
                      workspace=ws, grad_h=grad_h, grad_W=grad_W)
 
+    def held_outside_torch() -> int:
+        # device memory neither free nor in torch's pool (hipMemGetInfo)
+        free, total = torch.cuda.mem_get_info(dev)
+        return total - free - torch.cuda.memory_reserved(dev)
+
+    outside0 = held_outside_torch()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    outside1 = held_outside_torch()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
     trace = not args.no_trace
     start = torch.cuda.Event(enable_timing=True)
@@ -532,6 +539,7 @@ def main() -> int:
         marks[i][2].record()
     stop.record()
     torch.cuda.synchronize()
+    outside2 = held_outside_torch()
     fwd_ms = sorted(m[0].elapsed_time(m[1]) for m in marks)
     bwd_ms = sorted(m[1].elapsed_time(m[2]) for m in marks)
     step_ms = sorted(m[0].elapsed_time(m[2]) for m in marks)
@@ -623,6 +631,10 @@ def main() -> int:
                      "tflops": round(6.0 * wl.N * wl.d * wl.V / (bwd_ms[len(bwd_ms) // 2] / 1e3) / 1e12, 1)},
         "peak_gib": round(peak / 2**30, 3),
         "extra_gib": round((peak - in_out_bytes) / 2**30, 3),
+        # hipMemGetInfo cross-check: device memory taken outside torch's pool
+        # by the warmup steps (the library's code objects and static scratch,
+        # loaded on first use) and by the timed steps (0: no allocation per call)
+        "device_bytes_outside_torch": {"warmup": outside1 - outside0, "timed_steps": outside2 - outside1},
         "inputs_outputs_gib": round(in_out_bytes / 2**30, 3),
         "loss": float(loss.item()),
         "wall_s_timed": round(wall, 3),
