@@ -494,24 +494,104 @@ __device__ __forceinline__ void wave_append(bool take, uint64_t key, uint64_t* l
   if (take) list[base + below] = key;
 }
 
+// The threshold's two digits: 12 bits each fix the top 24 bits of the
+// logit's ordered bits. The first digit (sign, exponent and three mantissa
+// bits) spreads the sampled keys over enough bins that the histogram's LDS
+// atomics rarely meet on one address.
+constexpr int kThreshDigit = 12;
+constexpr int kThreshBins = 1 << kThreshDigit;
+constexpr int kThreshLoads = kMaxSample / (4 * kSelThreads);  // 16-byte sample loads per thread
+static_assert(kThreshDigit * 2 == kThreshBits, "two digits fix the threshold's bits");
+static_assert(kThreshBins % (4 * kSelThreads) == 0, "each thread clears whole 16-byte groups of bins");
+
+struct BinPick {
+  uint32_t bin;    // the digit's bin holding the need-th largest key
+  uint32_t above;  // keys in higher bins
+  uint32_t count;  // keys in the bin
+};
+
+// One digit of the threshold over the workgroup's sampled keys (each thread's
+// in registers: ob[q][e] where live[q]): a histogram of bits [shift, shift +
+// 12) among the keys whose bits from hi_shift up equal hi (every key when
+// !match), then the bin holding the need-th largest of them. need >= 1 and
+// at most the number of keys counted.
+template <int Q>
+__device__ BinPick thresh_digit(const uint32_t (&ob)[Q][4], const bool (&live)[Q], int shift, bool match,
+                                int hi_shift, uint32_t hi, uint32_t need, uint32_t* hist, uint32_t* wave_tot,
+                                uint32_t* s_vals) {
+  const int tid = threadIdx.x;
+  for (int b = tid * 4; b < kThreshBins; b += kSelThreads * 4) *reinterpret_cast<u32x4*>(hist + b) = u32x4{0, 0, 0, 0};
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (live[q] && (!match || (ob[q][e] >> hi_shift) == hi))
+        atomicAdd(&hist[(ob[q][e] >> shift) & (kThreshBins - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  // thread t owns bins [16 t, 16 t + 16); keys in later threads' bins are larger
+  constexpr int kPer = kThreshBins / kSelThreads;
+  const int b0 = tid * kPer;
+  uint32_t c[kPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(hist + b0 + 4 * v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[4 * v + e] = x[e];
+      mine += x[e];
+    }
+  }
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  uint32_t incl = mine;  // this thread's keys and those of the later lanes of its wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = static_cast<uint32_t>(__shfl_down(static_cast<int>(incl), o, 64));
+    if (lane + o < 64) incl += y;
+  }
+  if (lane == 0) wave_tot[wv] = incl;
+  __syncthreads();
+  uint32_t above = incl - mine;
+  for (int w2 = wv + 1; w2 < kSelThreads / 64; ++w2) above += wave_tot[w2];
+  if (above < need && above + mine >= need) {
+#pragma unroll
+    for (int b = kPer - 1; b >= 0; --b) {
+      if (above + c[b] >= need) {
+        s_vals[0] = static_cast<uint32_t>(b0 + b);
+        s_vals[1] = above;
+        s_vals[2] = c[b];
+        break;
+      }
+      above += c[b];
+    }
+  }
+  __syncthreads();
+  const BinPick r{s_vals[0], s_vals[1], s_vals[2]};
+  __syncthreads();  // every thread has read s_vals and wave_tot
+  return r;
+}
+
 // One workgroup per row of the pass: thr[row] = a key at or below the row's
-// j-th largest sampled key, exactly it unless the bin of 24-bit prefixes at it
-// holds more keys (then the bin's lower bound); 0 when j = 0 (every key is a
-// candidate). Any threshold gives the exact top K as long as at least K of the
-// row's keys reach it and none is dropped (the pick checks both), so aiming
-// at the j-th key need not be exact. The row's sampled keys at or above the
-// threshold go to its extra candidate slice (xcap slots; the sweep skips the
-// sampled tiles), their number to xcnt[row]. Workgroup 0 also clears the
-// pass's redo flag (the previous pass's redo has read it: launches are in
-// stream order).
+// j-th largest sampled key: the lower bound of the bin of 24-bit prefixes
+// that holds it (of its 12-bit bin when that bin is taken whole); 0 when
+// j = 0 (every key is a candidate). Any threshold gives the exact top K as
+// long as at least K of the row's keys reach it and none is dropped (the pick
+// checks both), so aiming at the j-th key need not be exact. The row's
+// sampled keys at or above the threshold go to its extra candidate slice
+// (xcap slots; the sweep skips the sampled tiles), their number to xcnt[row].
+// Workgroup 0 also clears the pass's redo flag (the previous pass's redo has
+// read it: launches are in stream order).
 __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __restrict__ sample, int S, int stride,
                                                              int j, uint64_t* __restrict__ thr,
                                                              uint32_t* __restrict__ xcnt,
                                                              uint64_t* __restrict__ xcand, int xcap,
                                                              uint32_t* flag, DebugCheck dbg) {
   // dbg spans: 0 the sample's logits, 1 extra slices, 2 thresholds, 3 extra-slice counts
-  __shared__ uint32_t sv[kMaxSample];
-  __shared__ uint32_t hist[1 << kFusedDigitBits];
+  __shared__ __align__(16) uint32_t hist[kThreshBins];
   __shared__ uint32_t wave_tot[kSelThreads / 64];
   __shared__ uint32_t s_vals[3];
   __shared__ uint32_t s_hits;
@@ -521,39 +601,52 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
   if (tid == 0) s_hits = 0;
   const float* zr = sample + static_cast<int64_t>(row) * S;
   if (!dcheck_range(dbg, 0, kDbgTopkWork, zr, static_cast<uint64_t>(S) * 4)) return;
-  for (int i = tid * 4; i < S; i += kSelThreads * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(zr + i);
+  // sampled logit i = 4 f + e, f = tid + 256 q: the ordered bits in registers
+  uint32_t ob[kThreshLoads][4];
+  bool live[kThreshLoads];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[i + e] = ordered_bits(v[e]);
+  for (int q = 0; q < kThreshLoads; ++q) {
+    const int f = tid + kSelThreads * q;
+    live[q] = 4 * f < S;
+    const f32x4 v = live[q] ? *reinterpret_cast<const f32x4*>(zr + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ob[q][e] = ordered_bits(v[e]);
   }
-  __syncthreads();
-  const uint32_t* svp = sv;
-  auto key_at = [svp, stride](int i) {
-    return (static_cast<uint64_t>(svp[i]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - sample_col(i, stride));
-  };
-  uint64_t t = 0;
+  uint32_t t32 = 0;
   if (j > 0) {
-    SelectState st{0, 0, static_cast<uint32_t>(j)};
-    select_rest<kFusedDigitBits>(key_at, S, st, hist, wave_tot, s_vals, kThreshBits);
-    t = st.pbits >= 64 ? st.prefix : st.prefix << (64 - st.pbits);
+    const BinPick d1 = thresh_digit(ob, live, 32 - kThreshDigit, false, 32, 0u, static_cast<uint32_t>(j), hist,
+                                    wave_tot, s_vals);
+    t32 = d1.bin << (32 - kThreshDigit);
+    const uint32_t need = static_cast<uint32_t>(j) - d1.above;
+    if (d1.count != need) {
+      const BinPick d2 = thresh_digit(ob, live, 32 - 2 * kThreshDigit, true, 32 - kThreshDigit, d1.bin, need,
+                                      hist, wave_tot, s_vals);
+      t32 |= d2.bin << (32 - 2 * kThreshDigit);
+    }
   }
+  const uint64_t t = static_cast<uint64_t>(t32) << 32;
   // the keys at or above the threshold go straight to the row's extra slice
   // (in no particular order; the first xcap of them), counted in s_hits
   uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
-  for (int i0 = 0; i0 < S; i0 += kSelThreads) {
-    const int i = i0 + tid;
-    const uint64_t key = i < S ? key_at(i) : 0;
-    const bool take = i < S && key >= t;
-    const uint64_t m = __ballot(take);
-    if (m == 0) continue;
-    const int lane = tid & 63;
-    const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(&s_hits, static_cast<uint32_t>(__popcll(m)));
-    base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
-    if (take && base + below < static_cast<uint32_t>(xcap)) dstore(dbg, 1, kDbgTopkWork, xrow + base + below, key);
+  const int lane = tid & 63;
+#pragma unroll
+  for (int q = 0; q < kThreshLoads; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (tid + kSelThreads * q) + e;
+      const bool take = live[q] && ob[q][e] >= t32;
+      const uint64_t m = __ballot(take);
+      if (m == 0) continue;
+      const uint64_t key =
+          (static_cast<uint64_t>(ob[q][e]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - sample_col(i, stride));
+      const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      uint32_t base = 0;
+      if (lane == leader) base = atomicAdd(&s_hits, static_cast<uint32_t>(__popcll(m)));
+      base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
+      if (take && base + below < static_cast<uint32_t>(xcap)) dstore(dbg, 1, kDbgTopkWork, xrow + base + below, key);
+    }
   }
   __syncthreads();
   const uint32_t nh = s_hits;
@@ -662,11 +755,16 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
 // redo flag is set and nothing is written.
 constexpr int kMaxSlices = 2 * kTargetBlocks;
 constexpr int kPickBatch = 6;  // slot loads issued before any is used
-// candidates gathered into LDS (more are selected in place): room for the
-// usual count (the 1024 targeted for K <= 128) with a small workgroup
-// footprint, so that four rows' workgroups share a CU
-constexpr int kPickCand = 3072;
+// Two instantiations differ only in LDS room: CandCap candidates gathered
+// into LDS (a row with more is selected in place, over its slots) and KeysCap
+// output keys (at least Kp). For K <= 128 about 1024 candidates are targeted:
+// 1536 slots and 128 keys take 16 KiB, so that eight rows' workgroups share a
+// CU; larger K takes 3072 and 1024 (36 KiB, four per CU).
+constexpr int kPickCandSmall = 1536;
+constexpr int kPickKeysSmall = 128;
+constexpr int kPickCandLarge = 3072;
 
+template <int CandCap, int KeysCap>
 __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __restrict__ xcnt,
                                                            const uint64_t* __restrict__ xcand, int xcap,
                                                            const uint32_t* __restrict__ cnt,
@@ -676,8 +774,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
                                                            float* __restrict__ t_logit, DebugCheck dbg) {
   // dbg spans: 0 extra-slice counts, 1 extra slices, 2 slice counts, 3 candidate slices, 4 t_idx, 5 t_logit
   __shared__ uint32_t hist[1 << kFusedDigitBits];
-  __shared__ uint64_t keys[kMaxK];
-  __shared__ uint64_t cand[kPickCand];
+  static_assert(KeysCap <= kMaxK && (KeysCap <= 128 || KeysCap == kMaxK), "the block sort needs room for Kp");
+  __shared__ uint64_t keys[KeysCap];
+  __shared__ uint64_t cand[CandCap];
   __shared__ uint32_t s_cnt[kMaxSlices];
   __shared__ uint32_t wave_tot[kSelThreads / 64];
   __shared__ uint64_t s_and[kSelThreads / 64], s_or[kSelThreads / 64];
@@ -723,7 +822,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   // every used slot of every slice, in slot order; unused slots read as 0
   const int list = slices * slice_cap;
   SelectState st{0, 0, static_cast<uint32_t>(K)};
-  if (n <= static_cast<uint32_t>(kPickCand)) {
+  if (n <= static_cast<uint32_t>(CandCap)) {
     for (int i0 = 0; i0 < list; i0 += kSelThreads * kPickBatch) {
       uint64_t k[kPickBatch];
       bool take[kPickBatch];
@@ -943,8 +1042,10 @@ hipError_t launch_topk(const TopkPlan& p, const uint16_t* h, const uint16_t* W, 
     }
     {
       TraceScope ts(st, "topk_pick", 0.0, 4.0 * rows * S + 8.0 * rows * p.K);
-      hipLaunchKernelGGL(k_topk_pick, dim3(rows), dim3(kSelThreads), 0, st, xcnt, xcand, p.xcap, cnt, cand,
-                         2 * splits, slice_cap, p.K, Kp, c0, flag, t_idx, t_logit,
+      auto* pick = Kp <= kPickKeysSmall ? k_topk_pick<kPickCandSmall, kPickKeysSmall>
+                                        : k_topk_pick<kPickCandLarge, kMaxK>;
+      hipLaunchKernelGGL(pick, dim3(rows), dim3(kSelThreads), 0, st, xcnt, xcand, p.xcap, cnt, cand, 2 * splits,
+                         slice_cap, p.K, Kp, c0, flag, t_idx, t_logit,
                          make_debug_check(sp.word, {xcnt_span, xcand_span, cnt_span, cand_span, sp.t_idx, sp.t_logit}));
     }
     // redo of the pass by the materialised route, only if a row flagged it
