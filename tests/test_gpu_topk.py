@@ -284,6 +284,37 @@ def test_topk_feeds_the_loss():
     assert np.isfinite(loss.item()) and loss.item() >= -1e-5
 
 
+def test_topk_pick_selects_in_place_past_its_lds_buffer():
+    """K = 100 over the large-head vocabulary, with the sampled tiles' logits
+    0.3 lower than the rest: the threshold (the 33rd largest of the 4096
+    sampled keys, aimed at 1024 candidates) lets about 2200 keys of each row
+    through, more than the 1536 the pick holds in LDS for K <= 128 but well
+    within the candidate slices. Those rows are selected in place over the
+    slices; the output must equal the materialised route's bit for bit."""
+    dev = _dev()
+    N, d, V, K = 512, 64, 128256, 100
+    rng = np.random.default_rng(91)
+    cols = _tile_pattern(V, stride=32)  # the fused route's 16 sampled tiles
+    hf = rng.standard_normal((N, d)).astype(np.float32)
+    hf[:, 0] = 1.0
+    Wf = (rng.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32)
+    Wf[:, 0] = np.where(cols, -0.3, 0.0)
+    h, hb = _to_dev_bf16(hf, dev)
+    W, Wb = _to_dev_bf16(Wf, dev)
+    # precondition, from the fp32 logits of the bf16 inputs: most rows pass
+    # more than 1536 keys at the 33rd largest sampled logit
+    z = hb @ Wb.T
+    kth = -np.sort(-z[:, cols], axis=1)[:, 32]
+    n_pass = (z >= kth[:, None]).sum(axis=1)
+    print(f"[topk-pick-in-place] N={N} V={V} K={K}: candidates per row {int(n_pass.min())}..{int(n_pass.max())}",
+          flush=True)
+    assert np.mean(n_pass > 1536) > 0.9
+    a_i, a_l = fkl.topk(h, W, K)
+    b_i, b_l = fkl.topk(h, W, K, materialize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_i, b_i) and torch.equal(a_l, b_l)
+
+
 def test_topk_fullsize_sampled_rows():
     """The large-head workload's shape (N=16384, d=4096, V=128256, K=100) with a
     perturbed teacher head: sampled rows against the oracle."""
