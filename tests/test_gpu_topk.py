@@ -356,3 +356,45 @@ def test_topk_fused_redo_spans_several_blocks_at_the_large_head():
     high = np.nonzero(cols)[0]
     assert (a_i.cpu().numpy() == high[:K][None, :]).all()
     assert (a_l.cpu().numpy() == 1.0).all()
+
+
+def _stress_case(i):
+    """Shape and inputs of random builder case i: one of five logit patterns
+    (Gaussian, integer with many ties, a column offset on a random half of
+    the vocabulary, heavy-tailed, a few huge logits per row)."""
+    rng = np.random.default_rng(60000 + i)
+    V = int(rng.choice([int(rng.integers(1, 2000)), int(rng.integers(2000, 40000)), int(rng.integers(40000, 140000))]))
+    K = int(min(V, rng.choice([1, int(rng.integers(2, 129)), int(rng.integers(129, 1025))])))
+    d = 8 * int(rng.integers(1, 24))
+    N = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 2000))]))
+    kind = i % 5
+    h = rng.standard_normal((N, d)).astype(np.float32)
+    W = (rng.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32)
+    if kind == 1:
+        h = rng.integers(-2, 3, (N, d)).astype(np.float32)
+        W = rng.integers(-1, 2, (V, d)).astype(np.float32)
+    elif kind == 2:
+        h[:, 0] = 1.0
+        W[:, 0] = np.where(rng.random(V) < 0.5, -0.4, 0.0)
+    elif kind == 3:
+        W *= rng.standard_cauchy((V, 1)).astype(np.float32).clip(-50, 50)
+    elif kind == 4:
+        W[rng.choice(V, min(V, 3), replace=False)] *= 100.0
+    chunk = int(rng.choice([0, 0, int(rng.integers(1, 600))]))
+    return N, d, V, K, kind, chunk, h, W
+
+
+@pytest.mark.parametrize("i", range(96))
+def test_topk_routes_agree_on_random_patterns(i):
+    """Random shapes and logit patterns: the fused route equals the
+    materialised route bit for bit (each route exact on its own, so any
+    difference is a bug in one of them)."""
+    dev = _dev()
+    N, d, V, K, kind, chunk, h, W = _stress_case(i)
+    print(f"[topk-random] case {i}: N={N} d={d} V={V} K={K} pattern={kind} chunk={chunk}", flush=True)
+    hd, _ = _to_dev_bf16(h, dev)
+    Wd, _ = _to_dev_bf16(W, dev)
+    a_i, a_l = fkl.topk(hd, Wd, K, chunk=chunk)
+    b_i, b_l = fkl.topk(hd, Wd, K, materialize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_i, b_i) and torch.equal(a_l, b_l)
