@@ -217,14 +217,14 @@ fkl_status fkl_forward(const fkl_shape* shape, const void* h, const void* W,
 /*
  * Forward pass without a workspace argument, for callers that cannot
  * allocate (code under HIP graph capture, tight serving loops, harnesses
- * that forbid allocation): the same computation, kernels and results as
- * fkl_forward, with the workspace taken from a static device array of the
- * library, FKL_STATIC_SCRATCH_BYTES (32 MiB) on every GPU the library runs
- * on, held until the process ends. Allocates nothing. With vslab = 0, where
- * fkl_forward's passes of at least min(N, 16384) rows would need more than
- * the scratch (fwd_bytes of fkl_workspace_size), passes of at least
- * min(N, 8192) rows are taken instead; the results then differ from
- * fkl_forward's only in fp32 summation order.
+ * that forbid allocation): the same computation and kernels as fkl_forward,
+ * with the workspace taken from a static device array of the library,
+ * FKL_STATIC_SCRATCH_BYTES (32 MiB) on every GPU the library runs on, held
+ * until the process ends. Allocates nothing. The results are fkl_forward's
+ * bit for bit, except that with vslab = 0, where fkl_forward's passes of at
+ * least min(N, 16384) rows would need more than the scratch (fwd_bytes of
+ * fkl_workspace_size), passes of at least min(N, 8192) rows are taken
+ * instead, which changes only the fp32 summation order.
  *
  * Arguments and outputs as fkl_forward. The stream must belong to the
  * current device (the scratch used is that device's copy).
