@@ -625,6 +625,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_thresh(const float* __rest
     }
   }
   const uint64_t t = static_cast<uint64_t>(t32) << 32;
+  __syncthreads();  // s_hits is zero before any wave counts into it (j = 0 runs no digit)
   // the keys at or above the threshold go straight to the row's extra slice
   // (in no particular order; the first xcap of them), counted in s_hits
   uint64_t* xrow = xcand + static_cast<int64_t>(row) * xcap;
