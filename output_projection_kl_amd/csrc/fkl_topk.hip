@@ -479,21 +479,6 @@ constexpr int kMaxSample = kTopkMaxSampleTiles * kTile;
 constexpr int kFusedDigitBits = 8;   // radix digits of the fused route's selections
 constexpr int kThreshBits = 24;      // the threshold is fixed to its top 24 bits
 
-// Each wave appends the keys its lanes take to list[] (room reserved with one
-// LDS atomic on *count per wave).
-__device__ __forceinline__ void wave_append(bool take, uint64_t key, uint64_t* list, uint32_t* count) {
-  const uint64_t m = __ballot(take);
-  if (m == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(count, static_cast<uint32_t>(__popcll(m)));
-  base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
-  if (take) list[base + below] = key;
-}
-
 // The threshold's two digits: 12 bits each fix the top 24 bits of the
 // logit's ordered bits. The first digit (sign, exponent and three mantissa
 // bits) spreads the sampled keys over enough bins that the histogram's LDS
@@ -755,6 +740,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void k_topk_sweep(TopkSweepParams
 // overflowed (keys were dropped), the row cannot be answered here: the pass's
 // redo flag is set and nothing is written.
 constexpr int kMaxSlices = 2 * kTargetBlocks;
+static_assert(kMaxSlices % kSelThreads == 0, "each thread owns the same number of slice offsets");
 constexpr int kPickBatch = 6;  // slot loads issued before any is used
 // Two instantiations differ only in LDS room: CandCap candidates gathered
 // into LDS (a row with more is selected in place, over its slots) and KeysCap
@@ -779,10 +765,11 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   __shared__ uint64_t keys[KeysCap];
   __shared__ uint64_t cand[CandCap];
   __shared__ uint32_t s_cnt[kMaxSlices];
+  __shared__ uint32_t s_off[kMaxSlices];
   __shared__ uint32_t wave_tot[kSelThreads / 64];
   __shared__ uint64_t s_and[kSelThreads / 64], s_or[kSelThreads / 64];
   __shared__ uint32_t s_vals[3];
-  __shared__ uint32_t s_fill, s_cand, s_over;
+  __shared__ uint32_t s_fill, s_over;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const uint32_t* crow = cnt + static_cast<int64_t>(row) * slices;
@@ -796,7 +783,6 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   for (int i = tid; i < Kp; i += kSelThreads) keys[i] = 0;
   if (tid == 0) {
     s_fill = 0;
-    s_cand = 0;
     s_over = 0;
   }
   uint32_t n_part = 0;
@@ -824,23 +810,67 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_pick(const uint32_t* __res
   const int list = slices * slice_cap;
   SelectState st{0, 0, static_cast<uint32_t>(K)};
   if (n <= static_cast<uint32_t>(CandCap)) {
-    for (int i0 = 0; i0 < list; i0 += kSelThreads * kPickBatch) {
-      uint64_t k[kPickBatch];
-      bool take[kPickBatch];
+    // Candidate t of the sweep's slices goes to cand[t]: an exclusive prefix
+    // sum of the slice counts (thread t owns slices kOffPer t ..) places each
+    // slice's used slots, so only those are loaded, in one batch per thread
+    // for the usual count, and no atomics are needed.
+    constexpr int kOffPer = kMaxSlices / kSelThreads;
+    uint32_t c[kOffPer];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < kOffPer; ++e) {
+      const int sl = tid * kOffPer + e;
+      c[e] = sl < slices ? s_cnt[sl] : 0u;
+      mine += c[e];
+    }
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    uint32_t incl = mine;  // this thread's slices and those of the earlier lanes of its wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), o, 64));
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    uint32_t before = incl - mine;
+    for (int w2 = 0; w2 < wv; ++w2) before += wave_tot[w2];
+#pragma unroll
+    for (int e = 0; e < kOffPer; ++e) {
+      const int sl = tid * kOffPer + e;
+      if (sl < slices) s_off[sl] = before;
+      before += c[e];
+    }
+    __syncthreads();
+    const uint32_t np = n - nx;  // candidates in the sweep's slices
+    for (uint32_t t0 = 0; t0 < np; t0 += kSelThreads * kPickBatch) {
+      int64_t slot[kPickBatch];
 #pragma unroll
       for (int b = 0; b < kPickBatch; ++b) {
-        const int i = i0 + b * kSelThreads + tid;
-        const int sl = i / slice_cap;
-        take[b] = i < list && static_cast<uint32_t>(i - sl * slice_cap) < s_cnt[sl < slices ? sl : 0];
-        k[b] = take[b] ? cg[i] : 0;
+        const uint32_t t = t0 + b * kSelThreads + tid;
+        slot[b] = -1;
+        if (t < np) {
+          // the last slice whose first candidate is at or before t (it is
+          // not empty: the next slice starts after t)
+          int lo = 0, hi = slices - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= t) lo = mid;
+            else hi = mid - 1;
+          }
+          slot[b] = static_cast<int64_t>(lo) * slice_cap + (t - s_off[lo]);
+        }
       }
+      uint64_t k[kPickBatch];
 #pragma unroll
-      for (int b = 0; b < kPickBatch; ++b) wave_append(take[b], k[b], cand, &s_cand);
+      for (int b = 0; b < kPickBatch; ++b) k[b] = slot[b] >= 0 ? cg[slot[b]] : 0;
+#pragma unroll
+      for (int b = 0; b < kPickBatch; ++b) {
+        const uint32_t t = t0 + b * kSelThreads + tid;
+        if (t < np) cand[t] = k[b];
+      }
     }
-    for (uint32_t i0 = 0; i0 < nx; i0 += kSelThreads) {
-      const uint32_t i = i0 + tid;
-      wave_append(i < nx, i < nx ? xg[i] : 0, cand, &s_cand);
-    }
+    for (uint32_t t = tid; t < nx; t += kSelThreads) cand[np + t] = xg[t];
     __syncthreads();
     // The candidates all lie at or above the threshold, so their leading bits
     // (the logit's sign, exponent and first mantissa bits) are mostly shared:
